@@ -1,0 +1,370 @@
+/*
+ * CPU FP64 oracle for the vocabulary-head + CTC loss path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline leg do.  It shares no code, header, table or helper with the HIP
+ * implementation.
+ *
+ * What it computes is the plain definition, written out, of full-vocabulary
+ * CTC through an affine head (source: "Pruned CTC for Memory-Efficient
+ * Large-Vocabulary ASR Training", Sec. 3.1 problem statement, Eq. 1 and 2;
+ * Sec. 3.2 Proposition 1 and the logit gradient of Eq. 5):
+ *
+ *   Z = X W^T + 1 b^T                         (every vocabulary column)
+ *   lambda_m = log sum_v exp Z[m][v]          (Eq. 1, the normalizer)
+ *   logp[m][v] = Z[m][v] - lambda_m
+ *   loss_n = -log sum over alignments pi with B(pi) = y_n of
+ *            prod_t p_{pi_t}(frame t)         (Eq. 2, textbook CTC forward
+ *                                              recursion on the
+ *                                              blank-interleaved labels)
+ *   dZ[m][v] = grad * (p_v(m) - gamma_v(m))   (Eq. 5, gamma = occupancy)
+ *   dX = dZ W,  dW = dZ^T X,  db = column sums of dZ.
+ *
+ * Everything is IEEE FP64 with natural-order loops.  The selected-class set
+ * and the chunk width of the reduced method play no part in the numerics.
+ * Utterances whose target cannot be aligned (|y| + r > T, r = number of
+ * adjacent equal label pairs; App. B.1 of the same paper) and utterances
+ * whose loss comes out nonfinite contribute zero loss and zero gradient
+ * (App. B.1; PrunedCTC README, return value).
+ *
+ * Parity pins for every function here live in tests/test_oracle_pins.py
+ * (brute-force alignment enumeration, closed forms, finite differences,
+ * the reduced-vocabulary identity of Proposition 1, and invariants).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORACLE_OK 0
+#define ORACLE_ERR_ARG 1
+#define ORACLE_ERR_TARGET 2
+#define ORACLE_ERR_LENGTHS 3
+#define ORACLE_ERR_NOMEM 4
+
+/* log(exp(a) + exp(b)) with -inf handled. */
+static double log_add(double a, double b) {
+  if (a == -INFINITY) return b;
+  if (b == -INFINITY) return a;
+  double hi = a > b ? a : b;
+  double lo = a > b ? b : a;
+  return hi + log1p(exp(lo - hi));
+}
+
+/* Number of adjacent equal label pairs r_n (App. B.1). */
+static int repeat_pairs(const int32_t* y, int L) {
+  int r = 0;
+  for (int i = 0; i + 1 < L; ++i)
+    if (y[i] == y[i + 1]) ++r;
+  return r;
+}
+
+/*
+ * Structural alignability and the selected-class set.
+ *
+ * flags[n] = 1 iff |y_n| + r_n <= T_n (App. B.1).  U = blank first, then
+ * the distinct target labels of the whole batch in ascending id order;
+ * tgt_rel[i] = position of tgt[i] in U (App. B.1 and Sec. 3.2).
+ * Returns the number K of selected classes, or a negative error code.
+ */
+int oracle_select(int N, int V, int blank, const int32_t* frame_counts,
+                  const int32_t* tgt_off, const int32_t* tgt, int32_t* U,
+                  int32_t* tgt_rel, uint8_t* flags) {
+  if (N < 0 || V <= 0 || blank < 0 || blank >= V) return -ORACLE_ERR_ARG;
+  if (tgt_off[0] != 0) return -ORACLE_ERR_TARGET;
+  for (int n = 0; n < N; ++n) {
+    if (tgt_off[n + 1] < tgt_off[n]) return -ORACLE_ERR_TARGET;
+    if (frame_counts[n] <= 0) return -ORACLE_ERR_LENGTHS;
+  }
+  int Ltot = tgt_off[N];
+  unsigned char* present = (unsigned char*)calloc((size_t)V, 1);
+  if (!present) return -ORACLE_ERR_NOMEM;
+  for (int i = 0; i < Ltot; ++i) {
+    if (tgt[i] < 0 || tgt[i] >= V || tgt[i] == blank) {
+      free(present);
+      return -ORACLE_ERR_TARGET;
+    }
+    present[tgt[i]] = 1;
+  }
+  int K = 0;
+  U[K++] = blank;
+  for (int v = 0; v < V; ++v)
+    if (present[v] && v != blank) U[K++] = v;
+  for (int i = 0; i < Ltot; ++i) {
+    int lo = 1, hi = K - 1; /* U[1..K-1] is ascending */
+    while (lo < hi) {
+      int mid = (lo + hi) / 2;
+      if (U[mid] < tgt[i]) lo = mid + 1; else hi = mid;
+    }
+    tgt_rel[i] = lo;
+  }
+  for (int n = 0; n < N; ++n) {
+    int L = tgt_off[n + 1] - tgt_off[n];
+    int r = repeat_pairs(tgt + tgt_off[n], L);
+    flags[n] = (L + r <= frame_counts[n]) ? 1 : 0;
+  }
+  free(present);
+  return K;
+}
+
+/*
+ * CTC for one utterance from raw logits Z (T x V, row-major).
+ *
+ * Computes lambda (Eq. 1), the log-likelihood by the forward recursion on
+ * the extended label sequence (blank, y1, blank, y2, ..., yL, blank), the
+ * backward recursion, the occupancies gamma and the logit gradient of Eq. 5:
+ *   dZ[t][v] = grad * (p_v(t) - gamma_v(t)).
+ * status: 0 = finite loss; 1 = not structurally alignable; 2 = nonfinite.
+ * For status != 0 the loss is 0 and dZ / gamma are all zero.
+ * Any of lambda_out, dZ, gamma may be NULL.
+ */
+int oracle_ctc_logits(int T, int V, int blank, const double* Z,
+                      const int32_t* y, int L, double grad,
+                      double* loss_out, int* status_out, double* lambda_out,
+                      double* dZ, double* gamma) {
+  if (T <= 0 || V <= 0 || L < 0 || blank < 0 || blank >= V)
+    return ORACLE_ERR_ARG;
+  for (int i = 0; i < L; ++i)
+    if (y[i] < 0 || y[i] >= V || y[i] == blank) return ORACLE_ERR_TARGET;
+  const int S = 2 * L + 1;
+  double* logp = (double*)malloc(sizeof(double) * (size_t)T * V);
+  double* alpha = (double*)malloc(sizeof(double) * (size_t)T * S);
+  double* beta = (double*)malloc(sizeof(double) * (size_t)T * S);
+  int32_t* ext = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
+  if (!logp || !alpha || !beta || !ext) {
+    free(logp); free(alpha); free(beta); free(ext);
+    return ORACLE_ERR_NOMEM;
+  }
+  /* Eq. 1: log-softmax over the whole vocabulary, one row at a time. */
+  for (int t = 0; t < T; ++t) {
+    const double* z = Z + (size_t)t * V;
+    double mx = -INFINITY;
+    for (int v = 0; v < V; ++v) if (z[v] > mx) mx = z[v];
+    double s = 0.0;
+    for (int v = 0; v < V; ++v) s += exp(z[v] - mx);
+    double lam = mx + log(s);
+    if (lambda_out) lambda_out[t] = lam;
+    for (int v = 0; v < V; ++v) logp[(size_t)t * V + v] = z[v] - lam;
+  }
+  for (int s = 0; s < S; ++s) ext[s] = (s % 2 == 0) ? blank : y[s / 2];
+
+  int r = repeat_pairs(y, L);
+  int status = 0;
+  double loss = 0.0;
+  if (L + r > T) {
+    status = 1;
+  } else {
+    /* Forward recursion (alpha includes the emission at frame t). */
+    for (int s = 0; s < S; ++s) alpha[s] = -INFINITY;
+    alpha[0] = logp[ext[0]];
+    if (S > 1) alpha[1] = logp[ext[1]];
+    for (int t = 1; t < T; ++t) {
+      const double* lp = logp + (size_t)t * V;
+      const double* prev = alpha + (size_t)(t - 1) * S;
+      double* cur = alpha + (size_t)t * S;
+      for (int s = 0; s < S; ++s) {
+        double a = prev[s];
+        if (s >= 1) a = log_add(a, prev[s - 1]);
+        if (s >= 2 && ext[s] != blank && ext[s] != ext[s - 2])
+          a = log_add(a, prev[s - 2]);
+        cur[s] = a + lp[ext[s]];
+      }
+    }
+    const double* last = alpha + (size_t)(T - 1) * S;
+    double logP = last[S - 1];
+    if (S > 1) logP = log_add(logP, last[S - 2]);
+    /* Backward recursion (beta also includes the emission at frame t). */
+    for (int s = 0; s < S; ++s) beta[(size_t)(T - 1) * S + s] = -INFINITY;
+    beta[(size_t)(T - 1) * S + S - 1] = logp[(size_t)(T - 1) * V + ext[S - 1]];
+    if (S > 1)
+      beta[(size_t)(T - 1) * S + S - 2] =
+          logp[(size_t)(T - 1) * V + ext[S - 2]];
+    for (int t = T - 2; t >= 0; --t) {
+      const double* lp = logp + (size_t)t * V;
+      const double* nxt = beta + (size_t)(t + 1) * S;
+      double* cur = beta + (size_t)t * S;
+      for (int s = 0; s < S; ++s) {
+        double b = nxt[s];
+        if (s + 1 < S) b = log_add(b, nxt[s + 1]);
+        if (s + 2 < S && ext[s] != blank && ext[s] != ext[s + 2])
+          b = log_add(b, nxt[s + 2]);
+        cur[s] = b + lp[ext[s]];
+      }
+    }
+    if (!isfinite(logP)) {
+      status = 2;
+    } else {
+      loss = -logP;
+    }
+    if (status == 0 && (dZ || gamma)) {
+      double* gam_row = (double*)malloc(sizeof(double) * (size_t)V);
+      if (!gam_row) {
+        free(logp); free(alpha); free(beta); free(ext);
+        return ORACLE_ERR_NOMEM;
+      }
+      for (int t = 0; t < T; ++t) {
+        memset(gam_row, 0, sizeof(double) * (size_t)V);
+        const double* lp = logp + (size_t)t * V;
+        for (int s = 0; s < S; ++s) {
+          double lg = alpha[(size_t)t * S + s] + beta[(size_t)t * S + s] -
+                      lp[ext[s]] - logP;
+          gam_row[ext[s]] += exp(lg);
+        }
+        for (int v = 0; v < V; ++v) {
+          if (gamma) gamma[(size_t)t * V + v] = gam_row[v];
+          if (dZ) dZ[(size_t)t * V + v] = grad * (exp(lp[v]) - gam_row[v]);
+        }
+      }
+      free(gam_row);
+    }
+  }
+  if (status != 0) {
+    if (dZ) memset(dZ, 0, sizeof(double) * (size_t)T * V);
+    if (gamma) memset(gamma, 0, sizeof(double) * (size_t)T * V);
+  }
+  *loss_out = loss;
+  *status_out = status;
+  free(logp); free(alpha); free(beta); free(ext);
+  return ORACLE_OK;
+}
+
+/*
+ * The whole path: head projection, CTC loss and gradients for a batch of N
+ * utterances stacked without padding into X (M x D, row-major; utterance n
+ * owns rows [o_n, o_n + T_n) with o_n = T_0 + ... + T_{n-1}).  W is V x D
+ * row-major, b has V entries (NULL = zero bias).  Targets are given in CSR
+ * form (tgt_off has N+1 entries).  grad is the scalar upstream gradient of
+ * the summed loss.
+ *
+ * Outputs (any pointer except loss_out may be NULL):
+ *   loss_out      summed loss over utterances with a finite loss
+ *   utt_loss[N]   per-utterance loss (0 for excluded utterances)
+ *   status[N]     0 finite, 1 unalignable, 2 nonfinite
+ *   lambda[M]     normalizer per frame (Eq. 1)
+ *   logp_cols     M x ncols log-probabilities at the columns cols[]
+ *   gamma_cols    M x ncols occupancies at the columns cols[]
+ *   dX[M*D], dW[V*D], db[V]   gradients (dW and db are overwritten)
+ * Utterances are processed one at a time; within one, the T_n x V logit
+ * block is materialised in FP64 (the dense reference groups whole
+ * utterances, App. B "accuracy" paragraph).
+ */
+int oracle_pcx(int N, int M, int D, int V, int blank, const double* X,
+               const double* W, const double* b, const int32_t* frame_counts,
+               const int32_t* tgt_off, const int32_t* tgt, double grad,
+               double* loss_out, double* utt_loss, int32_t* status,
+               double* lambda, int ncols, const int32_t* cols,
+               double* logp_cols, double* gamma_cols, double* dX, double* dW,
+               double* db) {
+  if (N < 0 || M < 0 || D <= 0 || V <= 0 || blank < 0 || blank >= V)
+    return ORACLE_ERR_ARG;
+  long long sumT = 0;
+  for (int n = 0; n < N; ++n) {
+    if (frame_counts[n] <= 0) return ORACLE_ERR_LENGTHS;
+    sumT += frame_counts[n];
+  }
+  if (sumT != M) return ORACLE_ERR_LENGTHS;
+  if (tgt_off[0] != 0) return ORACLE_ERR_TARGET;
+  for (int n = 0; n < N; ++n)
+    if (tgt_off[n + 1] < tgt_off[n]) return ORACLE_ERR_TARGET;
+  for (int i = 0; i < tgt_off[N]; ++i)
+    if (tgt[i] < 0 || tgt[i] >= V || tgt[i] == blank) return ORACLE_ERR_TARGET;
+  for (int c = 0; c < ncols; ++c)
+    if (cols[c] < 0 || cols[c] >= V) return ORACLE_ERR_ARG;
+
+  if (dW) memset(dW, 0, sizeof(double) * (size_t)V * D);
+  if (db) memset(db, 0, sizeof(double) * (size_t)V);
+  const int want_grad = (dX || dW || db || gamma_cols) ? 1 : 0;
+  double total = 0.0;
+  int row0 = 0;
+  for (int n = 0; n < N; ++n) {
+    const int T = frame_counts[n];
+    const int L = tgt_off[n + 1] - tgt_off[n];
+    const double* Xn = X + (size_t)row0 * D;
+    double* Zn = (double*)malloc(sizeof(double) * (size_t)T * V);
+    double* lam = (double*)malloc(sizeof(double) * (size_t)T);
+    double* dZn = want_grad ? (double*)malloc(sizeof(double) * (size_t)T * V) : NULL;
+    double* gam = gamma_cols ? (double*)malloc(sizeof(double) * (size_t)T * V) : NULL;
+    if (!Zn || !lam || (want_grad && !dZn) || (gamma_cols && !gam)) {
+      free(Zn); free(lam); free(dZn); free(gam);
+      return ORACLE_ERR_NOMEM;
+    }
+    /* Z_n = X_n W^T + b, natural-order dot products (Sec. 3.1). */
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int t = 0; t < T; ++t) {
+      for (int v = 0; v < V; ++v) {
+        const double* x = Xn + (size_t)t * D;
+        const double* w = W + (size_t)v * D;
+        double acc = 0.0;
+        for (int d = 0; d < D; ++d) acc += x[d] * w[d];
+        Zn[(size_t)t * V + v] = acc + (b ? b[v] : 0.0);
+      }
+    }
+    double loss_n = 0.0;
+    int st = 0;
+    int rc = oracle_ctc_logits(T, V, blank, Zn, tgt + tgt_off[n], L, grad,
+                               &loss_n, &st, lam, dZn, gam);
+    if (rc != ORACLE_OK) {
+      free(Zn); free(lam); free(dZn); free(gam);
+      return rc;
+    }
+    if (utt_loss) utt_loss[n] = loss_n;
+    if (status) status[n] = st;
+    if (st == 0) total += loss_n;
+    if (lambda) memcpy(lambda + row0, lam, sizeof(double) * (size_t)T);
+    for (int t = 0; t < T; ++t) {
+      for (int c = 0; c < ncols; ++c) {
+        if (logp_cols)
+          logp_cols[(size_t)(row0 + t) * ncols + c] =
+              Zn[(size_t)t * V + cols[c]] - lam[t];
+        if (gamma_cols)
+          gamma_cols[(size_t)(row0 + t) * ncols + c] = gam[(size_t)t * V + cols[c]];
+      }
+    }
+    /* dX_n = dZ_n W */
+    if (dX) {
+#pragma omp parallel for schedule(static)
+      for (int t = 0; t < T; ++t) {
+        double* dx = dX + (size_t)(row0 + t) * D;
+        for (int d = 0; d < D; ++d) dx[d] = 0.0;
+        for (int v = 0; v < V; ++v) {
+          const double g = dZn[(size_t)t * V + v];
+          const double* w = W + (size_t)v * D;
+          for (int d = 0; d < D; ++d) dx[d] += g * w[d];
+        }
+      }
+    }
+    /* dW += dZ_n^T X_n,  db += column sums of dZ_n */
+    if (dW || db) {
+#pragma omp parallel for schedule(static)
+      for (int v = 0; v < V; ++v) {
+        for (int t = 0; t < T; ++t) {
+          const double g = dZn[(size_t)t * V + v];
+          if (db) db[v] += g;
+          if (dW) {
+            double* dw = dW + (size_t)v * D;
+            const double* x = Xn + (size_t)t * D;
+            for (int d = 0; d < D; ++d) dw[d] += g * x[d];
+          }
+        }
+      }
+    }
+    free(Zn); free(lam); free(dZn); free(gam);
+    row0 += T;
+  }
+  *loss_out = total;
+  return ORACLE_OK;
+}
+
+/* Number of threads OpenMP will use for the parallel loops above. */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
