@@ -1,0 +1,178 @@
+/*
+ * pcx: vocabulary-head projection fused with the exact reduced-class CTC loss
+ * and its gradients, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows "Pruned CTC for Memory-Efficient Large-Vocabulary
+ * ASR Training" (Sec. 3.1 problem statement, Eq. 1-2; Sec. 3.2 selected
+ * classes and Proposition 1; Sec. 3.3 / App. B.1 chunked projection, FP64
+ * normalizer and backward recomputation) with an unbounded alignment beam,
+ * i.e. the pages' "unpruned reduced CTC".  The calls mirror the interface of
+ * the PrunedCTC README (pruned_ctc_loss: encoder states, head weight and
+ * bias, ragged targets, frame counts, chunk size, blank id; the return value
+ * is the plain sum of per-utterance losses; fp32 or bf16 inputs, gradients
+ * in the input dtype; only first-order gradients).
+ *
+ * Plain C ABI: no C++ or framework types.  Every device pointer is memory on
+ * the current HIP device; every "stream" is a hipStream_t passed as void*
+ * (NULL = the default stream).  All work is ordered on that stream.  No call
+ * throws; each returns a pcx_status and, on failure, pcx_last_error() gives a
+ * message (thread-local, valid until the next pcx call on that thread).
+ */
+#ifndef PCX_H
+#define PCX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type shared by X, W and b (and the gradients written back). */
+typedef enum {
+  PCX_F32 = 0,  /* IEEE binary32 */
+  PCX_BF16 = 1  /* bfloat16; float16 is not supported (README constraints) */
+} pcx_dtype;
+
+typedef enum {
+  PCX_OK = 0,
+  PCX_ERR_ARG = 1,     /* null pointer, negative or inconsistent size      */
+  PCX_ERR_DTYPE = 2,   /* dtype other than PCX_F32 / PCX_BF16              */
+  PCX_ERR_TARGET = 3,  /* label outside [0, V), blank inside a target,     */
+                       /* target offsets not monotone or not ending at L   */
+  PCX_ERR_LENGTHS = 4, /* a frame count <= 0, or the counts do not sum to M */
+  PCX_ERR_STATE = 5,   /* backward without a successful forward            */
+  PCX_ERR_HIP = 6,     /* HIP runtime failure (allocation, launch, copy)   */
+  PCX_ERR_LIMIT = 7    /* a target longer than PCX_MAX_TARGET_LEN labels   */
+} pcx_status;
+
+/* Longest target (in labels) the alignment kernels accept. */
+#define PCX_MAX_TARGET_LEN 2047
+
+/* Opaque per-call-site context: holds the device workspace and what the
+ * forward pass leaves for the backward pass (selected classes, relabelled
+ * targets, flags, normalizers, selected-class scores S, DP tables). */
+typedef struct pcx_ctx pcx_ctx;
+
+/* Filled by pcx_forward. */
+typedef struct {
+  int32_t K;               /* number of selected classes |U|               */
+  int32_t n_unalignable;   /* utterances with |y| + r > T (zero loss/grad)  */
+  int32_t n_nonfinite;     /* alignable utterances whose loss was not finite */
+  int32_t max_target_len;  /* longest target in the batch                   */
+  uint64_t workspace_bytes;/* device bytes the context holds after the call */
+} pcx_fwd_info;
+
+/* Create / destroy a context.  The context owns its device workspace, which
+ * grows on demand (hipMalloc) and is released by pcx_destroy.  A context may
+ * be used by one thread at a time. */
+pcx_status pcx_create(pcx_ctx** out_ctx);
+void pcx_destroy(pcx_ctx* ctx);
+
+/*
+ * Forward pass: selected classes, chunked projection with the FP64 online
+ * normalizer, S = Z[:, U] - lambda rounded once to FP32, the FP64 CTC
+ * forward recursion over the K selected columns, and the summed loss.
+ *
+ *   X             device, M x D row-major: the head inputs of all utterances
+ *                 stacked without padding, utterance n owning the T_n rows
+ *                 after those of utterances 0..n-1 (Sec. 3.1).
+ *   W             device, V x D row-major (nn.Linear weight layout).
+ *   b             device, V entries, or NULL for a zero bias.
+ *   dtype         PCX_F32 or PCX_BF16, the element type of X, W and b.
+ *   M, D, V, N    frames, head width, vocabulary size, utterances (N >= 0,
+ *                 M >= 0, D >= 1, V >= 1).
+ *   tgt_off       device int32, N + 1 monotone offsets into tgt, tgt_off[0]
+ *                 = 0 and tgt_off[N] = L_tot (CSR form of the ragged,
+ *                 blank-free targets).
+ *   tgt           device int32, L_tot labels in [0, V) \ {blank}.
+ *   L_tot         number of labels in tgt.
+ *   frame_counts  device int32, N positive frame counts summing to M (may be
+ *                 NULL when N = 0).
+ *   blank         blank class id in [0, V).
+ *   chunk         vocabulary chunk width C >= 1 used by the backward pass for
+ *                 its one M x C gradient block (App. B.1); results do not
+ *                 depend on it beyond rounding.
+ *   stream        hipStream_t (void*), NULL for the default stream.
+ *   loss          host out, may be NULL: sum of the finite per-utterance
+ *                 losses (unalignable / nonfinite ones contribute 0; the
+ *                 README's "excluded with a warning" case is reported in
+ *                 info instead of printed).
+ *   info          host out, may be NULL.
+ *
+ * X, W and b must stay alive and unchanged until the matching pcx_backward.
+ * The call synchronises the stream twice (to size the workspace once K is
+ * known, and to read the loss back).  Errors in the device-resident targets
+ * and lengths are detected on the device and reported after the first sync.
+ */
+pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W,
+                       const void* b, int32_t dtype, int64_t M, int64_t D,
+                       int64_t V, int32_t N, const int32_t* tgt_off,
+                       const int32_t* tgt, int64_t L_tot,
+                       const int32_t* frame_counts, int32_t blank,
+                       int32_t chunk, void* stream, double* loss,
+                       pcx_fwd_info* info);
+
+/*
+ * Backward pass for the last successful pcx_forward on ctx: the FP64 CTC
+ * backward recursion, occupancies gamma on the selected classes, and, one
+ * vocabulary chunk at a time, the recomputed logits, the logit gradient
+ *   dZ[m][v] = grad_loss * (g_m p_v(m) - gamma_v(m))   (Eq. 5 / Eq. 7)
+ * and the products dX = dZ W, dW = dZ^T X, db = column sums of dZ.
+ *
+ *   grad_loss  upstream gradient of the summed loss (any scaling, e.g. a
+ *              division by the target-token count, goes here).
+ *   dX         device, M x D in the input dtype, or NULL to skip.
+ *   dW         device, V x D in the input dtype, or NULL to skip.
+ *   db         device, V in the input dtype, or NULL to skip.
+ * Outputs are overwritten, not accumulated.  Rows of excluded utterances get
+ * exact zeros.  May be called more than once per forward.  No host sync.
+ */
+pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
+                        void* db, void* stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* pcx_last_error(void);
+
+/*
+ * Inspection getters (synchronous device-to-host copies after the context's
+ * stream has finished), used by parity tests.  Each copies at most
+ * `capacity` elements into the host buffer and fails with PCX_ERR_ARG if the
+ * buffer is too small, PCX_ERR_STATE if no forward has completed.
+ *   selected    K int32: U, blank first then ascending distinct labels.
+ *   relabeled   L_tot int32: index of each target label in U.
+ *   alignable   N uint8: 1 iff |y_n| + r_n <= T_n.
+ *   utt_losses  N double: per-utterance loss (0 when excluded).
+ *   utt_status  N int32: 0 finite, 1 unalignable, 2 nonfinite.
+ *   normalizer  M double: lambda_m (Eq. 1).
+ *   scores      K x M float, class-major: S[j][m] = fp32(Z[m][U[j]] - lambda_m).
+ *   occupancy   K x M float, class-major: gamma_{U[j]}(m) (after a backward).
+ */
+pcx_status pcx_get_selected(pcx_ctx* ctx, int32_t* out, int64_t capacity);
+pcx_status pcx_get_relabeled(pcx_ctx* ctx, int32_t* out, int64_t capacity);
+pcx_status pcx_get_alignable(pcx_ctx* ctx, uint8_t* out, int64_t capacity);
+pcx_status pcx_get_utt_losses(pcx_ctx* ctx, double* out, int64_t capacity);
+pcx_status pcx_get_utt_status(pcx_ctx* ctx, int32_t* out, int64_t capacity);
+pcx_status pcx_get_normalizer(pcx_ctx* ctx, double* out, int64_t capacity);
+pcx_status pcx_get_scores(pcx_ctx* ctx, float* out, int64_t capacity);
+pcx_status pcx_get_occupancy(pcx_ctx* ctx, float* out, int64_t capacity);
+
+/*
+ * Optional per-kernel timing.  While enabled, every kernel the context
+ * launches is bracketed by two hipEvents recorded on the launch stream;
+ * pcx_profile_read waits for the recorded events and returns, for kernel
+ * family i in [0, pcx_profile_count()), its name, the summed event-measured
+ * duration in milliseconds and the number of launches since the last reset.
+ * Off by default; enabling adds two event records per launch.
+ */
+pcx_status pcx_profile_enable(pcx_ctx* ctx, int32_t on);
+pcx_status pcx_profile_reset(pcx_ctx* ctx);
+int32_t pcx_profile_count(void);
+pcx_status pcx_profile_read(pcx_ctx* ctx, int32_t i, const char** name,
+                            double* total_ms, int64_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PCX_H */

@@ -1,0 +1,109 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+* libpcx.so loads and exports every function include/pcx.h declares, and the
+  Python binding's signature table covers exactly those functions;
+* argument validation that happens before any device work: NULL context,
+  unsupported dtype (fp16), bad sizes, bad blank / chunk, backward or getters
+  before a forward pass (PCX_ERR_* codes, message via pcx_last_error).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pcx.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pcx_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from vocabulary_ctc_loss_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from vocabulary_ctc_loss_amd import build
+        build.build()
+    return _lib.load()
+
+
+def test_header_declares_the_expected_api():
+    fns = declared_functions()
+    for f in ("pcx_create", "pcx_destroy", "pcx_forward", "pcx_backward", "pcx_last_error"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from vocabulary_ctc_loss_amd import _lib
+    fns = declared_functions()
+    for f in fns:
+        assert hasattr(lib, f), f
+    assert sorted(_lib.SIGNATURES) == fns
+
+
+def _ctx(lib):
+    h = ctypes.c_void_p()
+    assert lib.pcx_create(ctypes.byref(h)) == 0
+    return h
+
+
+def _fwd(lib, h, **kw):
+    a = dict(X=1, W=1, b=None, dtype=0, M=4, D=8, V=6, N=1, off=1, tgt=1, L=2, fc=1,
+             blank=0, chunk=4)
+    a.update(kw)
+    loss = ctypes.c_double()
+    return lib.pcx_forward(h, a["X"], a["W"], a["b"], a["dtype"], a["M"], a["D"], a["V"], a["N"],
+                           a["off"], a["tgt"], a["L"], a["fc"], a["blank"], a["chunk"], None,
+                           ctypes.byref(loss), None)
+
+
+def test_null_context_is_rejected(lib):
+    assert _fwd(lib, None) == 1
+    assert b"ctx" in lib.pcx_last_error()
+    assert lib.pcx_backward(None, 1.0, None, None, None, None) == 1
+
+
+def test_argument_validation_before_device_work(lib):
+    h = _ctx(lib)
+    try:
+        assert _fwd(lib, h, dtype=2) == 2          # fp16 unsupported
+        assert b"dtype" in lib.pcx_last_error()
+        assert _fwd(lib, h, dtype=7) == 2
+        assert _fwd(lib, h, M=-1) == 1
+        assert _fwd(lib, h, D=0) == 1
+        assert _fwd(lib, h, V=0) == 1
+        assert _fwd(lib, h, N=-2) == 1
+        assert _fwd(lib, h, blank=6) == 1          # blank outside [0, V)
+        assert _fwd(lib, h, blank=-1) == 1
+        assert _fwd(lib, h, chunk=0) == 1
+        assert _fwd(lib, h, off=None) == 1
+        assert _fwd(lib, h, tgt=None) == 1          # L_tot > 0 needs labels
+        assert _fwd(lib, h, X=None) == 1
+        assert _fwd(lib, h, M=2**31) == 1           # beyond the 32-bit index range
+        # no forward has succeeded: backward and getters refuse
+        assert lib.pcx_backward(h, 1.0, None, None, None, None) == 5
+        buf = (ctypes.c_int32 * 8)()
+        assert lib.pcx_get_selected(h, buf, 8) == 5
+        assert lib.pcx_get_occupancy(h, buf, 8) == 5
+    finally:
+        lib.pcx_destroy(h)
+
+
+def test_profile_api_without_device(lib):
+    h = _ctx(lib)
+    try:
+        assert lib.pcx_profile_count() >= 10
+        assert lib.pcx_profile_enable(h, 1) == 0
+        assert lib.pcx_profile_reset(h) == 0
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double()
+        n = ctypes.c_int64()
+        assert lib.pcx_profile_read(h, 1, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)) == 0
+        assert name.value == b"fwd_gemm_lse" and n.value == 0
+        assert lib.pcx_profile_read(h, 999, None, None, None) == 1
+    finally:
+        lib.pcx_destroy(h)

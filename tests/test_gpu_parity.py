@@ -1,0 +1,254 @@
+"""Parity of the HIP path (through the C ABI) with the CPU FP64 oracle.
+
+Bar: U, relabelled targets and alignability flags bit-exact; loss relative
+error <= 1e-5 and dX / dW / db relative Frobenius error <= 1e-5 for fp32
+inputs, <= 2e-2 for bf16 inputs; all-zero references (excluded utterances)
+must come back as exact zeros.  Intermediates are checked too: the FP64
+normalizer lambda, the FP32 scores S = Z[:, U] - lambda and the occupancies
+gamma on the selected classes.
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+import workloads
+from pcx_harness import rel_fro, run_oracle, run_pcx, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _labels(rng, n, V, blank, k=None):
+    ids = np.array([v for v in range(V) if v != blank])
+    if k is not None:
+        ids = ids[:k]
+    return rng.choice(ids, size=n).astype(np.int32)
+
+
+def case(name):
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    if name == "readme":
+        return workloads.make("tiny", seed=0)
+    if name == "tiles":      # several M tiles, ragged D (K tail), ragged chunks
+        return workloads.make_random(1, N=6, T_lo=40, T_hi=130, V=700, D=72, chunk=200)
+    if name == "spans":      # several normalizer spans, ragged last span
+        return workloads.make_random(2, N=4, T_lo=60, T_hi=160, V=5000, D=64, chunk=1024)
+    if name == "blank_last":
+        return workloads.make_random(3, N=5, T_lo=20, T_hi=90, V=300, D=64, blank=299, chunk=64)
+    if name == "blank_mid":
+        return workloads.make_random(4, N=5, T_lo=20, T_hi=90, V=257, D=40, blank=100, chunk=100)
+    if name == "odd_D":      # D not a multiple of the vector width: scalar staging path
+        return workloads.make_random(5, N=3, T_lo=10, T_hi=50, V=77, D=13, chunk=30)
+    if name == "v_lt_c":
+        return workloads.make_random(6, N=3, T_lo=30, T_hi=70, V=50, D=32, chunk=4096)
+    if name == "all_classes":   # K = V
+        T = [60, 50, 70]
+        L = [13, 13, 13]
+        labels = np.arange(1, 40, dtype=np.int32)
+        return workloads.make_random(7, N=3, T_lo=0, T_hi=0, V=40, D=32, chunk=16,
+                                     frame_counts=T, target_lengths=L, labels=labels)
+    if name == "unalignable_mix":
+        # targets: [1 1 2 2] needs 6 frames; [3 4 5] needs 3; [6 6 6] needs 5; [7] needs 1
+        T = [5, 3, 4, 9, 40]
+        ys = [[1, 1, 2, 2], [3, 4, 5], [6, 6, 6], [7], list(_labels(rng, 12, 60, 0))]
+        L = [len(y) for y in ys]
+        return workloads.make_random(8, N=5, T_lo=0, T_hi=0, V=60, D=24, chunk=32,
+                                     frame_counts=T, target_lengths=L,
+                                     labels=np.concatenate(ys).astype(np.int32))
+    if name == "single_alignment":   # T = L + r for every utterance
+        ys = []
+        T = []
+        for n in range(4):
+            y = list(_labels(rng, 30 + 10 * n, 90, 0, k=6))  # few classes: many repeats
+            r = sum(1 for i in range(len(y) - 1) if y[i] == y[i + 1])
+            ys.append(y)
+            T.append(len(y) + r)
+        return workloads.make_random(9, N=4, T_lo=0, T_hi=0, V=90, D=48, chunk=64,
+                                     frame_counts=T, target_lengths=[len(y) for y in ys],
+                                     labels=np.concatenate(ys).astype(np.int32))
+    if name == "empty_targets":
+        T = [7, 20, 1, 33]
+        ys = [[], list(_labels(rng, 5, 30, 0)), [], list(_labels(rng, 8, 30, 0))]
+        return workloads.make_random(10, N=4, T_lo=0, T_hi=0, V=30, D=16, chunk=8,
+                                     frame_counts=T, target_lengths=[len(y) for y in ys],
+                                     labels=np.concatenate([np.asarray(y, np.int32) for y in ys]))
+    if name == "long_targets":   # 2L + 1 > 1024 states: several states per thread
+        T = [1300, 700]
+        L = [600, 300]
+        return workloads.make_random(11, N=2, T_lo=0, T_hi=0, V=500, D=32, chunk=256,
+                                     frame_counts=T, target_lengths=L)
+    if name == "one_utt":
+        return workloads.make_random(12, N=1, T_lo=200, T_hi=200, V=1000, D=64, chunk=512)
+    if name == "bf16_llm":
+        return workloads.make_random(13, N=4, T_lo=50, T_hi=120, V=3000, D=256, blank=2999,
+                                     chunk=1024, dtype="bf16", llm_head=True, len_div=3.0,
+                                     zipf_s=1.05)
+    if name == "bf16_head":
+        return workloads.make_random(14, N=3, T_lo=30, T_hi=90, V=900, D=136, chunk=256,
+                                     dtype="bf16")
+    raise KeyError(name)
+
+
+CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
+         "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
+         "long_targets", "one_utt", "bf16_llm", "bf16_head"]
+
+
+@pytest.mark.parametrize("name", CASES)
+def test_parity_with_oracle(name):
+    bt = case(name)
+    print("case", name, "N", bt.N, "M", bt.M, "D", bt.D, "V", bt.V, "C", bt.chunk, bt.dtype,
+          flush=True)
+    got = run_pcx(bt)
+    U, rel, flags = __import__("oracle").select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off,
+                                                bt.tgt)
+    ref = run_oracle(bt, cols=U, want_gamma=True)
+    tol = tolerance(bt)
+    # integer outputs: bit-exact
+    assert got["U"].tolist() == U.tolist()
+    assert got["rel"].tolist() == rel.tolist()
+    assert got["flags"].tolist() == flags.tolist()
+    assert got["info"]["K"] == len(U)
+    assert got["status"].tolist() == ref["status"].tolist()
+    # loss and per-utterance losses
+    assert abs(got["loss"] - ref["loss"]) <= tol * max(abs(ref["loss"]), 1e-30), \
+        (got["loss"], ref["loss"])
+    assert rel_fro(got["utt_loss"], ref["utt_loss"]) <= tol
+    # intermediates
+    if bt.dtype == "f32":
+        np.testing.assert_allclose(got["lam"], ref["lambda"], rtol=0, atol=2e-5)
+        np.testing.assert_allclose(got["S"], ref["logp_cols"].T, rtol=0, atol=2e-5)
+        np.testing.assert_allclose(got["Gam"], ref["gamma_cols"].T, rtol=0, atol=1e-5)
+    # gradients
+    for k in ("dX", "dW", "db"):
+        if ref[k] is None or got[k] is None:
+            continue
+        e = rel_fro(got[k], ref[k])
+        assert e <= tol, (k, e)
+    # excluded utterances: exact zeros in their dX rows
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    for n in range(bt.N):
+        if ref["status"][n] != 0:
+            assert np.all(got["dX"][row_off[n]:row_off[n + 1]] == 0.0)
+
+
+def test_grad_scaling_and_skipped_outputs():
+    bt = case("tiles")
+    ref = run_oracle(bt, grad=-0.37)
+    got = run_pcx(bt, grad=-0.37, want_dW=False, getters=False)
+    assert got["dW"] is None
+    assert rel_fro(got["dX"], ref["dX"]) <= 1e-5
+    assert rel_fro(got["db"], ref["db"]) <= 1e-5
+
+
+def test_deterministic_bitwise():
+    bt = case("spans")
+    a = run_pcx(bt, getters=False)
+    b = run_pcx(bt, getters=False)
+    assert a["loss"] == b["loss"]
+    for k in ("dX", "dW", "db"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_chunk_width_changes_only_rounding():
+    bt = case("tiles")
+    a = run_pcx(bt, getters=False)
+    import dataclasses
+    b = run_pcx(dataclasses.replace(bt, chunk=700), getters=False)
+    assert a["loss"] == b["loss"]  # forward does not depend on C
+    for k in ("dX", "dW", "db"):
+        assert rel_fro(b[k], a[k]) <= 1e-6, k
+
+
+def test_context_reuse_and_repeated_backward():
+    from vocabulary_ctc_loss_amd import Context
+    ctx = Context()
+    try:
+        for name in ("tiles", "readme", "spans"):
+            bt = case(name)
+            ref = run_oracle(bt)
+            got = run_pcx(bt, ctx=ctx, getters=False)
+            assert abs(got["loss"] - ref["loss"]) <= 1e-5 * abs(ref["loss"])
+            assert rel_fro(got["dW"], ref["dW"]) <= 1e-5
+    finally:
+        ctx.close()
+
+
+def test_empty_batch():
+    import torch
+    from vocabulary_ctc_loss_amd import Context
+    dev = "cuda:0"
+    X = torch.zeros((0, 16), device=dev)
+    W = torch.randn((10, 16), device=dev)
+    b = torch.randn((10,), device=dev)
+    off = torch.zeros(1, dtype=torch.int32, device=dev)
+    tgt = torch.zeros(0, dtype=torch.int32, device=dev)
+    fc = torch.zeros(0, dtype=torch.int32, device=dev)
+    c = Context()
+    loss, info = c.forward(X, W, b, off, tgt, fc, 0, 4)
+    assert loss == 0.0 and info["K"] == 1
+    dW = torch.full_like(W, 7.0)
+    db = torch.full_like(b, 7.0)
+    c.backward(1.0, None, dW, db)
+    torch.cuda.synchronize()
+    assert torch.all(dW == 0) and torch.all(db == 0)
+    c.close()
+
+
+def test_device_side_validation_errors():
+    import torch
+    from vocabulary_ctc_loss_amd import Context, PcxError
+    bt = case("readme")
+    from pcx_harness import to_device
+    X, W, b, off, tgt, fc = to_device(bt)
+    c = Context()
+    with pytest.raises(PcxError) as e:
+        bad = tgt.clone()
+        bad[1] = 0  # blank inside a target
+        c.forward(X, W, b, off, bad, fc, 0, 4)
+    assert e.value.status == 3
+    with pytest.raises(PcxError) as e:
+        bad = tgt.clone()
+        bad[0] = 6  # label == V
+        c.forward(X, W, b, off, bad, fc, 0, 4)
+    assert e.value.status == 3
+    with pytest.raises(PcxError) as e:
+        badfc = fc.clone()
+        badfc[0] = 11  # frame counts no longer sum to M
+        c.forward(X, W, b, off, tgt, badfc, 0, 4)
+    assert e.value.status == 4
+    with pytest.raises(PcxError) as e:
+        badfc = fc.clone()
+        badfc[0] = 0
+        badfc[1] = 21
+        c.forward(X, W, b, off, tgt, badfc, 0, 4)
+    assert e.value.status == 4
+    with pytest.raises(PcxError) as e:
+        c.forward(X.half(), W.half(), b.half(), off, tgt, fc, 0, 4)
+    assert e.value.status == 2
+    with pytest.raises(PcxError) as e:   # failed forward leaves no state for backward
+        c.backward(1.0, torch.empty_like(X))
+    assert e.value.status == 5
+    # and the context still works afterwards
+    loss, _ = c.forward(X, W, b, off, tgt, fc, 0, 4)
+    assert np.isfinite(loss)
+    c.close()
+
+
+def test_autograd_function():
+    import torch
+    from vocabulary_ctc_loss_amd import pruned_ctc_loss
+    bt = case("blank_mid")
+    from pcx_harness import to_device
+    X, W, b, off, tgt, fc = to_device(bt)
+    X.requires_grad_(True)
+    W.requires_grad_(True)
+    b.requires_grad_(True)
+    loss = pruned_ctc_loss(X, W, b, (off, tgt), fc, blank_id=bt.blank, chunk_size=bt.chunk)
+    (2.0 * loss).backward()
+    ref = run_oracle(bt, grad=2.0)
+    assert loss.dtype == torch.float32
+    assert abs(loss.item() - ref["loss"]) <= 1e-5 * abs(ref["loss"])
+    assert rel_fro(X.grad.double().cpu().numpy(), ref["dX"]) <= 1e-5
+    assert rel_fro(W.grad.double().cpu().numpy(), ref["dW"]) <= 1e-5
+    assert rel_fro(b.grad.double().cpu().numpy(), ref["db"]) <= 1e-5

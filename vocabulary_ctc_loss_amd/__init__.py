@@ -1,0 +1,206 @@
+"""pcx: vocabulary-head projection fused with the exact reduced-class CTC loss
+on AMD MI355X (gfx950).
+
+Python face of the C ABI in include/pcx.h ("Pruned CTC for Memory-Efficient
+Large-Vocabulary ASR Training", unpruned reduced CTC; interface after the
+PrunedCTC README's pruned_ctc_loss).  PyTorch supplies device memory and
+streams; the computation runs in the library's HIP kernels.  Importing works
+without a GPU; any call that reaches the library needs it built and a GPU.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Sequence
+
+import numpy as np
+
+from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PcxError, check,  # noqa: F401
+                   load)
+
+__all__ = ["Context", "PcxError", "pruned_ctc_loss", "pack_targets", "load", "LIB_PATH"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return PCX_F32
+    if t.dtype == torch.bfloat16:
+        return PCX_BF16
+    return 2 if t.dtype == torch.float16 else 99  # rejected by the library
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream_handle(stream) -> Optional[int]:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream or None
+
+
+def pack_targets(targets: Sequence[Sequence[int]], device=None):
+    """Ragged targets -> (offsets int32 [N+1], labels int32 [L_tot]) tensors."""
+    torch = _torch()
+    lens = [len(y) for y in targets]
+    off = np.zeros(len(targets) + 1, dtype=np.int32)
+    off[1:] = np.cumsum(lens)
+    vals = np.concatenate([np.asarray(y, np.int32) for y in targets]) if targets \
+        else np.zeros(0, np.int32)
+    return (torch.from_numpy(off).to(device), torch.from_numpy(vals.astype(np.int32)).to(device))
+
+
+class Context:
+    """One pcx_ctx: workspace plus the forward state a backward pass needs."""
+
+    def __init__(self):
+        self._lib = load()
+        h = ctypes.c_void_p()
+        check(self._lib.pcx_create(ctypes.byref(h)))
+        self._h = h
+        self.info = None
+        self._shape = None
+
+    def close(self):
+        if getattr(self, "_h", None) is not None and self._h.value:
+            self._lib.pcx_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # -------------------------------------------------------------- calls
+    def forward(self, X, W, b, tgt_off, tgt, frame_counts, blank: int = 0,
+                chunk: int = 4096, stream=None):
+        """Run pcx_forward; returns (summed loss as float, info dict)."""
+        for name, t in (("X", X), ("W", W), ("tgt_off", tgt_off), ("frame_counts", frame_counts)):
+            if not t.is_contiguous():
+                raise ValueError("%s must be contiguous" % name)
+        M, D = X.shape
+        V = W.shape[0]
+        N = frame_counts.shape[0]
+        L_tot = tgt.shape[0]
+        loss = ctypes.c_double(0.0)
+        info = FwdInfo()
+        check(self._lib.pcx_forward(
+            self._h, _ptr(X), _ptr(W), _ptr(b), _dtype_code(X), M, D, V, N, _ptr(tgt_off),
+            _ptr(tgt) if L_tot else None, L_tot, _ptr(frame_counts), int(blank), int(chunk),
+            _stream_handle(stream), ctypes.byref(loss), ctypes.byref(info)))
+        self.info = {f: getattr(info, f) for f, _ in FwdInfo._fields_}
+        self._shape = dict(M=M, D=D, V=V, N=N, L_tot=L_tot, K=info.K)
+        return loss.value, self.info
+
+    def backward(self, grad_loss: float = 1.0, dX=None, dW=None, db=None, stream=None):
+        check(self._lib.pcx_backward(self._h, float(grad_loss), _ptr(dX), _ptr(dW), _ptr(db),
+                                     _stream_handle(stream)))
+
+    # -------------------------------------------------------------- getters
+    def _get(self, fn, n, dtype):
+        out = np.zeros(max(1, n), dtype=dtype)
+        check(fn(self._h, out.ctypes.data_as(ctypes.c_void_p), n))
+        return out[:n]
+
+    def selected(self):
+        return self._get(self._lib.pcx_get_selected, self._shape["K"], np.int32)
+
+    def relabeled(self):
+        return self._get(self._lib.pcx_get_relabeled, self._shape["L_tot"], np.int32)
+
+    def alignable(self):
+        return self._get(self._lib.pcx_get_alignable, self._shape["N"], np.uint8).astype(bool)
+
+    def utt_losses(self):
+        return self._get(self._lib.pcx_get_utt_losses, self._shape["N"], np.float64)
+
+    def utt_status(self):
+        return self._get(self._lib.pcx_get_utt_status, self._shape["N"], np.int32)
+
+    def normalizer(self):
+        return self._get(self._lib.pcx_get_normalizer, self._shape["M"], np.float64)
+
+    def scores(self):
+        K, M = self._shape["K"], self._shape["M"]
+        return self._get(self._lib.pcx_get_scores, K * M, np.float32).reshape(K, M)
+
+    def occupancy(self):
+        K, M = self._shape["K"], self._shape["M"]
+        return self._get(self._lib.pcx_get_occupancy, K * M, np.float32).reshape(K, M)
+
+    # -------------------------------------------------------------- timing
+    def profile_enable(self, on: bool = True):
+        check(self._lib.pcx_profile_enable(self._h, 1 if on else 0))
+
+    def profile_reset(self):
+        check(self._lib.pcx_profile_reset(self._h))
+
+    def profile_read(self):
+        out = {}
+        for i in range(self._lib.pcx_profile_count()):
+            name = ctypes.c_char_p()
+            ms = ctypes.c_double()
+            n = ctypes.c_int64()
+            check(self._lib.pcx_profile_read(self._h, i, ctypes.byref(name), ctypes.byref(ms),
+                                             ctypes.byref(n)))
+            out[name.value.decode()] = (ms.value, n.value)
+        return out
+
+
+def _make_function():
+    torch = _torch()
+
+    class PcxLossFunction(torch.autograd.Function):
+        @staticmethod
+        def forward(fctx, X, W, b, tgt_off, tgt, frame_counts, blank, chunk):
+            c = Context()
+            loss, _ = c.forward(X, W, b, tgt_off, tgt, frame_counts, blank, chunk)
+            fctx.pcx = c
+            fctx.shapes = (X, W, b)
+            return torch.tensor(loss, dtype=torch.float32, device=X.device)
+
+        @staticmethod
+        def backward(fctx, grad):
+            X, W, b = fctx.shapes
+            need = fctx.needs_input_grad
+            dX = torch.empty_like(X) if need[0] else None
+            dW = torch.empty_like(W) if need[1] else None
+            db = torch.empty_like(b) if (b is not None and need[2]) else None
+            fctx.pcx.backward(float(grad.item()), dX, dW, db)
+            return dX, dW, db, None, None, None, None, None
+
+    return PcxLossFunction
+
+
+_FN = None
+
+
+def pruned_ctc_loss(X, weight, bias, targets, frame_counts, blank_id: int = 0,
+                    chunk_size: int = 4096):
+    """Summed CTC loss of the affine head (X weight^T + bias) over ragged targets.
+
+    X: (M, D) stacked head inputs (fp32 or bf16) on the GPU; weight (V, D); bias
+    (V,) or None; targets: list of label lists or an (offsets, labels) pair of
+    int32 device tensors; frame_counts: (N,) frame counts.  Returns a float32
+    scalar; gradients flow to X, weight and bias in their own dtypes.
+    """
+    global _FN
+    torch = _torch()
+    if _FN is None:
+        _FN = _make_function()
+    if isinstance(targets, (tuple, list)) and len(targets) == 2 and torch.is_tensor(targets[0]):
+        tgt_off, tgt = targets
+    else:
+        tgt_off, tgt = pack_targets(targets, device=X.device)
+    tgt_off = tgt_off.to(device=X.device, dtype=torch.int32).contiguous()
+    tgt = tgt.to(device=X.device, dtype=torch.int32).contiguous()
+    fc = frame_counts.to(device=X.device, dtype=torch.int32).contiguous()
+    return _FN.apply(X.contiguous(), weight.contiguous(),
+                     None if bias is None else bias.contiguous(), tgt_off, tgt, fc,
+                     int(blank_id), int(chunk_size))

@@ -1,0 +1,86 @@
+"""ctypes binding of libpcx.so (the C ABI declared in include/pcx.h).
+
+Argument marshalling only: every step of the loss runs in the HIP kernels of
+the library.  If the library has not been built the import of this module
+fails loudly; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpcx.so")
+
+PCX_F32 = 0
+PCX_BF16 = 1
+
+STATUS_NAMES = {
+    0: "PCX_OK", 1: "PCX_ERR_ARG", 2: "PCX_ERR_DTYPE", 3: "PCX_ERR_TARGET",
+    4: "PCX_ERR_LENGTHS", 5: "PCX_ERR_STATE", 6: "PCX_ERR_HIP", 7: "PCX_ERR_LIMIT",
+}
+
+# Every function include/pcx.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_D = ctypes.c_double
+SIGNATURES = {
+    "pcx_create": (_I32, [ctypes.POINTER(_P)]),
+    "pcx_destroy": (None, [_P]),
+    "pcx_forward": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _I64, _P,
+                           _I32, _I32, _P, ctypes.POINTER(_D), _P]),
+    "pcx_backward": (_I32, [_P, _D, _P, _P, _P, _P]),
+    "pcx_last_error": (ctypes.c_char_p, []),
+    "pcx_get_selected": (_I32, [_P, _P, _I64]),
+    "pcx_get_relabeled": (_I32, [_P, _P, _I64]),
+    "pcx_get_alignable": (_I32, [_P, _P, _I64]),
+    "pcx_get_utt_losses": (_I32, [_P, _P, _I64]),
+    "pcx_get_utt_status": (_I32, [_P, _P, _I64]),
+    "pcx_get_normalizer": (_I32, [_P, _P, _I64]),
+    "pcx_get_scores": (_I32, [_P, _P, _I64]),
+    "pcx_get_occupancy": (_I32, [_P, _P, _I64]),
+    "pcx_profile_enable": (_I32, [_P, _I32]),
+    "pcx_profile_reset": (_I32, [_P]),
+    "pcx_profile_count": (_I32, []),
+    "pcx_profile_read": (_I32, [_P, _I32, ctypes.POINTER(ctypes.c_char_p),
+                                ctypes.POINTER(_D), ctypes.POINTER(_I64)]),
+}
+
+
+class FwdInfo(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_int32), ("n_unalignable", ctypes.c_int32),
+                ("n_nonfinite", ctypes.c_int32), ("max_target_len", ctypes.c_int32),
+                ("workspace_bytes", ctypes.c_uint64)]
+
+
+class PcxError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__("%s: %s" % (STATUS_NAMES.get(status, str(status)), message))
+        self.status = status
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libpcx.so; raises if it was not built (no fallback path exists)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                "libpcx.so is not built (expected at %s); run "
+                "`python -m vocabulary_ctc_loss_amd.build` or __graft_entry__.build()" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        msg = load().pcx_last_error()
+        raise PcxError(status, msg.decode() if msg else "")

@@ -1,0 +1,496 @@
+// C ABI of the pcx library: argument checks, the per-context workspace, the
+// launch sequence of the forward and backward passes, optional per-kernel
+// event timing, and the inspection getters.  Declarations: include/pcx.h.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+#include <vector>
+
+#include "../../include/pcx.h"
+#include "pcx_common.h"
+
+using namespace pcx;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+pcx_status fail(pcx_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+#define PCX_HIP(call)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (call);                                                             \
+    if (e_ != hipSuccess)                                                               \
+      return fail(PCX_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));          \
+  } while (0)
+
+// A grow-only device buffer.
+struct DevBuf {
+  void* p = nullptr;
+  size_t cap = 0;
+};
+
+// Kernel families timed by the optional event profiler.
+enum Kid {
+  K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA, K_LOSS, K_BETA, K_FILL, K_OCC,
+  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_COUNT
+};
+const char* kKidNames[K_COUNT] = {
+    "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha", "loss_sum",
+    "ctc_beta", "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
+    "dw_reduce", "db_reduce", "cast"};
+
+struct Pending {
+  int kid;
+  hipEvent_t a, b;
+};
+
+}  // namespace
+
+struct pcx_ctx {
+  // workspace
+  DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
+  DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
+  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart;
+  Meta* host_meta = nullptr;  // pinned
+  // forward state kept for backward / getters
+  bool fwd_ok = false;
+  bool bwd_done = false;
+  hipStream_t stream = nullptr;
+  const void* X = nullptr;
+  const void* W = nullptr;
+  const void* b = nullptr;
+  int dtype = 0;
+  int M = 0, D = 0, V = 0, N = 0, blank = 0, chunk = 1, K = 0, max_L = 0, max_T = 0;
+  long long L_tot = 0, dp_total = 0;
+  int nspan = 0;
+  // profiling
+  bool prof = false;
+  std::vector<Pending> pending;
+  std::vector<hipEvent_t> pool;
+  double prof_ms[K_COUNT] = {0};
+  long long prof_n[K_COUNT] = {0};
+};
+
+namespace {
+
+size_t total_bytes(const pcx_ctx* c) {
+  const DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
+                          &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
+                          &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
+                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart};
+  size_t t = 0;
+  for (const DevBuf* b : bufs) t += b->cap;
+  return t;
+}
+
+pcx_status ensure(pcx_ctx* c, DevBuf& b, size_t bytes, hipStream_t st) {
+  if (bytes == 0) bytes = 16;
+  if (b.cap >= bytes) return PCX_OK;
+  if (b.p) {
+    PCX_HIP(hipStreamSynchronize(st));
+    PCX_HIP(hipFree(b.p));
+    b.p = nullptr;
+    b.cap = 0;
+  }
+  bytes = (bytes + 255) & ~size_t(255);
+  hipError_t e = hipMalloc(&b.p, bytes);
+  if (e != hipSuccess) {
+    b.p = nullptr;
+    return fail(PCX_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  }
+  b.cap = bytes;
+  (void)c;
+  return PCX_OK;
+}
+
+hipEvent_t take_event(pcx_ctx* c) {
+  if (!c->pool.empty()) {
+    hipEvent_t e = c->pool.back();
+    c->pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Collect finished event pairs into the per-kernel totals.
+void prof_drain(pcx_ctx* c) {
+  for (Pending& p : c->pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+      c->prof_ms[p.kid] += ms;
+      c->prof_n[p.kid] += 1;
+    }
+    c->pool.push_back(p.a);
+    c->pool.push_back(p.b);
+  }
+  c->pending.clear();
+}
+
+// RAII bracket of one kernel launch with events on the launch stream.
+struct Timed {
+  pcx_ctx* c;
+  int kid;
+  hipStream_t st;
+  hipEvent_t a = nullptr;
+  Timed(pcx_ctx* c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
+    if (c->prof) {
+      a = take_event(c);
+      if (a) (void)hipEventRecord(a, st);
+    }
+  }
+  ~Timed() {
+    if (c->prof && a) {
+      hipEvent_t b = take_event(c);
+      if (b) {
+        (void)hipEventRecord(b, st);
+        c->pending.push_back({kid, a, b});
+      } else {
+        c->pool.push_back(a);
+      }
+    }
+  }
+};
+
+#define LAUNCH(kid, call)                                                          \
+  do {                                                                             \
+    hipError_t e_;                                                                 \
+    {                                                                              \
+      Timed t_(ctx, kid, st);                                                      \
+      e_ = (call);                                                                 \
+    }                                                                              \
+    if (e_ != hipSuccess)                                                          \
+      return fail(PCX_ERR_HIP, "%s launch failed: %s", kKidNames[kid],             \
+                  hipGetErrorString(e_));                                          \
+  } while (0)
+
+#define ENSURE(buf, bytes)                                      \
+  do {                                                          \
+    pcx_status s_ = ensure(ctx, ctx->buf, (size_t)(bytes), st); \
+    if (s_ != PCX_OK) return s_;                                \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* pcx_last_error(void) { return g_last_error.c_str(); }
+
+pcx_status pcx_create(pcx_ctx** out_ctx) {
+  g_last_error.clear();
+  if (!out_ctx) return fail(PCX_ERR_ARG, "out_ctx is NULL");
+  // No HIP call here: device and pinned memory are taken on first use.
+  pcx_ctx* c = new (std::nothrow) pcx_ctx();
+  if (!c) return fail(PCX_ERR_ARG, "out of host memory");
+  *out_ctx = c;
+  return PCX_OK;
+}
+
+void pcx_destroy(pcx_ctx* c) {
+  if (!c) return;
+  if (c->host_meta || c->meta.p) (void)hipDeviceSynchronize();
+  DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
+                    &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha, &c->beta,
+                    &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
+                    &c->dXacc, &c->dwpart, &c->dbpart};
+  for (DevBuf* b : bufs)
+    if (b->p) (void)hipFree(b->p);
+  for (Pending& p : c->pending) {
+    (void)hipEventDestroy(p.a);
+    (void)hipEventDestroy(p.b);
+  }
+  for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+  if (c->host_meta) (void)hipHostFree(c->host_meta);
+  delete c;
+}
+
+pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b, int32_t dtype,
+                       int64_t M, int64_t D, int64_t V, int32_t N, const int32_t* tgt_off,
+                       const int32_t* tgt, int64_t L_tot, const int32_t* frame_counts,
+                       int32_t blank, int32_t chunk, void* stream, double* loss,
+                       pcx_fwd_info* info) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  ctx->fwd_ok = false;
+  ctx->bwd_done = false;
+  if (dtype != PCX_F32 && dtype != PCX_BF16)
+    return fail(PCX_ERR_DTYPE, "dtype %d is not supported (fp32 or bf16 only)", (int)dtype);
+  if (M < 0 || D < 1 || V < 1 || N < 0 || L_tot < 0)
+    return fail(PCX_ERR_ARG, "bad sizes M=%lld D=%lld V=%lld N=%d L_tot=%lld", (long long)M,
+                (long long)D, (long long)V, (int)N, (long long)L_tot);
+  if (M > INT_MAX / 2 || D > INT_MAX / 2 || V > INT_MAX / 2 || L_tot > INT_MAX / 2)
+    return fail(PCX_ERR_ARG, "sizes exceed the 32-bit index range");
+  if (blank < 0 || blank >= V) return fail(PCX_ERR_ARG, "blank %d outside [0, V)", (int)blank);
+  if (chunk < 1) return fail(PCX_ERR_ARG, "chunk must be >= 1");
+  if (!tgt_off) return fail(PCX_ERR_ARG, "tgt_off is NULL");
+  if (N > 0 && !frame_counts) return fail(PCX_ERR_ARG, "frame_counts is NULL");
+  if (L_tot > 0 && !tgt) return fail(PCX_ERR_ARG, "tgt is NULL");
+  if (M > 0 && (!X || !W)) return fail(PCX_ERR_ARG, "X / W is NULL");
+  hipStream_t st = (hipStream_t)stream;
+  const int iM = (int)M, iD = (int)D, iV = (int)V;
+  if (!ctx->host_meta) {
+    hipError_t e = hipHostMalloc((void**)&ctx->host_meta, sizeof(Meta), hipHostMallocDefault);
+    if (e != hipSuccess) {
+      ctx->host_meta = nullptr;
+      return fail(PCX_ERR_HIP, "hipHostMalloc failed: %s", hipGetErrorString(e));
+    }
+  }
+
+  ENSURE(meta, sizeof(Meta));
+  ENSURE(row_off, (N + 1) * sizeof(int));
+  ENSURE(flags, (N + 1) * sizeof(uint8_t));
+  ENSURE(dp_off, (N + 1) * sizeof(long long));
+  ENSURE(col2sel, (size_t)V * sizeof(int));
+  const long long Ucap = (L_tot + 1 < V) ? L_tot + 1 : V;
+  ENSURE(U, Ucap * sizeof(int));
+  ENSURE(tgt_rel, (L_tot + 1) * sizeof(int));
+  ENSURE(tgt_off, (N + 1) * sizeof(int));
+  Meta* dmeta = (Meta*)ctx->meta.p;
+  // The context keeps its own copy of the offsets for the backward pass.
+  PCX_HIP(hipMemcpyAsync(ctx->tgt_off.p, tgt_off, (N + 1) * sizeof(int), hipMemcpyDeviceToDevice,
+                         st));
+
+  LAUNCH(K_PREPARE, launch_prepare(st, N, iM, iV, blank, L_tot, tgt_off, tgt, frame_counts,
+                                   (int*)ctx->row_off.p, (uint8_t*)ctx->flags.p,
+                                   (long long*)ctx->dp_off.p, (int*)ctx->col2sel.p,
+                                   (int*)ctx->U.p, (int*)ctx->tgt_rel.p, dmeta));
+  PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
+  PCX_HIP(hipStreamSynchronize(st));
+  const Meta hm = *ctx->host_meta;
+  if (hm.err & ERRBIT_LENGTHS)
+    return fail(PCX_ERR_LENGTHS, "frame counts must be positive and sum to M=%d", iM);
+  if (hm.err & ERRBIT_TARGET)
+    return fail(PCX_ERR_TARGET,
+                "targets invalid: labels must lie in [0, V) without blank and offsets must be "
+                "monotone from 0 to L_tot");
+  if (hm.max_L > PCX_MAX_TARGET_LEN)
+    return fail(PCX_ERR_LIMIT, "target of %d labels exceeds the supported %d", hm.max_L,
+                PCX_MAX_TARGET_LEN);
+  const int K = hm.K;
+  ctx->K = K;
+  ctx->max_L = hm.max_L;
+  ctx->max_T = hm.max_T;
+  ctx->dp_total = hm.dp_total;
+
+  const int nspan = (iV + LSE_SPAN - 1) / LSE_SPAN;
+  ctx->nspan = nspan;
+  ENSURE(part, (size_t)M * nspan * sizeof(double2));
+  ENSURE(lam, (size_t)M * sizeof(double));
+  ENSURE(lamf, (size_t)M * sizeof(float));
+  ENSURE(S, (size_t)K * M * sizeof(float));
+  ENSURE(alpha, (size_t)hm.dp_total * sizeof(double));
+  ENSURE(utt_loss, (size_t)(N + 1) * sizeof(double));
+  ENSURE(utt_logp, (size_t)(N + 1) * sizeof(double));
+  ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
+
+  if (M > 0) {
+    LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
+                                     (float*)ctx->S.p, (double2*)ctx->part.p, nspan));
+    LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,
+                                   (double*)ctx->lam.p, (float*)ctx->lamf.p));
+    LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
+  }
+  LAUNCH(K_ALPHA, launch_alpha(st, (const float*)ctx->S.p, iM, N, hm.max_L,
+                               (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                               (const int*)ctx->tgt_rel.p,
+                               (const uint8_t*)ctx->flags.p, (const long long*)ctx->dp_off.p,
+                               (double*)ctx->alpha.p, (double*)ctx->utt_loss.p,
+                               (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p));
+  LAUNCH(K_LOSS, launch_loss_sum(st, N, (const double*)ctx->utt_loss.p,
+                                 (const int*)ctx->utt_status.p, dmeta));
+  PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
+  PCX_HIP(hipStreamSynchronize(st));
+  const Meta fm = *ctx->host_meta;
+
+  ctx->stream = st;
+  ctx->X = X;
+  ctx->W = W;
+  ctx->b = b;
+  ctx->dtype = dtype;
+  ctx->M = iM;
+  ctx->D = iD;
+  ctx->V = iV;
+  ctx->N = N;
+  ctx->blank = blank;
+  ctx->chunk = chunk < iV ? chunk : iV;
+  ctx->L_tot = L_tot;
+  ctx->fwd_ok = true;
+  if (loss) *loss = fm.loss;
+  if (info) {
+    info->K = K;
+    info->n_unalignable = fm.n_unalignable;
+    info->n_nonfinite = fm.n_nonfinite;
+    info->max_target_len = hm.max_L;
+    info->workspace_bytes = total_bytes(ctx);
+  }
+  return PCX_OK;
+}
+
+pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void* db,
+                        void* stream) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "pcx_backward needs a successful pcx_forward");
+  hipStream_t st = (hipStream_t)stream;
+  const int M = ctx->M, D = ctx->D, V = ctx->V, N = ctx->N, K = ctx->K, dt = ctx->dtype;
+  const int C = ctx->chunk;
+  const size_t esz = dt == PCX_F32 ? 4 : 2;
+  if (!dX && !dW && !db) return PCX_OK;
+  if (M == 0) {
+    // No frames: every head gradient is zero.
+    if (dW) PCX_HIP(hipMemsetAsync(dW, 0, (size_t)V * D * esz, st));
+    if (db) PCX_HIP(hipMemsetAsync(db, 0, (size_t)V * esz, st));
+    return PCX_OK;
+  }
+  const int* row_off = (const int*)ctx->row_off.p;
+  const int* toff = (const int*)ctx->tgt_off.p;
+  const int* trel = (const int*)ctx->tgt_rel.p;
+  const int* ustat = (const int*)ctx->utt_status.p;
+  const long long* dpo = (const long long*)ctx->dp_off.p;
+  const float* S = (const float*)ctx->S.p;
+
+  ENSURE(beta, (size_t)ctx->dp_total * sizeof(double));
+  ENSURE(Gam, (size_t)K * M * sizeof(float));
+  ENSURE(g, (size_t)M * sizeof(double));
+  LAUNCH(K_BETA, launch_beta(st, S, M, N, ctx->max_L, row_off, toff, trel, ustat, dpo,
+                             (double*)ctx->beta.p));
+  LAUNCH(K_FILL, launch_fill_f32(st, (float*)ctx->Gam.p, (long long)K * M, 0.f));
+  LAUNCH(K_OCC, launch_occupancy(st, S, M, N, ctx->max_T, ctx->max_L, row_off, toff, trel, ustat,
+                                 (const double*)ctx->utt_logp.p, dpo,
+                                 (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
+                                 (float*)ctx->Gam.p, (double*)ctx->g.p));
+
+  const int mtiles = (M + GEMM_BM - 1) / GEMM_BM;
+  ENSURE(dZ, (size_t)M * C * esz);
+  ENSURE(dbpart, (size_t)mtiles * C * sizeof(float));
+  float* dxacc = nullptr;
+  if (dX) {
+    if (dt == PCX_F32) {
+      dxacc = (float*)dX;
+    } else {
+      ENSURE(dXacc, (size_t)M * D * sizeof(float));
+      dxacc = (float*)ctx->dXacc.p;
+    }
+  }
+  // Split of the frame reduction of dW: enough work-groups to fill the chip,
+  // at least 1024 frames per split; fixed for a given shape.
+  const int wtiles = ((C + GEMM_BM - 1) / GEMM_BM) * ((D + GEMM_BN - 1) / GEMM_BN);
+  int splitk = (1024 + wtiles - 1) / wtiles;
+  const int maxsplit = (M + 1023) / 1024;
+  if (splitk > maxsplit) splitk = maxsplit;
+  if (splitk < 1) splitk = 1;
+  if (dW) ENSURE(dwpart, (size_t)splitk * C * D * sizeof(float));
+
+  const int nchunks = (V + C - 1) / C;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    const int c0 = ch * C, c1 = (c0 + C < V) ? c0 + C : V;
+    LAUNCH(K_RECOMPUTE,
+           launch_recompute(st, dt, ctx->X, ctx->W, ctx->b, M, D, c0, c1,
+                            (const int*)ctx->col2sel.p, (const float*)ctx->lamf.p,
+                            (const double*)ctx->g.p, S, (const float*)ctx->Gam.p, grad_loss,
+                            ctx->dZ.p, C, (float*)ctx->dbpart.p));
+    if (dX) LAUNCH(K_DX, launch_dx(st, dt, ctx->dZ.p, C, ctx->W, M, D, c0, c1, dxacc, ch == 0));
+    if (dW) {
+      LAUNCH(K_DW, launch_dw(st, dt, ctx->dZ.p, C, ctx->X, M, D, c0, c1,
+                             (float*)ctx->dwpart.p, splitk));
+      LAUNCH(K_DW_REDUCE, launch_dw_reduce(st, dt, (const float*)ctx->dwpart.p, splitk, c1 - c0,
+                                           D, dW, c0));
+    }
+    if (db)
+      LAUNCH(K_DB_REDUCE, launch_db_reduce(st, dt, (const float*)ctx->dbpart.p, mtiles, c1 - c0,
+                                           C, db, c0));
+  }
+  if (dX && dt != PCX_F32)
+    LAUNCH(K_CAST, launch_cast_out(st, dt, dxacc, dX, (long long)M * D));
+  ctx->bwd_done = true;
+  return PCX_OK;
+}
+
+// ------------------------------------------------------------- profiling
+pcx_status pcx_profile_enable(pcx_ctx* ctx, int32_t on) {
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  ctx->prof = on != 0;
+  return PCX_OK;
+}
+
+pcx_status pcx_profile_reset(pcx_ctx* ctx) {
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  prof_drain(ctx);
+  for (int i = 0; i < K_COUNT; ++i) {
+    ctx->prof_ms[i] = 0.0;
+    ctx->prof_n[i] = 0;
+  }
+  return PCX_OK;
+}
+
+int32_t pcx_profile_count(void) { return K_COUNT; }
+
+pcx_status pcx_profile_read(pcx_ctx* ctx, int32_t i, const char** name, double* total_ms,
+                            int64_t* launches) {
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (i < 0 || i >= K_COUNT) return fail(PCX_ERR_ARG, "kernel index %d out of range", (int)i);
+  prof_drain(ctx);
+  if (name) *name = kKidNames[i];
+  if (total_ms) *total_ms = ctx->prof_ms[i];
+  if (launches) *launches = ctx->prof_n[i];
+  return PCX_OK;
+}
+
+// ------------------------------------------------------------- getters
+static pcx_status get_copy(pcx_ctx* ctx, const DevBuf& b, size_t n, size_t esz, void* out,
+                           int64_t capacity, bool need_bwd) {
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "no completed forward pass");
+  if (need_bwd && !ctx->bwd_done) return fail(PCX_ERR_STATE, "no completed backward pass");
+  if (!out || capacity < (int64_t)n) return fail(PCX_ERR_ARG, "output buffer too small (%lld < %zu)",
+                                                  (long long)capacity, n);
+  if (n == 0) return PCX_OK;
+  PCX_HIP(hipStreamSynchronize(ctx->stream));
+  PCX_HIP(hipMemcpy(out, b.p, n * esz, hipMemcpyDeviceToHost));
+  return PCX_OK;
+}
+
+pcx_status pcx_get_selected(pcx_ctx* ctx, int32_t* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->U : DevBuf(), ctx ? ctx->K : 0, 4, out, capacity, false);
+}
+pcx_status pcx_get_relabeled(pcx_ctx* ctx, int32_t* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->tgt_rel : DevBuf(), ctx ? ctx->L_tot : 0, 4, out, capacity,
+                  false);
+}
+pcx_status pcx_get_alignable(pcx_ctx* ctx, uint8_t* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->flags : DevBuf(), ctx ? ctx->N : 0, 1, out, capacity, false);
+}
+pcx_status pcx_get_utt_losses(pcx_ctx* ctx, double* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->utt_loss : DevBuf(), ctx ? ctx->N : 0, 8, out, capacity, false);
+}
+pcx_status pcx_get_utt_status(pcx_ctx* ctx, int32_t* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->utt_status : DevBuf(), ctx ? ctx->N : 0, 4, out, capacity,
+                  false);
+}
+pcx_status pcx_get_normalizer(pcx_ctx* ctx, double* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->lam : DevBuf(), ctx ? ctx->M : 0, 8, out, capacity, false);
+}
+pcx_status pcx_get_scores(pcx_ctx* ctx, float* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->S : DevBuf(), ctx ? (size_t)ctx->K * ctx->M : 0, 4, out,
+                  capacity, false);
+}
+pcx_status pcx_get_occupancy(pcx_ctx* ctx, float* out, int64_t capacity) {
+  return get_copy(ctx, ctx ? ctx->Gam : DevBuf(), ctx ? (size_t)ctx->K * ctx->M : 0, 4, out,
+                  capacity, true);
+}
+
+}  // extern "C"

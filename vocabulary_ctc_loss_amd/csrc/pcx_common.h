@@ -1,0 +1,123 @@
+// Shared device helpers and kernel launchers of the pcx library (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pcx {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 values travel as their 16-bit patterns.
+typedef uint16_t bf16_t;
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+
+// Round-to-nearest-even fp32 -> bf16 (NaNs stay NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static constexpr int VEC = 4;  // elements per 16-byte vector
+  __device__ static float to_f32(float x) { return x; }
+  __device__ static float from_f32(float x) { return x; }
+};
+template <> struct Elem<bf16_t> {
+  static constexpr int VEC = 8;
+  __device__ static float to_f32(bf16_t x) { return bf16_to_f32(x); }
+  __device__ static bf16_t from_f32(float x) { return f32_to_bf16(x); }
+};
+
+// Error bits raised by the validation kernels.
+enum : int {
+  ERRBIT_TARGET = 1,   // label out of range / blank in target / bad offsets
+  ERRBIT_LENGTHS = 2,  // frame count <= 0 or sum != M
+};
+
+// Small device-resident summary read back by the host after selection and
+// after the loss reduction.
+struct Meta {
+  int err;
+  int K;
+  int max_L;
+  int max_T;
+  long long dp_total;   // sum_n T_n * (2 L_n + 1)
+  double loss;
+  int n_unalignable;
+  int n_nonfinite;
+  int pad[2];
+};
+
+// Utterance status codes.
+enum : int { UTT_OK = 0, UTT_UNALIGNABLE = 1, UTT_NONFINITE = 2 };
+
+// GEMM tile geometry shared by every MFMA kernel: 256 threads as a 2 x 2 grid
+// of waves, each wave owning a 64 x 64 block of 2 x 2 MFMA 32x32 tiles.
+constexpr int GEMM_BM = 128;
+constexpr int GEMM_BN = 128;
+constexpr int GEMM_THREADS = 256;
+// Columns folded into one normalizer partial by the forward kernel.
+constexpr int LSE_SPAN = 2048;
+// Frames per work-group of the occupancy kernel.
+constexpr int OCC_FRAMES = 32;
+
+// ---------------------------------------------------------------- launchers
+// Selection / validation (pcx_select.hip).
+hipError_t launch_prepare(hipStream_t st, int N, int M, int V, int blank, long long L_tot,
+                          const int* tgt_off, const int* tgt, const int* frame_counts,
+                          int* row_off, uint8_t* flags, long long* dp_off,
+                          int* col2sel, int* U, int* tgt_rel, Meta* meta);
+
+// Forward head (pcx_gemm.hip).
+hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W,
+                          const void* b, int M, int D, int V, const int* col2sel,
+                          float* Zsel, double2* part, int nspan);
+hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan,
+                         double* lam, float* lamf);
+hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int M);
+
+// Backward head (pcx_gemm.hip).
+hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W,
+                            const void* b, int M, int D, int c0, int c1,
+                            const int* col2sel, const float* lamf, const double* g,
+                            const float* S, const float* Gam, double grad,
+                            void* dZ, int ldz, float* dbpart);
+hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
+                     int M, int D, int c0, int c1, float* dXacc, int first);
+hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
+                     int M, int D, int c0, int c1, float* part, int splitk);
+hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk,
+                            int rows, int D, void* dW, long long row_base);
+hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int mtiles,
+                            int cols, int ld, void* db, long long col_base);
+hipError_t launch_cast_out(hipStream_t st, int dtype, const float* src, void* dst,
+                           long long n);
+
+// Alignment DP (pcx_ctc.hip).
+hipError_t launch_alpha(hipStream_t st, const float* S, int M, int N, int max_L,
+                        const int* row_off, const int* tgt_off, const int* tgt_rel,
+                        const uint8_t* flags, const long long* dp_off, double* alpha,
+                        double* utt_loss, double* utt_logp, int* utt_status);
+hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss,
+                           const int* utt_status, Meta* meta);
+hipError_t launch_beta(hipStream_t st, const float* S, int M, int N, int max_L,
+                       const int* row_off, const int* tgt_off, const int* tgt_rel,
+                       const int* utt_status, const long long* dp_off, double* beta);
+hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int max_T,
+                            int max_L, const int* row_off, const int* tgt_off,
+                            const int* tgt_rel, const int* utt_status,
+                            const double* utt_logp, const long long* dp_off,
+                            const double* alpha, const double* beta, float* Gam,
+                            double* g);
+hipError_t launch_fill_f32(hipStream_t st, float* p, long long n, float v);
+
+}  // namespace pcx
