@@ -63,7 +63,7 @@ struct pcx_ctx {
   // workspace
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
-  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart;
+  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt;
   Meta* host_meta = nullptr;  // pinned
   // forward state kept for backward / getters
   bool fwd_ok = false;
@@ -90,7 +90,7 @@ size_t total_bytes(const pcx_ctx* c) {
   const DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                           &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
-                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart};
+                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -206,7 +206,7 @@ void pcx_destroy(pcx_ctx* c) {
   DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                     &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha, &c->beta,
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
-                    &c->dXacc, &c->dwpart, &c->dbpart};
+                    &c->dXacc, &c->dwpart, &c->dbpart, &c->wt};
   for (DevBuf* b : bufs)
     if (b->p) (void)hipFree(b->p);
   for (Pending& p : c->pending) {
@@ -383,6 +383,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       dxacc = (float*)dX;
     } else {
       ENSURE(dXacc, (size_t)M * D * sizeof(float));
+      ENSURE(wt, (size_t)D * C * esz);
       dxacc = (float*)ctx->dXacc.p;
     }
   }
@@ -403,7 +404,9 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
                             (const int*)ctx->col2sel.p, (const float*)ctx->lamf.p,
                             (const double*)ctx->g.p, S, (const float*)ctx->Gam.p, grad_loss,
                             ctx->dZ.p, C, (float*)ctx->dbpart.p));
-    if (dX) LAUNCH(K_DX, launch_dx(st, dt, ctx->dZ.p, C, ctx->W, M, D, c0, c1, dxacc, ch == 0));
+    if (dX)
+      LAUNCH(K_DX, launch_dx(st, dt, ctx->dZ.p, C, ctx->W, M, D, c0, c1, dxacc, ch == 0,
+                             ctx->wt.p));
     if (dW) {
       LAUNCH(K_DW, launch_dw(st, dt, ctx->dZ.p, C, ctx->X, M, D, c0, c1,
                              (float*)ctx->dwpart.p, splitk));

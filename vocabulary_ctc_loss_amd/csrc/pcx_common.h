@@ -91,8 +91,9 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const int* col2sel, const float* lamf, const double* g,
                             const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart);
+// wt: D x ldz scratch for the transposed weight chunk (bf16 only).
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
-                     int M, int D, int c0, int c1, float* dXacc, int first);
+                     int M, int D, int c0, int c1, float* dXacc, int first, void* wt);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
 hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk,

@@ -22,8 +22,10 @@
 // LDS; within a k-tile, lane half h (lanes 32h..32h+31) feeds the k values of
 // the half-row it owns, which is just a fixed relabelling of the reduction
 // index shared by both operands.  Operands are K-contiguous (row-major along
-// the reduction) or MN-contiguous; the latter are transposed on the way into
-// LDS so that the MFMA side always reads 16-byte vectors.
+// the reduction) or MN-contiguous.  fp32 MN-contiguous tiles are staged as
+// they lie ([k][mn]) and read one k row per MFMA; for bf16 the one product
+// with an MN-contiguous operand on the hot path (dX = dZ W_c) reads a
+// transposed copy of the chunk's weight rows instead.
 #include <float.h>
 #include <math.h>
 
@@ -69,13 +71,26 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
   return xcd * per + min(xcd, rem) + local;
 }
 
-// Global -> registers -> LDS staging of one 128 (mn) x BK (k) operand tile.
+// LDS layouts of one staged 128 (mn) x BK (k) operand tile:
+//  * row layout [mn][LDK], k contiguous: K-contiguous operands, and bf16
+//    MN-contiguous operands (transposed element by element on the way in);
+//  * column layout [k][LDM], mn contiguous: fp32 MN-contiguous operands,
+//    written straight from the 16-byte global loads.
+constexpr int LDM = 128 + 4;
+
+template <typename T, bool KMAJOR>
+struct ColLayout {
+  static constexpr bool value = !KMAJOR && sizeof(T) == 4;
+};
+
+// Global -> registers -> LDS staging of one operand tile.
 // KMAJOR: element (mn, k) is g[mn * ld + k]; otherwise g[k * ld + mn].
 template <typename T, bool KMAJOR>
 struct Stage {
   static constexpr int VEC = Geo<T>::VEC;
   static constexpr int BK = Geo<T>::BK;
   static constexpr int LDK = Geo<T>::LDK;
+  static constexpr bool COL = ColLayout<T, KMAJOR>::value;
 
   __device__ static __forceinline__ void coords(int q, int& mn, int& k) {
     const int v = threadIdx.x + NT * q;
@@ -133,6 +148,8 @@ struct Stage {
       coords(q, mn, k);
       if (KMAJOR) {
         *reinterpret_cast<uint4*>(s + mn * LDK + k) = r[q].u;
+      } else if (COL) {
+        *reinterpret_cast<uint4*>(s + k * LDM + mn) = r[q].u;
       } else {
 #pragma unroll
         for (int e = 0; e < VEC; ++e) s[(mn + e) * LDK + k] = reinterpret_cast<const T*>(&r[q])[e];
@@ -142,25 +159,39 @@ struct Stage {
 };
 
 // MFMA work on one staged k-tile for this wavefront's 64 x 64 block.
-template <typename T>
+//
+// fp32: a k-tile holds 32 k values; the 16 v_mfma_f32_32x32x2f32 steps s of
+// a lane in half h consume k = 16*(s/8) + 8*h + s%8.  Four consecutive steps
+// read four consecutive k, so a row-layout fragment is one 16-byte LDS read,
+// and in the column layout the two lane halves read rows 8 apart, which lands
+// them on disjoint LDS banks.
+template <typename T, bool ACOL, bool BCOL>
 struct Mma;
 
-template <>
-struct Mma<float> {
-  static constexpr int LDK = Geo<float>::LDK;
+template <bool COL>
+__device__ __forceinline__ f32x4 frag_f32(const float* __restrict__ S, int row, int h, int kc) {
+  constexpr int LDK = Geo<float>::LDK;
+  const int k0 = ((kc >> 1) << 4) + (h << 3) + ((kc & 1) << 2);
+  if (!COL) return *reinterpret_cast<const f32x4*>(S + row * LDK + k0);
+  f32x4 v;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = S[(k0 + e) * LDM + row];
+  return v;
+}
+
+template <bool ACOL, bool BCOL>
+struct Mma<float, ACOL, BCOL> {
   __device__ static __forceinline__ void run(const float* __restrict__ As,
                                              const float* __restrict__ Bs, f32x16 (&acc)[2][2],
                                              int wm, int wn) {
     const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
-    const float* a0 = As + (wm * 64 + i) * LDK + h * 16;
-    const float* b0 = Bs + (wn * 64 + i) * LDK + h * 16;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
       f32x4 a[2], b[2];
-      a[0] = *reinterpret_cast<const f32x4*>(a0 + kc * 4);
-      a[1] = *reinterpret_cast<const f32x4*>(a0 + 32 * LDK + kc * 4);
-      b[0] = *reinterpret_cast<const f32x4*>(b0 + kc * 4);
-      b[1] = *reinterpret_cast<const f32x4*>(b0 + 32 * LDK + kc * 4);
+      a[0] = frag_f32<ACOL>(As, wm * 64 + i, h, kc);
+      a[1] = frag_f32<ACOL>(As, wm * 64 + 32 + i, h, kc);
+      b[0] = frag_f32<BCOL>(Bs, wn * 64 + i, h, kc);
+      b[1] = frag_f32<BCOL>(Bs, wn * 64 + 32 + i, h, kc);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
@@ -173,8 +204,10 @@ struct Mma<float> {
   }
 };
 
+// bf16: a k-tile holds 64 k values; lane half h feeds k in [32h, 32h + 32),
+// eight per v_mfma_f32_32x32x16_bf16 (row layout only).
 template <>
-struct Mma<bf16_t> {
+struct Mma<bf16_t, false, false> {
   static constexpr int LDK = Geo<bf16_t>::LDK;
   __device__ static __forceinline__ void run(const bf16_t* __restrict__ As,
                                              const bf16_t* __restrict__ Bs, f32x16 (&acc)[2][2],
@@ -208,6 +241,8 @@ __device__ __forceinline__ void gemm_tile(const T* __restrict__ A, long long lda
                                           f32x16 (&acc)[2][2], char* smem) {
   constexpr int BK = Geo<T>::BK;
   constexpr int OPER = Geo<T>::OPER;
+  constexpr bool ACOL = ColLayout<T, AK>::value;
+  constexpr bool BCOL = ColLayout<T, BK_>::value;
   T* As = reinterpret_cast<T*>(smem);
   T* Bs = As + 2 * OPER;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
@@ -233,7 +268,7 @@ __device__ __forceinline__ void gemm_tile(const T* __restrict__ A, long long lda
       Stage<T, AK>::load(A, lda, m0, m_lim, k0, k_end, a_vec, ra);
       Stage<T, BK_>::load(B, ldb, n0, n_lim, k0, k_end, b_vec, rb);
     }
-    Mma<T>::run(As + cur * OPER, Bs + cur * OPER, acc, wm, wn);
+    Mma<T, ACOL, BCOL>::run(As + cur * OPER, Bs + cur * OPER, acc, wm, wn);
     if (more) {
       Stage<T, AK>::store(As + (cur ^ 1) * OPER, ra);
       Stage<T, BK_>::store(Bs + (cur ^ 1) * OPER, rb);
@@ -436,18 +471,20 @@ __global__ __launch_bounds__(NT, 2) void k_recompute(
   if (hh == 0 && v < c1) dbpart[(long long)mt * ldz + (v - c0)] = colsum + s_db[c];
 }
 
-// dXacc[m][d] (+)= sum_{c in chunk} dZ[m][c] W[c0 + c][d].
-template <typename T>
+// dXacc[m][d] (+)= sum_{c in chunk} dZ[m][c] W[c0 + c][d].  With BKM the
+// weight operand is the transposed chunk Wt[d][c] (leading dimension ldb),
+// otherwise the chunk's rows W[c0 + c][d] (leading dimension D).
+template <typename T, bool BKM>
 __global__ __launch_bounds__(NT, 2) void k_dx(const T* __restrict__ dZ, int ldz,
-                                              const T* __restrict__ Wc, int M, int D, int Cc,
-                                              float* __restrict__ dXacc, int first, int mtiles,
-                                              int a_vec, int b_vec) {
+                                              const T* __restrict__ Wc, int ldb, int M, int D,
+                                              int Cc, float* __restrict__ dXacc, int first,
+                                              int mtiles, int a_vec, int b_vec) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = lin % mtiles, nt = lin / mtiles;
   const int m0 = mt * BM, n0 = nt * BN;
   f32x16 acc[2][2];
-  gemm_tile<T, true, false>(dZ, ldz, m0, M, Wc, D, n0, D, 0, Cc, a_vec, b_vec, acc, smem);
+  gemm_tile<T, true, BKM>(dZ, ldz, m0, M, Wc, ldb, n0, D, 0, Cc, a_vec, b_vec, acc, smem);
   const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
   const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
 #pragma unroll
@@ -518,6 +555,24 @@ __global__ void k_db_reduce(const float* __restrict__ dbpart, int mtiles, int co
   float s = 0.f;
   for (int k = 0; k < mtiles; ++k) s += dbpart[(long long)k * ld + i];
   db[col_base + i] = Elem<T>::from_f32(s);
+}
+
+// dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS).
+template <typename T>
+__global__ void k_transpose(const T* __restrict__ src, int rows, int D, T* __restrict__ dst,
+                            int ldd) {
+  __shared__ T t[64][65];
+  const int r0 = blockIdx.y * 64, d0 = blockIdx.x * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int rr = r0 + r, dd = d0 + tx;
+    t[r][tx] = (rr < rows && dd < D) ? src[(long long)rr * D + dd] : T(0);
+  }
+  __syncthreads();
+  for (int d = ty; d < 64; d += 4) {
+    const int dd = d0 + d, rr = r0 + tx;
+    if (dd < D && rr < rows) dst[(long long)dd * ldd + rr] = t[tx][d];
+  }
 }
 
 __global__ void k_cast_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, long long n) {
@@ -593,7 +648,7 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
 }
 
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W, int M,
-                     int D, int c0, int c1, float* dXacc, int first) {
+                     int D, int c0, int c1, float* dXacc, int first, void* wt) {
   const int mtiles = ceil_div(M, BM);
   const int grid = mtiles * ceil_div(D, BN);
   if (grid == 0) return hipSuccess;
@@ -602,14 +657,18 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
     const float* Wc = (const float*)W + (long long)c0 * D;
     const int av = (ldz % 4 == 0) && aligned16(dZ);
     const int bv = (D % 4 == 0) && aligned16(Wc);
-    k_dx<float><<<grid, NT, 0, st>>>((const float*)dZ, ldz, Wc, M, D, Cc, dXacc, first, mtiles,
-                                     av, bv);
+    k_dx<float, false><<<grid, NT, 0, st>>>((const float*)dZ, ldz, Wc, D, M, D, Cc, dXacc, first,
+                                            mtiles, av, bv);
   } else {
+    // bf16: stage W_c^T (D x Cc, leading dimension ldz) so both operands are
+    // K-contiguous.
     const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
+    dim3 tg(ceil_div(D, 64), ceil_div(Cc, 64));
+    k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, D, (bf16_t*)wt, ldz);
     const int av = (ldz % 8 == 0) && aligned16(dZ);
-    const int bv = (D % 8 == 0) && aligned16(Wc);
-    k_dx<bf16_t><<<grid, NT, 0, st>>>((const bf16_t*)dZ, ldz, Wc, M, D, Cc, dXacc, first, mtiles,
-                                      av, bv);
+    const int bv = (ldz % 8 == 0) && aligned16(wt);
+    k_dx<bf16_t, true><<<grid, NT, 0, st>>>((const bf16_t*)dZ, ldz, (const bf16_t*)wt, ldz, M, D,
+                                            Cc, dXacc, first, mtiles, av, bv);
   }
   return hipGetLastError();
 }
