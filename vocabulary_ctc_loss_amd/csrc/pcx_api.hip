@@ -374,7 +374,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
                                  (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
                                  (float*)ctx->Gam.p, (double*)ctx->g.p));
 
-  const int mtiles = (M + GEMM_BM - 1) / GEMM_BM;
+  const int mtiles = (M + rec_tile_rows(dt) - 1) / rec_tile_rows(dt);
   ENSURE(dZ, (size_t)M * C * esz);
   ENSURE(dbpart, (size_t)mtiles * C * sizeof(float));
   float* dxacc = nullptr;
@@ -389,7 +389,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   }
   // Split of the frame reduction of dW: enough work-groups to fill the chip,
   // at least 1024 frames per split; fixed for a given shape.
-  const int wtiles = ((C + GEMM_BM - 1) / GEMM_BM) * ((D + GEMM_BN - 1) / GEMM_BN);
+  const int wtiles = dw_tiles(dt, C, D);
   int splitk = (1024 + wtiles - 1) / wtiles;
   const int maxsplit = (M + 1023) / 1024;
   if (splitk > maxsplit) splitk = maxsplit;

@@ -60,11 +60,6 @@ struct Meta {
 // Utterance status codes.
 enum : int { UTT_OK = 0, UTT_UNALIGNABLE = 1, UTT_NONFINITE = 2 };
 
-// GEMM tile geometry shared by every MFMA kernel: 256 threads as a 2 x 2 grid
-// of waves, each wave owning a 64 x 64 block of 2 x 2 MFMA 32x32 tiles.
-constexpr int GEMM_BM = 128;
-constexpr int GEMM_BN = 128;
-constexpr int GEMM_THREADS = 256;
 // Columns folded into one normalizer partial by the forward kernel.
 constexpr int LSE_SPAN = 2048;
 // Frames per work-group of the occupancy kernel.
@@ -92,6 +87,10 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart);
 // wt: D x ldz scratch for the transposed weight chunk (bf16 only).
+// Rows of the recompute tile (one bias-gradient partial per row tile) and
+// the number of output tiles of one dW product.
+int rec_tile_rows(int dtype);
+int dw_tiles(int dtype, int C, int D);
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
                      int M, int D, int c0, int c1, float* dXacc, int first, void* wt);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,

@@ -35,25 +35,9 @@ namespace pcx {
 
 namespace {
 
-constexpr int BM = GEMM_BM;
-constexpr int BN = GEMM_BN;
-constexpr int NT = GEMM_THREADS;
-constexpr int ROW_BYTES = 128;  // one operand row of a k-tile
-constexpr int PAD_BYTES = 16;   // LDS row padding
-constexpr int TILE_LD = BM + 4; // accumulator tile in LDS, column-major [col][row]
-constexpr int EPI_BYTES = BN * TILE_LD * 4;
-
-template <typename T>
-struct Geo {
-  static constexpr int VEC = Elem<T>::VEC;
-  static constexpr int BK = ROW_BYTES / (int)sizeof(T);                 // 32 fp32 / 64 bf16
-  static constexpr int LDK = (ROW_BYTES + PAD_BYTES) / (int)sizeof(T);  // LDS row stride
-  static constexpr int OPER = 128 * LDK;                                // one operand buffer
-  static constexpr int STAGE_BYTES = 2 * 2 * OPER * (int)sizeof(T);
-};
-
 constexpr int cmax(int a, int b) { return a > b ? a : b; }
-constexpr int SMEM_BYTES = cmax(cmax(Geo<float>::STAGE_BYTES, Geo<bf16_t>::STAGE_BYTES), EPI_BYTES);
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 union Vec16 {
   uint4 u;
@@ -71,13 +55,34 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
   return xcd * per + min(xcd, rem) + local;
 }
 
-// LDS layouts of one staged 128 (mn) x BK (k) operand tile:
+// Tile configuration of one GEMM kernel: a BM x BN work-group tile computed
+// by (BM/WM) x (BN/WN) wavefronts of WM x WN, each a grid of MFMA 32 x 32
+// blocks; KB bytes of every operand row are staged per k step.
+template <typename T, int BM_, int BN_, int WM_, int WN_, int KB_, int MINWG_>
+struct Cfg {
+  using type = T;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int WGM = BM / WM, WGN = BN / WN;
+  static constexpr int WAVES = WGM * WGN;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int FM = WM / 32, FN = WN / 32;
+  static constexpr int VEC = Elem<T>::VEC;
+  static constexpr int BK = KB_ / (int)sizeof(T);          // k values per stage
+  static constexpr int LDK = (KB_ + 16) / (int)sizeof(T);  // row-layout stride
+  static constexpr int LDMA = BM + 4, LDMB = BN + 4;       // column-layout strides
+  static constexpr int OPA = cmax(BM * LDK, BK * LDMA);    // one A buffer (elements)
+  static constexpr int OPB = cmax(BN * LDK, BK * LDMB);
+  static constexpr int STAGE_BYTES = 2 * (OPA + OPB) * (int)sizeof(T);
+  static constexpr int MINWG = MINWG_;
+  static_assert(BM % WM == 0 && BN % WN == 0 && WM % 32 == 0 && WN % 32 == 0, "tile shape");
+  static_assert(sizeof(T) == 4 ? BK % 16 == 0 : BK % 32 == 0, "k step");
+};
+
+// LDS layouts of one staged ROWS (mn) x BK (k) operand tile:
 //  * row layout [mn][LDK], k contiguous: K-contiguous operands, and bf16
 //    MN-contiguous operands (transposed element by element on the way in);
-//  * column layout [k][LDM], mn contiguous: fp32 MN-contiguous operands,
+//  * column layout [k][ROWS + 4], mn contiguous: fp32 MN-contiguous operands,
 //    written straight from the 16-byte global loads.
-constexpr int LDM = 128 + 4;
-
 template <typename T, bool KMAJOR>
 struct ColLayout {
   static constexpr bool value = !KMAJOR && sizeof(T) == 4;
@@ -85,33 +90,43 @@ struct ColLayout {
 
 // Global -> registers -> LDS staging of one operand tile.
 // KMAJOR: element (mn, k) is g[mn * ld + k]; otherwise g[k * ld + mn].
-template <typename T, bool KMAJOR>
+template <class C, int ROWS, bool KMAJOR>
 struct Stage {
-  static constexpr int VEC = Geo<T>::VEC;
-  static constexpr int BK = Geo<T>::BK;
-  static constexpr int LDK = Geo<T>::LDK;
+  using T = typename C::type;
+  static constexpr int VEC = C::VEC;
+  static constexpr int BK = C::BK;
+  static constexpr int LDK = C::LDK;
+  static constexpr int LDM = ROWS + 4;
   static constexpr bool COL = ColLayout<T, KMAJOR>::value;
+  static constexpr int NV = ROWS * BK / VEC;  // 16-byte vectors per tile
+  static constexpr int Q = NV / C::THREADS;    // per thread
+  static_assert(NV % C::THREADS == 0, "staging split");
 
   __device__ static __forceinline__ void coords(int q, int& mn, int& k) {
-    const int v = threadIdx.x + NT * q;
+    const int v = threadIdx.x + C::THREADS * q;
     if (KMAJOR) {
       mn = v / (BK / VEC);
       k = (v % (BK / VEC)) * VEC;
     } else {
-      k = v / (128 / VEC);
-      mn = (v % (128 / VEC)) * VEC;
+      k = v / (ROWS / VEC);
+      mn = (v % (ROWS / VEC)) * VEC;
     }
   }
 
-  __device__ static __forceinline__ void load(const T* __restrict__ g, long long ld, int mn0,
+  // FULL: the whole tile is in bounds and 16-byte aligned (no checks).
+  template <bool FULL>
+  __device__ static __forceinline__ void load(const T* g, long long ld, int mn0,
                                               int mn_lim, int k0, int k_lim, bool vec_ok,
-                                              Vec16 (&r)[4]) {
+                                              Vec16 (&r)[Q]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       int mn, k;
       coords(q, mn, k);
       const int gm = mn0 + mn, gk = k0 + k;
-      if (KMAJOR) {
+      if (FULL) {
+        const long long off = KMAJOR ? (long long)gm * ld + gk : (long long)gk * ld + gm;
+        r[q].u = __builtin_bit_cast(uint4, *reinterpret_cast<const volatile u32x4*>(g + off));
+      } else if (KMAJOR) {
         if (vec_ok && gm < mn_lim && gk + VEC <= k_lim) {
           r[q].u = *reinterpret_cast<const uint4*>(g + (long long)gm * ld + gk);
         } else {
@@ -141,9 +156,9 @@ struct Stage {
     }
   }
 
-  __device__ static __forceinline__ void store(T* __restrict__ s, const Vec16 (&r)[4]) {
+  __device__ static __forceinline__ void store(T* __restrict__ s, const Vec16 (&r)[Q]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < Q; ++q) {
       int mn, k;
       coords(q, mn, k);
       if (KMAJOR) {
@@ -158,19 +173,13 @@ struct Stage {
   }
 };
 
-// MFMA work on one staged k-tile for this wavefront's 64 x 64 block.
-//
-// fp32: a k-tile holds 32 k values; the 16 v_mfma_f32_32x32x2f32 steps s of
-// a lane in half h consume k = 16*(s/8) + 8*h + s%8.  Four consecutive steps
-// read four consecutive k, so a row-layout fragment is one 16-byte LDS read,
-// and in the column layout the two lane halves read rows 8 apart, which lands
-// them on disjoint LDS banks.
-template <typename T, bool ACOL, bool BCOL>
-struct Mma;
-
-template <bool COL>
+// One fp32 operand fragment: the values lane (i, h) feeds to four
+// consecutive MFMA steps.  Within a stage of BK k values, step s of lane half
+// h consumes k = 16*(s/8) + 8*h + s%8: four consecutive steps read four
+// consecutive k (one 16-byte read in the row layout), and in the column
+// layout the two lane halves read rows 8 apart, on disjoint LDS banks.
+template <bool COL, int LDK, int LDM>
 __device__ __forceinline__ f32x4 frag_f32(const float* __restrict__ S, int row, int h, int kc) {
-  constexpr int LDK = Geo<float>::LDK;
   const int k0 = ((kc >> 1) << 4) + (h << 3) + ((kc & 1) << 2);
   if (!COL) return *reinterpret_cast<const f32x4*>(S + row * LDK + k0);
   f32x4 v;
@@ -179,120 +188,151 @@ __device__ __forceinline__ f32x4 frag_f32(const float* __restrict__ S, int row, 
   return v;
 }
 
-template <bool ACOL, bool BCOL>
-struct Mma<float, ACOL, BCOL> {
-  __device__ static __forceinline__ void run(const float* __restrict__ As,
-                                             const float* __restrict__ Bs, f32x16 (&acc)[2][2],
-                                             int wm, int wn) {
-    const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
+// MFMA work of one staged k step for this wavefront's WM x WN block.
+template <class C, bool ACOL, bool BCOL>
+__device__ __forceinline__ void mma_stage(const typename C::type* __restrict__ As,
+                                          const typename C::type* __restrict__ Bs,
+                                          f32x16 (&acc)[C::FM][C::FN], int wm, int wn) {
+  using T = typename C::type;
+  const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
+  if constexpr (sizeof(T) == 4) {
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) {
-      f32x4 a[2], b[2];
-      a[0] = frag_f32<ACOL>(As, wm * 64 + i, h, kc);
-      a[1] = frag_f32<ACOL>(As, wm * 64 + 32 + i, h, kc);
-      b[0] = frag_f32<BCOL>(Bs, wn * 64 + i, h, kc);
-      b[1] = frag_f32<BCOL>(Bs, wn * 64 + 32 + i, h, kc);
+    for (int kc = 0; kc < C::BK / 8; ++kc) {
+      f32x4 a[C::FM], b[C::FN];
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+        a[fi] = frag_f32<ACOL, C::LDK, C::LDMA>(As, wm * C::WM + fi * 32 + i, h, kc);
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj)
+        b[fj] = frag_f32<BCOL, C::LDK, C::LDMB>(Bs, wn * C::WN + fj * 32 + i, h, kc);
 #pragma unroll
       for (int e = 0; e < 4; ++e)
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
-          for (int ni = 0; ni < 2; ++ni)
-            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[mi][e], b[ni][e], acc[mi][ni],
+          for (int fj = 0; fj < C::FN; ++fj)
+            acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x2f32(a[fi][e], b[fj][e], acc[fi][fj],
                                                                0, 0, 0);
     }
-  }
-};
-
-// bf16: a k-tile holds 64 k values; lane half h feeds k in [32h, 32h + 32),
-// eight per v_mfma_f32_32x32x16_bf16 (row layout only).
-template <>
-struct Mma<bf16_t, false, false> {
-  static constexpr int LDK = Geo<bf16_t>::LDK;
-  __device__ static __forceinline__ void run(const bf16_t* __restrict__ As,
-                                             const bf16_t* __restrict__ Bs, f32x16 (&acc)[2][2],
-                                             int wm, int wn) {
-    const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
-    const bf16_t* a0 = As + (wm * 64 + i) * LDK + h * 32;
-    const bf16_t* b0 = Bs + (wn * 64 + i) * LDK + h * 32;
+  } else {
+    // bf16 (row layout only): lane half h feeds k in [h*BK/2, (h+1)*BK/2),
+    // eight per v_mfma_f32_32x32x16_bf16.
+    static_assert(!ACOL && !BCOL, "bf16 operands use the row layout");
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      bf16x8 a[2], b[2];
-      a[0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a0 + j * 8));
-      a[1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(a0 + 32 * LDK + j * 8));
-      b[0] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(b0 + j * 8));
-      b[1] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(b0 + 32 * LDK + j * 8));
+    for (int j = 0; j < C::BK / 16; ++j) {
+      bf16x8 a[C::FM], b[C::FN];
 #pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
+      for (int fi = 0; fi < C::FM; ++fi)
+        a[fi] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(As + (wm * C::WM + fi * 32 + i) * C::LDK +
+                                                    h * (C::BK / 2) + j * 8));
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+      for (int fj = 0; fj < C::FN; ++fj)
+        b[fj] = __builtin_bit_cast(
+            bf16x8, *reinterpret_cast<const uint4*>(Bs + (wn * C::WN + fj * 32 + i) * C::LDK +
+                                                    h * (C::BK / 2) + j * 8));
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < C::FN; ++fj)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi], b[fj], acc[fi][fj], 0, 0, 0);
     }
   }
-};
+}
 
-// acc = A[m0:m0+128, k] . B[n0:n0+128, k]^T over k in [k_begin, k_end).
-// Rows/columns past the limits and k past k_end read as zero.  Ends with a
-// barrier, so the caller may reuse `smem` right away.
-template <typename T, bool AK, bool BK_>
-__device__ __forceinline__ void gemm_tile(const T* __restrict__ A, long long lda, int m0, int m_lim,
-                                          const T* __restrict__ B, long long ldb, int n0, int n_lim,
-                                          int k_begin, int k_end, bool a_vec, bool b_vec,
-                                          f32x16 (&acc)[2][2], char* smem) {
-  constexpr int BK = Geo<T>::BK;
-  constexpr int OPER = Geo<T>::OPER;
-  constexpr bool ACOL = ColLayout<T, AK>::value;
-  constexpr bool BCOL = ColLayout<T, BK_>::value;
+template <class C, bool AK, bool BK_, bool FULL>
+__device__ __forceinline__ void gemm_tile_impl(const typename C::type* A,
+                                               long long lda, int m0, int m_lim,
+                                               const typename C::type* B,
+                                               long long ldb, int n0, int n_lim, int k_begin,
+                                               int k_end, bool a_vec, bool b_vec,
+                                               f32x16 (&acc)[C::FM][C::FN], char* smem) {
+  using T = typename C::type;
+  using SA = Stage<C, C::BM, AK>;
+  using SB = Stage<C, C::BN, BK_>;
   T* As = reinterpret_cast<T*>(smem);
-  T* Bs = As + 2 * OPER;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
-#pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.f;
-  const int nk = (k_end - k_begin + BK - 1) / BK;
-  if (nk <= 0) return;
-  Vec16 ra[4], rb[4];
-  Stage<T, AK>::load(A, lda, m0, m_lim, k_begin, k_end, a_vec, ra);
-  Stage<T, BK_>::load(B, ldb, n0, n_lim, k_begin, k_end, b_vec, rb);
-  Stage<T, AK>::store(As, ra);
-  Stage<T, BK_>::store(Bs, rb);
+  T* Bs = As + 2 * C::OPA;
+  const int w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
+  const int nk = (k_end - k_begin + C::BK - 1) / C::BK;
+  Vec16 ra[SA::Q], rb[SB::Q];
+  SA::template load<FULL>(A, lda, m0, m_lim, k_begin, k_end, a_vec, ra);
+  SB::template load<FULL>(B, ldb, n0, n_lim, k_begin, k_end, b_vec, rb);
+  SA::store(As, ra);
+  SB::store(Bs, rb);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = k_begin + (kt + 1) * BK;
-      Stage<T, AK>::load(A, lda, m0, m_lim, k0, k_end, a_vec, ra);
-      Stage<T, BK_>::load(B, ldb, n0, n_lim, k0, k_end, b_vec, rb);
-    }
-    Mma<T, ACOL, BCOL>::run(As + cur * OPER, Bs + cur * OPER, acc, wm, wn);
-    if (more) {
-      Stage<T, AK>::store(As + (cur ^ 1) * OPER, ra);
-      Stage<T, BK_>::store(Bs + (cur ^ 1) * OPER, rb);
-    }
+    // The last step reloads its own (in-bounds) stage into the idle buffer,
+    // which keeps the loop body free of branches.
+    const int k0 = k_begin + min(kt + 1, nk - 1) * C::BK;
+    SA::template load<FULL>(A, lda, m0, m_lim, k0, k_end, a_vec, ra);
+    SB::template load<FULL>(B, ldb, n0, n_lim, k0, k_end, b_vec, rb);
+    // Keep the next stage's global loads ahead of this stage's MFMAs so their
+    // latency hides behind the matrix work (a compiler-only memory fence: no
+    // memory operation moves across it, and the MFMAs wait on the LDS reads
+    // below it).
+    asm volatile("" ::: "memory");
+    mma_stage<C, SA::COL, SB::COL>(As + cur * C::OPA, Bs + cur * C::OPB, acc, wm, wn);
+    SA::store(As + (cur ^ 1) * C::OPA, ra);
+    SB::store(Bs + (cur ^ 1) * C::OPB, rb);
     __syncthreads();
   }
 }
 
-// Accumulator element (mi, ni, r) of lane l sits at tile row
-// wm*64 + mi*32 + 8*(r/4) + 4*(l/32) + r%4 and tile column wn*64 + ni*32 + l%32.
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[2][2], float* __restrict__ Zt) {
-  const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+// acc = A[m0:m0+BM, k] . B[n0:n0+BN, k]^T over k in [k_begin, k_end).
+// Rows/columns past the limits and k past k_end read as zero.  Ends with a
+// barrier, so the caller may reuse `smem` right away.
+template <class C, bool AK, bool BK_>
+__device__ __forceinline__ void gemm_tile(const typename C::type* __restrict__ A, long long lda,
+                                          int m0, int m_lim,
+                                          const typename C::type* __restrict__ B, long long ldb,
+                                          int n0, int n_lim, int k_begin, int k_end, bool a_vec,
+                                          bool b_vec, f32x16 (&acc)[C::FM][C::FN], char* smem) {
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = wn * 64 + ni * 32 + i;
+    for (int fj = 0; fj < C::FN; ++fj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fi][fj][r] = 0.f;
+  if (k_end <= k_begin) return;
+  const bool full = a_vec && b_vec && m0 + C::BM <= m_lim && n0 + C::BN <= n_lim &&
+                    (k_end - k_begin) % C::BK == 0;
+  if (full)
+    gemm_tile_impl<C, AK, BK_, true>(A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
+                                     b_vec, acc, smem);
+  else
+    gemm_tile_impl<C, AK, BK_, false>(A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
+                                      b_vec, acc, smem);
+}
+
+// Accumulator element (fi, fj, r) of lane l in wave (wm, wn) sits at tile row
+// wm*WM + fi*32 + 8*(r/4) + 4*(l/32) + r%4 and tile column wn*WN + fj*32 + l%32.
+template <class C>
+__device__ __forceinline__ int acc_row(int fi, int r) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return (w / C::WGN) * C::WM + fi * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+}
+template <class C>
+__device__ __forceinline__ int acc_col(int fj) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return (w % C::WGN) * C::WN + fj * 32 + (lane & 31);
+}
+
+// Write the accumulator tile to LDS column-major: Zt[col * ld + row].
+template <class C>
+__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[C::FM][C::FN],
+                                           float* __restrict__ Zt, int ld) {
+#pragma unroll
+  for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = acc_col<C>(fj);
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        const int row = wm * 64 + mi * 32 + rg * 8 + h * 4;
-        f32x4 v = {acc[mi][ni][rg * 4 + 0], acc[mi][ni][rg * 4 + 1], acc[mi][ni][rg * 4 + 2],
-                   acc[mi][ni][rg * 4 + 3]};
-        *reinterpret_cast<f32x4*>(Zt + col * TILE_LD + row) = v;
+        const int row = acc_row<C>(fi, rg * 4);
+        f32x4 v = {acc[fi][fj][rg * 4 + 0], acc[fi][fj][rg * 4 + 1], acc[fi][fj][rg * 4 + 2],
+                   acc[fi][fj][rg * 4 + 3]};
+        *reinterpret_cast<f32x4*>(Zt + col * ld + row) = v;
       }
     }
 }
@@ -311,71 +351,95 @@ __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double
   }
 }
 
-template <typename T>
-__device__ __forceinline__ float load_f32(const T* p, long long i) {
-  return Elem<T>::to_f32(p[i]);
-}
+
+// Tile configurations of the four head products (fp32 choices from a sweep
+// of tile / wave shapes on the V = 180k head: 128 x 128 work-group tiles,
+// 16-k stages; the dX product prefers eight 64 x 32 wavefronts).
+using CfgF32 = Cfg<float, 128, 128, 64, 64, 64, 2>;
+using CfgF32Dx = Cfg<float, 128, 128, 64, 32, 128, 2>;
+using CfgB16 = Cfg<bf16_t, 128, 128, 64, 64, 128, 2>;
+template <typename T> struct Pick;
+template <> struct Pick<float> {
+  using fwd = CfgF32;
+  using rec = CfgF32;
+  using dx = CfgF32Dx;
+  using dw = CfgF32;
+};
+template <> struct Pick<bf16_t> {
+  using fwd = CfgB16;
+  using rec = CfgB16;
+  using dx = CfgB16;
+  using dw = CfgB16;
+};
+
+template <class C>
+struct EpiSmem {
+  static constexpr int TL = C::BM + 4;  // accumulator tile in LDS, [col][row]
+  static constexpr int BYTES = cmax(C::STAGE_BYTES, C::BN * TL * 4);
+};
 
 // ------------------------------------------------------------- forward
-// One work-group: 128 frames x one LSE_SPAN-wide vocabulary span, walked in
-// 128-column tiles.  Per tile: MFMA logits, + bias, then per row the FP64
-// sum of exp(z - tile-row max) folded into the row's running partial, and a
-// gather of the selected columns into Zsel (class-major, K x M).
-template <typename T>
-__global__ __launch_bounds__(NT, 2) void k_fwd_lse(const T* __restrict__ X, const T* __restrict__ W,
-                                                   const T* __restrict__ bias, int M, int D, int V,
-                                                   const int* __restrict__ col2sel,
-                                                   float* __restrict__ Zsel,
-                                                   double2* __restrict__ part, int nspan,
-                                                   int mtiles, int vec_ok) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+// One work-group: BM frames x one LSE_SPAN-wide vocabulary span, walked in
+// BN-column tiles.  Per tile: MFMA logits, + bias, then per row the FP64 sum
+// of exp(z - row max over the tile) folded into the row's running partial,
+// and a gather of the selected columns into Zsel (class-major, K x M).
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
+    const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
+    const typename C::type* __restrict__ bias, int M, int D, int V,
+    const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
+    int nspan, int mtiles, int vec_ok) {
+  using T = typename C::type;
+  constexpr int BM = C::BM, BN = C::BN, TL = EpiSmem<C>::TL;
+  constexpr int TPR = C::THREADS / BM;  // threads sharing one row in the epilogue
+  constexpr int CPT = BN / TPR;         // columns per thread
+  static_assert(C::THREADS % BM == 0 && BN % TPR == 0, "epilogue split");
+  __shared__ __attribute__((aligned(16))) char smem[EpiSmem<C>::BYTES];
   __shared__ int s_sel[BN];
   __shared__ float s_bias[BN];
-  __shared__ float s_pm[BM];
-  __shared__ double s_ps[BM];
+  __shared__ float s_pm[TPR][BM];
+  __shared__ double s_ps[TPR][BM];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = lin % mtiles, sp = lin / mtiles;
   const int m0 = mt * BM;
   const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
-  const int r = threadIdx.x & (BM - 1), hh = threadIdx.x >> 7;
+  const int r = threadIdx.x % BM, pi = threadIdx.x / BM;
   const int m = m0 + r;
   float run_m = -INFINITY;
   double run_s = 0.0;
   float* Zt = reinterpret_cast<float*>(smem);
   for (int n0 = c_begin; n0 < c_end; n0 += BN) {
-    f32x16 acc[2][2];
-    gemm_tile<T, true, true>(X, D, m0, M, W, D, n0, c_end, 0, D, vec_ok, vec_ok, acc, smem);
-    acc_to_lds(acc, Zt);
-    if (threadIdx.x < BN) {
-      const int v = n0 + threadIdx.x;
-      s_sel[threadIdx.x] = v < c_end ? col2sel[v] : -1;
-      s_bias[threadIdx.x] = (bias != nullptr && v < c_end) ? load_f32(bias, v) : 0.f;
+    f32x16 acc[C::FM][C::FN];
+    gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c_end, 0, D, vec_ok, vec_ok, acc, smem);
+    acc_to_lds<C>(acc, Zt, TL);
+    for (int c = threadIdx.x; c < BN; c += C::THREADS) {
+      const int v = n0 + c;
+      s_sel[c] = v < c_end ? col2sel[v] : -1;
+      s_bias[c] = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
     }
     __syncthreads();
     const int ncol = min(BN, c_end - n0);
-    const int cb = hh * 64, ce = min(cb + 64, ncol);
+    const int cb = pi * CPT, ce = min(cb + CPT, ncol);
     if (m < M && ce > cb) {
       float mx = -INFINITY;
-      for (int c = cb; c < ce; ++c) mx = fmaxf(mx, Zt[c * TILE_LD + r] + s_bias[c]);
-      double s = 0.0;
+      for (int c = cb; c < ce; ++c) mx = fmaxf(mx, Zt[c * TL + r] + s_bias[c]);
+      double sum = 0.0;
       const double dmx = (double)mx;
       for (int c = cb; c < ce; ++c) {
-        const float z = Zt[c * TILE_LD + r] + s_bias[c];
-        s += exp((double)z - dmx);
+        const float z = Zt[c * TL + r] + s_bias[c];
+        sum += exp((double)z - dmx);
         const int sel = s_sel[c];
         if (sel >= 0) Zsel[(long long)sel * M + m] = z;
       }
-      lse_fold(run_m, run_s, mx, s);
+      lse_fold(run_m, run_s, mx, sum);
     }
     __syncthreads();
   }
-  if (hh == 1) {
-    s_pm[r] = run_m;
-    s_ps[r] = run_s;
-  }
+  s_pm[pi][r] = run_m;
+  s_ps[pi][r] = run_s;
   __syncthreads();
-  if (hh == 0 && m < M) {
-    lse_fold(run_m, run_s, s_pm[r], s_ps[r]);
+  if (pi == 0 && m < M) {
+    for (int q = 1; q < TPR; ++q) lse_fold(run_m, run_s, s_pm[q][r], s_ps[q][r]);
     part[(long long)m * nspan + sp] = make_double2((double)run_m, run_s);
   }
 }
@@ -407,54 +471,62 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 }
 
 // ------------------------------------------------------------- backward
-// Recompute one 128 x 128 tile of chunk logits and form the logit gradient
+// Recompute one BM x BN tile of chunk logits and form the logit gradient
 //   v not selected:  dZ = (grad g_m) * exp(fp32(z - fp32(lambda_m)))
 //   v = U[j]:        dZ = fp32(grad * (g_m exp(S[j][m]) - Gamma[j][m]))
 // (g_m = sum_j gamma_j(m), zero on excluded rows).  dZ goes to the chunk
 // block (row-major, leading dimension ldz) and the tile's column sums to
 // dbpart[mtile][col].
-template <typename T>
-__global__ __launch_bounds__(NT, 2) void k_recompute(
-    const T* __restrict__ X, const T* __restrict__ W, const T* __restrict__ bias, int M, int D,
-    int c0, int c1, const int* __restrict__ col2sel, const float* __restrict__ lamf,
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
+    const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
+    const typename C::type* __restrict__ bias, int M, int D, int c0, int c1,
+    const int* __restrict__ col2sel, const float* __restrict__ lamf,
     const double* __restrict__ g, const float* __restrict__ S, const float* __restrict__ Gam,
-    double grad, T* __restrict__ dZ, int ldz, float* __restrict__ dbpart, int mtiles,
-    int vec_ok) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+    double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
+    int mtiles, int vec_ok) {
+  using T = typename C::type;
+  constexpr int BM = C::BM, BN = C::BN, TL = EpiSmem<C>::TL;
+  constexpr int GROUPS = C::THREADS / BN;  // row groups in the epilogue
+  constexpr int RPG = BM / GROUPS;
+  static_assert(C::THREADS % BN == 0 && BM % GROUPS == 0, "epilogue split");
+  __shared__ __attribute__((aligned(16))) char smem[EpiSmem<C>::BYTES];
   __shared__ int s_sel[BN];
   __shared__ float s_bias[BN];
   __shared__ float s_lam[BM];
   __shared__ float s_rs[BM];
   __shared__ double s_g[BM];
-  __shared__ float s_db[BN];
+  __shared__ float s_db[GROUPS][BN];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = lin % mtiles, nt = lin / mtiles;
   const int m0 = mt * BM, n0 = c0 + nt * BN;
-  f32x16 acc[2][2];
-  gemm_tile<T, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
+  f32x16 acc[C::FM][C::FN];
+  gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   float* Zt = reinterpret_cast<float*>(smem);
-  acc_to_lds(acc, Zt);
-  if (threadIdx.x < BN) {
-    const int v = n0 + threadIdx.x;
-    s_sel[threadIdx.x] = v < c1 ? col2sel[v] : -1;
-    s_bias[threadIdx.x] = (bias != nullptr && v < c1) ? load_f32(bias, v) : 0.f;
-    const int mm = m0 + threadIdx.x;
+  acc_to_lds<C>(acc, Zt, TL);
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) {
+    const int v = n0 + c;
+    s_sel[c] = v < c1 ? col2sel[v] : -1;
+    s_bias[c] = (bias != nullptr && v < c1) ? Elem<T>::to_f32(bias[v]) : 0.f;
+  }
+  for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
+    const int mm = m0 + rr;
     const double gm = mm < M ? g[mm] : 0.0;
-    s_g[threadIdx.x] = gm;
-    s_rs[threadIdx.x] = (float)(grad * gm);
-    s_lam[threadIdx.x] = mm < M ? lamf[mm] : 0.f;
+    s_g[rr] = gm;
+    s_rs[rr] = (float)(grad * gm);
+    s_lam[rr] = mm < M ? lamf[mm] : 0.f;
   }
   __syncthreads();
-  const int c = threadIdx.x & (BN - 1), hh = threadIdx.x >> 7;
+  const int c = threadIdx.x % BN, grp = threadIdx.x / BN;
   const int v = n0 + c;
   float colsum = 0.f;
   if (v < c1) {
     const int sel = s_sel[c];
     const float bv = s_bias[c];
-    const int rend = min(hh * 64 + 64, M - m0);
-    for (int rr = hh * 64; rr < rend; ++rr) {
+    const int rend = min(grp * RPG + RPG, M - m0);
+    for (int rr = grp * RPG; rr < rend; ++rr) {
       const int mm = m0 + rr;
-      const float z = Zt[c * TILE_LD + rr] + bv;
+      const float z = Zt[c * TL + rr] + bv;
       float dz;
       if (sel < 0) {
         dz = s_rs[rr] * expf(z - s_lam[rr]);
@@ -466,71 +538,70 @@ __global__ __launch_bounds__(NT, 2) void k_recompute(
       colsum += dz;
     }
   }
-  if (hh == 1) s_db[c] = colsum;
+  s_db[grp][c] = colsum;
   __syncthreads();
-  if (hh == 0 && v < c1) dbpart[(long long)mt * ldz + (v - c0)] = colsum + s_db[c];
+  if (grp == 0 && v < c1) {
+    for (int q = 1; q < GROUPS; ++q) colsum += s_db[q][c];
+    dbpart[(long long)mt * ldz + (v - c0)] = colsum;
+  }
 }
 
 // dXacc[m][d] (+)= sum_{c in chunk} dZ[m][c] W[c0 + c][d].  With BKM the
 // weight operand is the transposed chunk Wt[d][c] (leading dimension ldb),
 // otherwise the chunk's rows W[c0 + c][d] (leading dimension D).
-template <typename T, bool BKM>
-__global__ __launch_bounds__(NT, 2) void k_dx(const T* __restrict__ dZ, int ldz,
-                                              const T* __restrict__ Wc, int ldb, int M, int D,
-                                              int Cc, float* __restrict__ dXacc, int first,
-                                              int mtiles, int a_vec, int b_vec) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+template <class C, bool BKM>
+__global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dx(
+    const typename C::type* __restrict__ dZ, int ldz, const typename C::type* __restrict__ Wc,
+    int ldb, int M, int D, int Cc, float* __restrict__ dXacc, int first, int mtiles, int a_vec,
+    int b_vec) {
+  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = lin % mtiles, nt = lin / mtiles;
-  const int m0 = mt * BM, n0 = nt * BN;
-  f32x16 acc[2][2];
-  gemm_tile<T, true, BKM>(dZ, ldz, m0, M, Wc, ldb, n0, D, 0, Cc, a_vec, b_vec, acc, smem);
-  const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  const int m0 = mt * C::BM, n0 = nt * C::BN;
+  f32x16 acc[C::FM][C::FN];
+  gemm_tile<C, true, BKM>(dZ, ldz, m0, M, Wc, ldb, n0, D, 0, Cc, a_vec, b_vec, acc, smem);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = n0 + wn * 64 + ni * 32 + i;
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = n0 + acc_col<C>(fj);
       if (col >= D) continue;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int row = m0 + wm * 64 + mi * 32 + (rr >> 2) * 8 + h * 4 + (rr & 3);
+        const int row = m0 + acc_row<C>(fi, rr);
         if (row < M) {
           float* p = dXacc + (long long)row * D + col;
-          *p = first ? acc[mi][ni][rr] : *p + acc[mi][ni][rr];
+          *p = first ? acc[fi][fj][rr] : *p + acc[fi][fj][rr];
         }
       }
     }
 }
 
 // part[s][i][d] = sum_{m in split s} dZ[m][i] X[m][d]  (i = chunk column).
-template <typename T>
-__global__ __launch_bounds__(NT, 2) void k_dw(const T* __restrict__ dZ, int ldz,
-                                              const T* __restrict__ X, int M, int D, int Cc,
-                                              float* __restrict__ part, int itiles, int ntiles,
-                                              int kchunk, int a_vec, int b_vec) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM_BYTES];
+template <class C>
+__global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dw(
+    const typename C::type* __restrict__ dZ, int ldz, const typename C::type* __restrict__ X,
+    int M, int D, int Cc, float* __restrict__ part, int itiles, int ntiles, int kchunk, int a_vec,
+    int b_vec) {
+  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int per = itiles * ntiles;
   const int s = lin / per, rem = lin % per;
   const int it = rem % itiles, nt = rem / itiles;
-  const int i0 = it * BM, n0 = nt * BN;
+  const int i0 = it * C::BM, n0 = nt * C::BN;
   const int kb = s * kchunk, ke = min(M, kb + kchunk);
-  f32x16 acc[2][2];
-  gemm_tile<T, false, false>(dZ, ldz, i0, Cc, X, D, n0, D, kb, ke, a_vec, b_vec, acc, smem);
-  const int lane = threadIdx.x & 63, li = lane & 31, h = lane >> 5;
-  const int w = threadIdx.x >> 6, wm = w >> 1, wn = w & 1;
+  f32x16 acc[C::FM][C::FN];
+  gemm_tile<C, false, false>(dZ, ldz, i0, Cc, X, D, n0, D, kb, ke, a_vec, b_vec, acc, smem);
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int col = n0 + wn * 64 + ni * 32 + li;
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = n0 + acc_col<C>(fj);
       if (col >= D) continue;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const int row = i0 + wm * 64 + mi * 32 + (rr >> 2) * 8 + h * 4 + (rr & 3);
-        if (row < Cc) part[((long long)s * Cc + row) * D + col] = acc[mi][ni][rr];
+        const int row = i0 + acc_row<C>(fi, rr);
+        if (row < Cc) part[((long long)s * Cc + row) * D + col] = acc[fi][fj][rr];
       }
     }
 }
@@ -594,22 +665,24 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 }  // namespace
 
+template <typename T>
+hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
+                     int V, const int* col2sel, float* Zsel, double2* part, int nspan) {
+  using C = typename Pick<T>::fwd;
+  const int mtiles = ceil_div(M, C::BM);
+  const int grid = mtiles * nspan;
+  if (grid == 0) return hipSuccess;
+  const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
+  k_fwd_lse<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, V,
+                                             col2sel, Zsel, part, nspan, mtiles, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                           int M, int D, int V, const int* col2sel, float* Zsel, double2* part,
                           int nspan) {
-  const int mtiles = ceil_div(M, BM);
-  const int grid = mtiles * nspan;
-  if (grid == 0) return hipSuccess;
-  if (dtype == 0) {
-    const int vec = (D % 4 == 0) && aligned16(X) && aligned16(W);
-    k_fwd_lse<float><<<grid, NT, 0, st>>>((const float*)X, (const float*)W, (const float*)b, M, D,
-                                          V, col2sel, Zsel, part, nspan, mtiles, vec);
-  } else {
-    const int vec = (D % 8 == 0) && aligned16(X) && aligned16(W);
-    k_fwd_lse<bf16_t><<<grid, NT, 0, st>>>((const bf16_t*)X, (const bf16_t*)W, (const bf16_t*)b,
-                                           M, D, V, col2sel, Zsel, part, nspan, mtiles, vec);
-  }
-  return hipGetLastError();
+  return dtype == 0 ? fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan)
+                    : fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
 }
 
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan, double* lam,
@@ -626,72 +699,91 @@ hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int
   return hipGetLastError();
 }
 
+template <typename T>
+hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
+                       int c0, int c1, const int* col2sel, const float* lamf, const double* g,
+                       const float* S, const float* Gam, double grad, void* dZ, int ldz,
+                       float* dbpart) {
+  using C = typename Pick<T>::rec;
+  const int mtiles = ceil_div(M, C::BM);
+  const int grid = mtiles * ceil_div(c1 - c0, C::BN);
+  if (grid == 0) return hipSuccess;
+  const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
+  k_recompute<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, c0, c1,
+                                               col2sel, lamf, g, S, Gam, grad, (T*)dZ, ldz,
+                                               dbpart, mtiles, vec);
+  return hipGetLastError();
+}
+
 hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                             int M, int D, int c0, int c1, const int* col2sel, const float* lamf,
                             const double* g, const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart) {
-  const int mtiles = ceil_div(M, BM);
-  const int grid = mtiles * ceil_div(c1 - c0, BN);
-  if (grid == 0) return hipSuccess;
-  if (dtype == 0) {
-    const int vec = (D % 4 == 0) && aligned16(X) && aligned16(W);
-    k_recompute<float><<<grid, NT, 0, st>>>((const float*)X, (const float*)W, (const float*)b, M,
-                                            D, c0, c1, col2sel, lamf, g, S, Gam, grad,
-                                            (float*)dZ, ldz, dbpart, mtiles, vec);
-  } else {
-    const int vec = (D % 8 == 0) && aligned16(X) && aligned16(W);
-    k_recompute<bf16_t><<<grid, NT, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
-                                             (const bf16_t*)b, M, D, c0, c1, col2sel, lamf, g, S,
-                                             Gam, grad, (bf16_t*)dZ, ldz, dbpart, mtiles, vec);
-  }
-  return hipGetLastError();
+  return dtype == 0 ? recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam,
+                                         grad, dZ, ldz, dbpart)
+                    : recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam,
+                                          grad, dZ, ldz, dbpart);
 }
 
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W, int M,
                      int D, int c0, int c1, float* dXacc, int first, void* wt) {
-  const int mtiles = ceil_div(M, BM);
-  const int grid = mtiles * ceil_div(D, BN);
-  if (grid == 0) return hipSuccess;
   const int Cc = c1 - c0;
   if (dtype == 0) {
+    using C = Pick<float>::dx;
+    const int mtiles = ceil_div(M, C::BM);
+    const int grid = mtiles * ceil_div(D, C::BN);
+    if (grid == 0) return hipSuccess;
     const float* Wc = (const float*)W + (long long)c0 * D;
     const int av = (ldz % 4 == 0) && aligned16(dZ);
     const int bv = (D % 4 == 0) && aligned16(Wc);
-    k_dx<float, false><<<grid, NT, 0, st>>>((const float*)dZ, ldz, Wc, D, M, D, Cc, dXacc, first,
-                                            mtiles, av, bv);
+    k_dx<C, false><<<grid, C::THREADS, 0, st>>>((const float*)dZ, ldz, Wc, D, M, D, Cc, dXacc,
+                                                first, mtiles, av, bv);
   } else {
     // bf16: stage W_c^T (D x Cc, leading dimension ldz) so both operands are
     // K-contiguous.
+    using C = Pick<bf16_t>::dx;
+    const int mtiles = ceil_div(M, C::BM);
+    const int grid = mtiles * ceil_div(D, C::BN);
+    if (grid == 0) return hipSuccess;
     const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
     dim3 tg(ceil_div(D, 64), ceil_div(Cc, 64));
     k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, D, (bf16_t*)wt, ldz);
     const int av = (ldz % 8 == 0) && aligned16(dZ);
     const int bv = (ldz % 8 == 0) && aligned16(wt);
-    k_dx<bf16_t, true><<<grid, NT, 0, st>>>((const bf16_t*)dZ, ldz, (const bf16_t*)wt, ldz, M, D,
-                                            Cc, dXacc, first, mtiles, av, bv);
+    k_dx<C, true><<<grid, C::THREADS, 0, st>>>((const bf16_t*)dZ, ldz, (const bf16_t*)wt, ldz, M,
+                                               D, Cc, dXacc, first, mtiles, av, bv);
   }
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t dw_t(hipStream_t st, const void* dZ, int ldz, const void* X, int M, int D, int c0,
+                int c1, float* part, int splitk) {
+  using C = typename Pick<T>::dw;
+  const int Cc = c1 - c0;
+  const int itiles = ceil_div(Cc, C::BM), ntiles = ceil_div(D, C::BN);
+  const int grid = itiles * ntiles * splitk;
+  if (grid == 0) return hipSuccess;
+  const int kchunk = ceil_div(ceil_div(M, splitk), 64) * 64;
+  const int av = (ldz % C::VEC == 0) && aligned16(dZ);
+  const int bv = (D % C::VEC == 0) && aligned16(X);
+  k_dw<C><<<grid, C::THREADS, 0, st>>>((const T*)dZ, ldz, (const T*)X, M, D, Cc, part, itiles,
+                                        ntiles, kchunk, av, bv);
   return hipGetLastError();
 }
 
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X, int M,
                      int D, int c0, int c1, float* part, int splitk) {
-  const int Cc = c1 - c0;
-  const int itiles = ceil_div(Cc, BM), ntiles = ceil_div(D, BN);
-  const int grid = itiles * ntiles * splitk;
-  if (grid == 0) return hipSuccess;
-  const int kchunk = ceil_div(ceil_div(M, splitk), 64) * 64;
-  if (dtype == 0) {
-    const int av = (ldz % 4 == 0) && aligned16(dZ);
-    const int bv = (D % 4 == 0) && aligned16(X);
-    k_dw<float><<<grid, NT, 0, st>>>((const float*)dZ, ldz, (const float*)X, M, D, Cc, part,
-                                     itiles, ntiles, kchunk, av, bv);
-  } else {
-    const int av = (ldz % 8 == 0) && aligned16(dZ);
-    const int bv = (D % 8 == 0) && aligned16(X);
-    k_dw<bf16_t><<<grid, NT, 0, st>>>((const bf16_t*)dZ, ldz, (const bf16_t*)X, M, D, Cc, part,
-                                      itiles, ntiles, kchunk, av, bv);
-  }
-  return hipGetLastError();
+  return dtype == 0 ? dw_t<float>(st, dZ, ldz, X, M, D, c0, c1, part, splitk)
+                    : dw_t<bf16_t>(st, dZ, ldz, X, M, D, c0, c1, part, splitk);
+}
+
+int rec_tile_rows(int dtype) { return dtype == 0 ? Pick<float>::rec::BM : Pick<bf16_t>::rec::BM; }
+
+int dw_tiles(int dtype, int C, int D) {
+  if (dtype == 0)
+    return ceil_div(C, Pick<float>::dw::BM) * ceil_div(D, Pick<float>::dw::BN);
+  return ceil_div(C, Pick<bf16_t>::dw::BM) * ceil_div(D, Pick<bf16_t>::dw::BN);
 }
 
 hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk, int rows,
