@@ -36,8 +36,9 @@ def run_pcx(bt: workloads.Batch, grad=1.0, want_dX=True, want_dW=True, want_db=T
     out = {"loss": loss, "info": info}
     if getters:
         out.update(U=c.selected(), rel=c.relabeled(), flags=c.alignable(),
-                   utt_loss=c.utt_losses(), status=c.utt_status(), lam=c.normalizer(),
-                   S=c.scores(), Gam=c.occupancy())
+                   utt_loss=c.utt_losses(), status=c.utt_status())
+        if getters != "light":
+            out.update(lam=c.normalizer(), S=c.scores(), Gam=c.occupancy())
     for k, t in (("dX", dX), ("dW", dW), ("db", db)):
         out[k] = None if t is None else t.double().cpu().numpy()
     if own:

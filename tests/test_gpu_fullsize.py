@@ -1,0 +1,58 @@
+"""Parity at the full workload sizes, in the launch configuration bench.py times.
+
+The oracle cannot redo a whole V = 180k or LLM-head batch in seconds, so:
+* U, relabelled targets and alignability flags are compared bit-exact on the
+  whole batch (cheap set arithmetic in the oracle);
+* per-utterance losses and the dX rows of sampled utterances are compared
+  with the oracle run on those utterances alone (both depend only on the
+  utterance itself);
+* dW and db, which mix all utterances, are checked by properties that hold
+  at any size: every alignable frame's logit-gradient row sums to zero, so
+  sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from pcx_harness import rel_fro, run_pcx, tolerance
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample(bt):
+    # the shortest utterance keeps the oracle's share of the test short
+    return [int(np.argmin(bt.frame_counts))]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["v500", "v5k", "v180k", "llm152k"])
+def test_full_size_sampled(name):
+    bt = workloads.make(name, seed=0)
+    print("workload", name, "M", bt.M, "V", bt.V, "D", bt.D, "N", bt.N, flush=True)
+    got = run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters="light")
+    U, rel, flags = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
+    assert got["U"].tolist() == U.tolist()
+    assert got["rel"].tolist() == rel.tolist()
+    assert got["flags"].tolist() == flags.tolist()
+    assert np.all(got["status"] == 0)
+    assert got["loss"] == pytest.approx(float(np.sum(got["utt_loss"])), rel=1e-12)
+    tol = tolerance(bt)
+    idx = _sample(bt)
+    sb = workloads.sample_utterances(bt, idx)
+    print("oracle on utterances", idx, "frames", sb.M, flush=True)
+    ref = oracle.pcx(sb.X, sb.W, sb.b, sb.frame_counts, sb.tgt_off, sb.tgt, sb.blank,
+                     want_dW=False, want_db=False)
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    for j, n in enumerate(idx):
+        assert abs(got["utt_loss"][n] - ref["utt_loss"][j]) <= tol * abs(ref["utt_loss"][j])
+    rows = np.concatenate([np.arange(row_off[n], row_off[n + 1]) for n in idx])
+    assert rel_fro(got["dX"][rows], ref["dX"]) <= tol
+    if bt.want_db:
+        db = got["db"]
+        assert abs(db.sum()) <= 1e-5 * np.abs(db).sum()
+    if bt.want_dW:
+        dW = got["dW"]
+        colsum = np.abs(dW.sum(0))
+        scale = np.abs(dW).sum(0)
+        assert np.all(colsum <= 1e-5 * scale)
