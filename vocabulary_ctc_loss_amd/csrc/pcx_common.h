@@ -25,6 +25,32 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// exp(x) for x <= 0 in IEEE double (0 below the double range; branch-free).
+// Cody-Waite reduction x = n ln2 + r with ln2 split into a 32-bit head (so
+// n * head is exact) and a tail, |r| <= ln2 / 2, then the degree-13 Taylor
+// polynomial of e^r (truncation < 1e-17 relative) and a scale by 2^n.
+__device__ __forceinline__ double exp_nonpos(double x) {
+  x = fmax(x, -746.0);  // -inf -> 0 through the underflowing scale below
+  const double n = rint(x * 0x1.71547652b82fep+0);  // x / ln2
+  double r = fma(-n, 0x1.62e42ff000000p-1, x);      // ln2 head
+  r = fma(-n, -0x1.718432a1b0e26p-35, r);           // ln2 tail
+  double p = 0x1.6124613a86d09p-33;                 // 1/13!
+  p = fma(p, r, 0x1.1eed8eff8d898p-29);             // 1/12!
+  p = fma(p, r, 0x1.ae64567f544e4p-26);             // 1/11!
+  p = fma(p, r, 0x1.27e4fb7789f5cp-22);             // 1/10!
+  p = fma(p, r, 0x1.71de3a556c734p-19);             // 1/9!
+  p = fma(p, r, 0x1.a01a01a01a01ap-16);             // 1/8!
+  p = fma(p, r, 0x1.a01a01a01a01ap-13);             // 1/7!
+  p = fma(p, r, 0x1.6c16c16c16c17p-10);             // 1/6!
+  p = fma(p, r, 0x1.1111111111111p-7);              // 1/5!
+  p = fma(p, r, 0x1.5555555555555p-5);              // 1/4!
+  p = fma(p, r, 0x1.5555555555555p-3);              // 1/3!
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(p, (int)n);
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int VEC = 4;  // elements per 16-byte vector

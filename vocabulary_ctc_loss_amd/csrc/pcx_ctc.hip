@@ -32,13 +32,13 @@ constexpr int PF = 8;  // frames per emission prefetch block
 __device__ __forceinline__ double lse3(double a, double b, double c) {
   const double m = fmax(a, fmax(b, c));
   if (m == -INFINITY) return -INFINITY;
-  return m + log(exp(a - m) + exp(b - m) + exp(c - m));
+  return m + log(exp_nonpos(a - m) + exp_nonpos(b - m) + exp_nonpos(c - m));
 }
 
 __device__ __forceinline__ double lse2(double a, double b) {
   const double m = fmax(a, b);
   if (m == -INFINITY) return -INFINITY;
-  return m + log(exp(a - m) + exp(b - m));
+  return m + log(exp_nonpos(a - m) + exp_nonpos(b - m));
 }
 
 // Forward recursion; alpha[t][s] (including the emission at t) is stored

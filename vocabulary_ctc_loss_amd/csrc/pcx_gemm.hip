@@ -344,10 +344,10 @@ __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double
     m1 = m2;
     s1 = s2;
   } else if (m2 > m1) {
-    s1 = s1 * exp((double)m1 - (double)m2) + s2;
+    s1 = s1 * exp_nonpos((double)m1 - (double)m2) + s2;
     m1 = m2;
   } else {
-    s1 = s1 + s2 * exp((double)m2 - (double)m1);
+    s1 = s1 + s2 * exp_nonpos((double)m2 - (double)m1);
   }
 }
 
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
       const double dmx = (double)mx;
       for (int c = cb; c < ce; ++c) {
         const float z = Zt[c * TL + r] + s_bias[c];
-        sum += exp((double)z - dmx);
+        sum += exp_nonpos((double)z - dmx);
         const int sel = s_sel[c];
         if (sel >= 0) Zsel[(long long)sel * M + m] = z;
       }
@@ -454,7 +454,7 @@ __global__ void k_lambda(const double2* __restrict__ part, int M, int nspan,
   for (int i = 0; i < nspan; ++i) mx = fmax(mx, p[i].x);
   double s = 0.0;
   for (int i = 0; i < nspan; ++i)
-    if (p[i].x != -INFINITY) s += p[i].y * exp(p[i].x - mx);
+    if (p[i].x != -INFINITY) s += p[i].y * exp_nonpos(p[i].x - mx);
   const double l = mx + log(s);
   lam[m] = l;
   lamf[m] = (float)l;
@@ -472,11 +472,14 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 
 // ------------------------------------------------------------- backward
 // Recompute one BM x BN tile of chunk logits and form the logit gradient
-//   v not selected:  dZ = (grad g_m) * exp(fp32(z - fp32(lambda_m)))
+//   v not selected:  dZ = (grad g_m) * exp(z - fp32(lambda_m)), evaluated in
+//                    fp32 as exp2(z log2e - fp32(lambda_m log2e)) with one
+//                    fused multiply-add for the argument;
 //   v = U[j]:        dZ = fp32(grad * (g_m exp(S[j][m]) - Gamma[j][m]))
-// (g_m = sum_j gamma_j(m), zero on excluded rows).  dZ goes to the chunk
-// block (row-major, leading dimension ldz) and the tile's column sums to
-// dbpart[mtile][col].
+//                    (S reused; the difference formed in FP64, one rounding)
+// (g_m = sum_j gamma_j(m), zero on excluded rows).  The epilogue works on the
+// MFMA accumulators in place: dZ goes to the chunk block (row-major,
+// leading dimension ldz) and the tile's column sums to dbpart[mtile][col].
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
@@ -486,24 +489,19 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
     int mtiles, int vec_ok) {
   using T = typename C::type;
-  constexpr int BM = C::BM, BN = C::BN, TL = EpiSmem<C>::TL;
-  constexpr int GROUPS = C::THREADS / BN;  // row groups in the epilogue
-  constexpr int RPG = BM / GROUPS;
-  static_assert(C::THREADS % BN == 0 && BM % GROUPS == 0, "epilogue split");
-  __shared__ __attribute__((aligned(16))) char smem[EpiSmem<C>::BYTES];
+  constexpr int BM = C::BM, BN = C::BN;
+  constexpr float LOG2E = 1.44269504088896340736f;
+  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ int s_sel[BN];
   __shared__ float s_bias[BN];
-  __shared__ float s_lam[BM];
+  __shared__ float s_lam2[BM];
   __shared__ float s_rs[BM];
   __shared__ double s_g[BM];
-  __shared__ float s_db[GROUPS][BN];
+  __shared__ float s_db[C::WGM][BN];
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int mt = lin % mtiles, nt = lin / mtiles;
   const int m0 = mt * BM, n0 = c0 + nt * BN;
-  f32x16 acc[C::FM][C::FN];
-  gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
-  float* Zt = reinterpret_cast<float*>(smem);
-  acc_to_lds<C>(acc, Zt, TL);
+  // Row and column data of the tile (visible after gemm_tile's barriers).
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
     s_sel[c] = v < c1 ? col2sel[v] : -1;
@@ -514,35 +512,71 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const double gm = mm < M ? g[mm] : 0.0;
     s_g[rr] = gm;
     s_rs[rr] = (float)(grad * gm);
-    s_lam[rr] = mm < M ? lamf[mm] : 0.f;
+    s_lam2[rr] = mm < M ? lamf[mm] * LOG2E : 0.f;
   }
-  __syncthreads();
-  const int c = threadIdx.x % BN, grp = threadIdx.x / BN;
-  const int v = n0 + c;
-  float colsum = 0.f;
-  if (v < c1) {
-    const int sel = s_sel[c];
-    const float bv = s_bias[c];
-    const int rend = min(grp * RPG + RPG, M - m0);
-    for (int rr = grp * RPG; rr < rend; ++rr) {
-      const int mm = m0 + rr;
-      const float z = Zt[c * TL + rr] + bv;
-      float dz;
-      if (sel < 0) {
-        dz = s_rs[rr] * expf(z - s_lam[rr]);
-      } else {
-        const long long o = (long long)sel * M + mm;
-        dz = (float)(grad * (s_g[rr] * exp((double)S[o]) - (double)Gam[o]));
+  f32x16 acc[C::FM][C::FN];
+  gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    const int col = acc_col<C>(fj);
+    const int v = n0 + col;
+    const bool cval = v < c1;
+    const int sel = s_sel[col];
+    const float bv = s_bias[col];
+    T* out = dZ + (v - c0);
+    float cs = 0.f;
+    if (sel < 0) {
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<C>(fi, r);
+          const float dz =
+              s_rs[row] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][r] + bv, LOG2E, -s_lam2[row]));
+          if (cval && m0 + row < M) {
+            out[(long long)(m0 + row) * ldz] = Elem<T>::from_f32(dz);
+            cs += dz;
+          }
+        }
+    } else {
+      const float* Sp = S + (long long)sel * M + m0;
+      const float* Gp = Gam + (long long)sel * M + m0;
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi) {
+        float sv[16], gv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<C>(fi, r);
+          const bool in = m0 + row < M;
+          sv[r] = in ? Sp[row] : 0.f;
+          gv[r] = in ? Gp[row] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<C>(fi, r);
+          const float dz = (float)(grad * (s_g[row] * exp((double)sv[r]) - (double)gv[r]));
+          if (cval && m0 + row < M) {
+            out[(long long)(m0 + row) * ldz] = Elem<T>::from_f32(dz);
+            cs += dz;
+          }
+        }
       }
-      dZ[(long long)mm * ldz + (v - c0)] = Elem<T>::from_f32(dz);
-      colsum += dz;
     }
+    // column sum: the two lane halves hold the same column, then the waves
+    // stacked along M; both combined in a fixed order.
+    cs += __shfl_xor(cs, 32, 64);
+    if (lane < 32) s_db[wm][col] = cs;
   }
-  s_db[grp][c] = colsum;
   __syncthreads();
-  if (grp == 0 && v < c1) {
-    for (int q = 1; q < GROUPS; ++q) colsum += s_db[q][c];
-    dbpart[(long long)mt * ldz + (v - c0)] = colsum;
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) {
+    const int v = n0 + c;
+    if (v < c1) {
+      float t = s_db[0][c];
+#pragma unroll
+      for (int q = 1; q < C::WGM; ++q) t += s_db[q][c];
+      dbpart[(long long)mt * ldz + (v - c0)] = t;
+    }
   }
 }
 
@@ -618,14 +652,24 @@ __global__ void k_dw_reduce(const float* __restrict__ part, int splitk, int rows
   }
 }
 
+// db[col] = sum over row tiles of dbpart[tile][col]: four fixed quarters of
+// the tiles per column, combined in order.
 template <typename T>
-__global__ void k_db_reduce(const float* __restrict__ dbpart, int mtiles, int cols, int ld,
-                            T* __restrict__ db, long long col_base) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= cols) return;
+__global__ __launch_bounds__(256) void k_db_reduce(const float* __restrict__ dbpart, int mtiles,
+                                                   int cols, int ld, T* __restrict__ db,
+                                                   long long col_base) {
+  __shared__ float part[4][64];
+  const int lc = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + lc;
+  const int per = (mtiles + 3) / 4;
+  const int k1 = min(mtiles, (q + 1) * per);
   float s = 0.f;
-  for (int k = 0; k < mtiles; ++k) s += dbpart[(long long)k * ld + i];
-  db[col_base + i] = Elem<T>::from_f32(s);
+  if (c < cols)
+    for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
+  part[q][lc] = s;
+  __syncthreads();
+  if (q == 0 && c < cols)
+    db[col_base + c] = Elem<T>::from_f32(((part[0][lc] + part[1][lc]) + part[2][lc]) + part[3][lc]);
 }
 
 // dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS).
@@ -803,11 +847,11 @@ hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int 
                             int ld, void* db, long long col_base) {
   if (cols == 0) return hipSuccess;
   if (dtype == 0)
-    k_db_reduce<float><<<ceil_div(cols, 256), 256, 0, st>>>(dbpart, mtiles, cols, ld, (float*)db,
-                                                            col_base);
+    k_db_reduce<float><<<ceil_div(cols, 64), 256, 0, st>>>(dbpart, mtiles, cols, ld, (float*)db,
+                                                           col_base);
   else
-    k_db_reduce<bf16_t><<<ceil_div(cols, 256), 256, 0, st>>>(dbpart, mtiles, cols, ld,
-                                                             (bf16_t*)db, col_base);
+    k_db_reduce<bf16_t><<<ceil_div(cols, 64), 256, 0, st>>>(dbpart, mtiles, cols, ld,
+                                                            (bf16_t*)db, col_base);
   return hipGetLastError();
 }
 
