@@ -46,8 +46,23 @@ def parse():
                    choices=["tiny", "v500", "v5k", "v180k", "llm152k"])
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-utts", type=int, default=1)
+    p.add_argument("--cpu-sample-utts", type=int, default=3)
+    p.add_argument("--copy-probe", action="store_true",
+                   help="only run a plain device copy of known size (HBM counter calibration)")
     return p.parse_args()
+
+
+def copy_probe():
+    """A plain 1 GiB device-to-device copy, repeated, as the reference for
+    scaling the FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 1 << 28  # fp32 elements = 1 GiB
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
 
 
 def gemm_flops_per_step(bt):
@@ -91,6 +106,9 @@ def cpu_baseline(bt, n_utts):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)

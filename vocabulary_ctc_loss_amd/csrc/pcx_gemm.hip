@@ -55,6 +55,19 @@ __device__ __forceinline__ int xcd_tile(int bid, int nblocks) {
   return xcd * per + min(xcd, rem) + local;
 }
 
+// Grouped order of an (mtiles x ntiles) tile grid: GM consecutive row tiles
+// form a group whose tiles are enumerated row-fastest, so the work-groups an
+// XCD runs at the same time cover a compact GM x (concurrent / GM) block and
+// share both operands' tiles in its L2.
+template <int GM>
+__device__ __forceinline__ void grouped_tile(int lin, int mtiles, int ntiles, int& mt, int& nt) {
+  const int per_group = GM * ntiles;
+  const int g = lin / per_group, j = lin % per_group;
+  const int gm = min(GM, mtiles - g * GM);
+  mt = g * GM + j % gm;
+  nt = j / gm;
+}
+
 // Tile configuration of one GEMM kernel: a BM x BN work-group tile computed
 // by (BM/WM) x (BN/WN) wavefronts of WM x WN, each a grid of MFMA 32 x 32
 // blocks; KB bytes of every operand row are staged per k step.
@@ -358,6 +371,7 @@ __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double
 using CfgF32 = Cfg<float, 128, 128, 64, 64, 64, 2>;
 using CfgF32Dx = Cfg<float, 128, 128, 64, 32, 128, 2>;
 using CfgB16 = Cfg<bf16_t, 128, 128, 64, 64, 128, 2>;
+using CfgB16W8 = Cfg<bf16_t, 128, 128, 32, 64, 128, 2>;
 template <typename T> struct Pick;
 template <> struct Pick<float> {
   using fwd = CfgF32;
@@ -367,8 +381,8 @@ template <> struct Pick<float> {
 };
 template <> struct Pick<bf16_t> {
   using fwd = CfgB16;
-  using rec = CfgB16;
-  using dx = CfgB16;
+  using rec = CfgB16W8;
+  using dx = CfgB16W8;
   using dw = CfgB16;
 };
 
@@ -399,8 +413,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   __shared__ float s_bias[BN];
   __shared__ float s_pm[TPR][BM];
   __shared__ double s_ps[TPR][BM];
-  const int lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int mt = lin % mtiles, sp = lin / mtiles;
+  int mt, sp;
+  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, nspan, mt, sp);
   const int m0 = mt * BM;
   const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
   const int r = threadIdx.x % BM, pi = threadIdx.x / BM;
@@ -498,8 +512,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   __shared__ float s_rs[BM];
   __shared__ double s_g[BM];
   __shared__ float s_db[C::WGM][BN];
-  const int lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int mt = lin % mtiles, nt = lin / mtiles;
+  int mt, nt;
+  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
   // Row and column data of the tile (visible after gemm_tile's barriers).
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
@@ -589,8 +603,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dx(
     int ldb, int M, int D, int Cc, float* __restrict__ dXacc, int first, int mtiles, int a_vec,
     int b_vec) {
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
+  // column tiles fastest: the work-groups sharing one block of dZ rows run
+  // together
+  const int ntiles = (D + C::BN - 1) / C::BN;
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int mt = lin % mtiles, nt = lin / mtiles;
+  const int nt = lin % ntiles, mt = lin / ntiles;
+  (void)mtiles;
   const int m0 = mt * C::BM, n0 = nt * C::BN;
   f32x16 acc[C::FM][C::FN];
   gemm_tile<C, true, BKM>(dZ, ldz, m0, M, Wc, ldb, n0, D, 0, Cc, a_vec, b_vec, acc, smem);
@@ -618,10 +636,12 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dw(
     int M, int D, int Cc, float* __restrict__ part, int itiles, int ntiles, int kchunk, int a_vec,
     int b_vec) {
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
+  // column tiles fastest: the work-groups sharing one block of dZ columns
+  // run together
   const int lin = xcd_tile(blockIdx.x, gridDim.x);
   const int per = itiles * ntiles;
   const int s = lin / per, rem = lin % per;
-  const int it = rem % itiles, nt = rem / itiles;
+  const int nt = rem % ntiles, it = rem / ntiles;
   const int i0 = it * C::BM, n0 = nt * C::BN;
   const int kb = s * kchunk, ke = min(M, kb + kchunk);
   f32x16 acc[C::FM][C::FN];
