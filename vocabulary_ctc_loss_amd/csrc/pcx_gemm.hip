@@ -253,8 +253,38 @@ __device__ __forceinline__ void mma_stage(const typename C::type* __restrict__ A
   }
 }
 
+// First k stage of a tile, loaded into registers ahead of time so that a
+// caller walking several tiles can overlap it with the previous epilogue.
+template <class C, bool AK, bool BK_>
+struct Prefetch {
+  Vec16 ra[Stage<C, C::BM, AK>::Q];
+  Vec16 rb[Stage<C, C::BN, BK_>::Q];
+  bool full;
+};
+
+template <class C, bool AK, bool BK_>
+__device__ __forceinline__ void gemm_prefetch(Prefetch<C, AK, BK_>& p,
+                                              const typename C::type* A, long long lda, int m0,
+                                              int m_lim, const typename C::type* B,
+                                              long long ldb, int n0, int n_lim, int k_begin,
+                                              int k_end, bool a_vec, bool b_vec) {
+  using SA = Stage<C, C::BM, AK>;
+  using SB = Stage<C, C::BN, BK_>;
+  p.full = a_vec && b_vec && m0 + C::BM <= m_lim && n0 + C::BN <= n_lim &&
+           (k_end - k_begin) % C::BK == 0;
+  if (k_end <= k_begin) return;
+  if (p.full) {
+    SA::template load<true>(A, lda, m0, m_lim, k_begin, k_end, a_vec, p.ra);
+    SB::template load<true>(B, ldb, n0, n_lim, k_begin, k_end, b_vec, p.rb);
+  } else {
+    SA::template load<false>(A, lda, m0, m_lim, k_begin, k_end, a_vec, p.ra);
+    SB::template load<false>(B, ldb, n0, n_lim, k_begin, k_end, b_vec, p.rb);
+  }
+}
+
 template <class C, bool AK, bool BK_, bool FULL>
-__device__ __forceinline__ void gemm_tile_impl(const typename C::type* A,
+__device__ __forceinline__ void gemm_tile_impl(Prefetch<C, AK, BK_>& p,
+                                               const typename C::type* A,
                                                long long lda, int m0, int m_lim,
                                                const typename C::type* B,
                                                long long ldb, int n0, int n_lim, int k_begin,
@@ -267,40 +297,39 @@ __device__ __forceinline__ void gemm_tile_impl(const typename C::type* A,
   T* Bs = As + 2 * C::OPA;
   const int w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
   const int nk = (k_end - k_begin + C::BK - 1) / C::BK;
-  Vec16 ra[SA::Q], rb[SB::Q];
-  SA::template load<FULL>(A, lda, m0, m_lim, k_begin, k_end, a_vec, ra);
-  SB::template load<FULL>(B, ldb, n0, n_lim, k_begin, k_end, b_vec, rb);
-  SA::store(As, ra);
-  SB::store(Bs, rb);
+  SA::store(As, p.ra);
+  SB::store(Bs, p.rb);
   __syncthreads();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     // The last step reloads its own (in-bounds) stage into the idle buffer,
     // which keeps the loop body free of branches.
     const int k0 = k_begin + min(kt + 1, nk - 1) * C::BK;
-    SA::template load<FULL>(A, lda, m0, m_lim, k0, k_end, a_vec, ra);
-    SB::template load<FULL>(B, ldb, n0, n_lim, k0, k_end, b_vec, rb);
+    SA::template load<FULL>(A, lda, m0, m_lim, k0, k_end, a_vec, p.ra);
+    SB::template load<FULL>(B, ldb, n0, n_lim, k0, k_end, b_vec, p.rb);
     // Keep the next stage's global loads ahead of this stage's MFMAs so their
     // latency hides behind the matrix work (a compiler-only memory fence: no
     // memory operation moves across it, and the MFMAs wait on the LDS reads
     // below it).
     asm volatile("" ::: "memory");
     mma_stage<C, SA::COL, SB::COL>(As + cur * C::OPA, Bs + cur * C::OPB, acc, wm, wn);
-    SA::store(As + (cur ^ 1) * C::OPA, ra);
-    SB::store(Bs + (cur ^ 1) * C::OPB, rb);
+    SA::store(As + (cur ^ 1) * C::OPA, p.ra);
+    SB::store(Bs + (cur ^ 1) * C::OPB, p.rb);
     __syncthreads();
   }
 }
 
-// acc = A[m0:m0+BM, k] . B[n0:n0+BN, k]^T over k in [k_begin, k_end).
+// acc = A[m0:m0+BM, k] . B[n0:n0+BN, k]^T over k in [k_begin, k_end), with
+// the first stage already in `p` (from gemm_prefetch on the same tile).
 // Rows/columns past the limits and k past k_end read as zero.  Ends with a
 // barrier, so the caller may reuse `smem` right away.
 template <class C, bool AK, bool BK_>
-__device__ __forceinline__ void gemm_tile(const typename C::type* __restrict__ A, long long lda,
-                                          int m0, int m_lim,
-                                          const typename C::type* __restrict__ B, long long ldb,
-                                          int n0, int n_lim, int k_begin, int k_end, bool a_vec,
-                                          bool b_vec, f32x16 (&acc)[C::FM][C::FN], char* smem) {
+__device__ __forceinline__ void gemm_tile_run(Prefetch<C, AK, BK_>& p,
+                                              const typename C::type* A, long long lda, int m0,
+                                              int m_lim, const typename C::type* B,
+                                              long long ldb, int n0, int n_lim, int k_begin,
+                                              int k_end, bool a_vec, bool b_vec,
+                                              f32x16 (&acc)[C::FM][C::FN], char* smem) {
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
@@ -308,14 +337,26 @@ __device__ __forceinline__ void gemm_tile(const typename C::type* __restrict__ A
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fi][fj][r] = 0.f;
   if (k_end <= k_begin) return;
-  const bool full = a_vec && b_vec && m0 + C::BM <= m_lim && n0 + C::BN <= n_lim &&
-                    (k_end - k_begin) % C::BK == 0;
-  if (full)
-    gemm_tile_impl<C, AK, BK_, true>(A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
-                                     b_vec, acc, smem);
+  if (p.full)
+    gemm_tile_impl<C, AK, BK_, true>(p, A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end,
+                                     a_vec, b_vec, acc, smem);
   else
-    gemm_tile_impl<C, AK, BK_, false>(A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
-                                      b_vec, acc, smem);
+    gemm_tile_impl<C, AK, BK_, false>(p, A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end,
+                                      a_vec, b_vec, acc, smem);
+}
+
+// One tile, no cross-tile overlap.
+template <class C, bool AK, bool BK_>
+__device__ __forceinline__ void gemm_tile(const typename C::type* __restrict__ A, long long lda,
+                                          int m0, int m_lim,
+                                          const typename C::type* __restrict__ B, long long ldb,
+                                          int n0, int n_lim, int k_begin, int k_end, bool a_vec,
+                                          bool b_vec, f32x16 (&acc)[C::FM][C::FN], char* smem) {
+  Prefetch<C, AK, BK_> p;
+  gemm_prefetch<C, AK, BK_>(p, A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
+                            b_vec);
+  gemm_tile_run<C, AK, BK_>(p, A, lda, m0, m_lim, B, ldb, n0, n_lim, k_begin, k_end, a_vec,
+                            b_vec, acc, smem);
 }
 
 // Accumulator element (fi, fj, r) of lane l in wave (wm, wn) sits at tile row
@@ -397,6 +438,9 @@ struct EpiSmem {
 // BN-column tiles.  Per tile: MFMA logits, + bias, then per row the FP64 sum
 // of exp(z - row max over the tile) folded into the row's running partial,
 // and a gather of the selected columns into Zsel (class-major, K x M).
+// Epilogue mapping: each thread owns 4 consecutive rows (one 16-byte LDS
+// read per column) and a group of CPT columns; the RG = THREADS / (BM / 4)
+// column groups of a row are folded in order at the end of the span.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
@@ -405,56 +449,102 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     int nspan, int mtiles, int vec_ok) {
   using T = typename C::type;
   constexpr int BM = C::BM, BN = C::BN, TL = EpiSmem<C>::TL;
-  constexpr int TPR = C::THREADS / BM;  // threads sharing one row in the epilogue
-  constexpr int CPT = BN / TPR;         // columns per thread
-  static_assert(C::THREADS % BM == 0 && BN % TPR == 0, "epilogue split");
+  constexpr int RQ = BM / 4;              // row quads
+  constexpr int RG = C::THREADS / RQ;     // column groups per row quad
+  constexpr int CPT = BN / RG;            // columns per thread
+  static_assert(C::THREADS % RQ == 0 && BN % RG == 0 && BN <= C::THREADS, "epilogue split");
+  static_assert(RG * BM * (4 + 8) <= EpiSmem<C>::BYTES, "fold scratch");
   __shared__ __attribute__((aligned(16))) char smem[EpiSmem<C>::BYTES];
   __shared__ int s_sel[BN];
   __shared__ float s_bias[BN];
-  __shared__ float s_pm[TPR][BM];
-  __shared__ double s_ps[TPR][BM];
   int mt, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, nspan, mt, sp);
   const int m0 = mt * BM;
   const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
-  const int r = threadIdx.x % BM, pi = threadIdx.x / BM;
-  const int m = m0 + r;
-  float run_m = -INFINITY;
-  double run_s = 0.0;
+  const int rq = threadIdx.x % RQ, cg = threadIdx.x / RQ;
+  const int r0 = 4 * rq;
+  float run_m[4];
+  double run_s[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    run_m[j] = -INFINITY;
+    run_s[j] = 0.0;
+  }
   float* Zt = reinterpret_cast<float*>(smem);
+  // Tiles are walked with the next tile's first k stage and column data
+  // loaded before the current tile's epilogue.
+  Prefetch<C, true, true> pf;
+  gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, c_begin, c_end, 0, D, vec_ok, vec_ok);
+  int nsel = -1;
+  float nbias = 0.f;
+  if (threadIdx.x < BN) {
+    const int v = c_begin + threadIdx.x;
+    nsel = v < c_end ? col2sel[v] : -1;
+    nbias = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
+  }
   for (int n0 = c_begin; n0 < c_end; n0 += BN) {
     f32x16 acc[C::FM][C::FN];
-    gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c_end, 0, D, vec_ok, vec_ok, acc, smem);
+    gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c_end, 0, D, vec_ok, vec_ok, acc,
+                                 smem);
+    const int cur_sel = nsel;
+    const float cur_bias = nbias;
+    if (n0 + BN < c_end) {
+      gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, n0 + BN, c_end, 0, D, vec_ok, vec_ok);
+      if (threadIdx.x < BN) {
+        const int v = n0 + BN + threadIdx.x;
+        nsel = v < c_end ? col2sel[v] : -1;
+        nbias = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
+      }
+    }
     acc_to_lds<C>(acc, Zt, TL);
-    for (int c = threadIdx.x; c < BN; c += C::THREADS) {
-      const int v = n0 + c;
-      s_sel[c] = v < c_end ? col2sel[v] : -1;
-      s_bias[c] = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
+    if (threadIdx.x < BN) {
+      s_sel[threadIdx.x] = cur_sel;
+      s_bias[threadIdx.x] = cur_bias;
     }
     __syncthreads();
     const int ncol = min(BN, c_end - n0);
-    const int cb = pi * CPT, ce = min(cb + CPT, ncol);
-    if (m < M && ce > cb) {
-      float mx = -INFINITY;
-      for (int c = cb; c < ce; ++c) mx = fmaxf(mx, Zt[c * TL + r] + s_bias[c]);
-      double sum = 0.0;
-      const double dmx = (double)mx;
+    const int cb = cg * CPT, ce = min(cb + CPT, ncol);
+    if (ce > cb) {
+      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
       for (int c = cb; c < ce; ++c) {
-        const float z = Zt[c * TL + r] + s_bias[c];
-        sum += exp_nonpos((double)z - dmx);
-        const int sel = s_sel[c];
-        if (sel >= 0) Zsel[(long long)sel * M + m] = z;
+        const f32x4 z = *reinterpret_cast<const f32x4*>(Zt + c * TL + r0);
+        const float bv = s_bias[c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], z[j] + bv);
       }
-      lse_fold(run_m, run_s, mx, sum);
+      double sum[4] = {0.0, 0.0, 0.0, 0.0};
+      for (int c = cb; c < ce; ++c) {
+        const f32x4 z4 = *reinterpret_cast<const f32x4*>(Zt + c * TL + r0);
+        const float bv = s_bias[c];
+        const int sel = s_sel[c];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float z = z4[j] + bv;
+          sum[j] += exp_nonpos((double)z - (double)mx[j]);
+          if (sel >= 0 && m0 + r0 + j < M) Zsel[(long long)sel * M + m0 + r0 + j] = z;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) lse_fold(run_m[j], run_s[j], mx[j], sum[j]);
     }
     __syncthreads();
   }
-  s_pm[pi][r] = run_m;
-  s_ps[pi][r] = run_s;
+  // fold the RG column groups of every row, in group order
+  float* f_m = reinterpret_cast<float*>(smem);
+  double* f_s = reinterpret_cast<double*>(smem + RG * BM * 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    f_m[cg * BM + r0 + j] = run_m[j];
+    f_s[cg * BM + r0 + j] = run_s[j];
+  }
   __syncthreads();
-  if (pi == 0 && m < M) {
-    for (int q = 1; q < TPR; ++q) lse_fold(run_m, run_s, s_pm[q][r], s_ps[q][r]);
-    part[(long long)m * nspan + sp] = make_double2((double)run_m, run_s);
+  for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
+    const int m = m0 + rr;
+    if (m >= M) continue;
+    float fm = f_m[rr];
+    double fs = f_s[rr];
+    for (int q = 1; q < RG; ++q) lse_fold(fm, fs, f_m[q * BM + rr], f_s[q * BM + rr]);
+    part[(long long)m * nspan + sp] = make_double2((double)fm, fs);
   }
 }
 
