@@ -51,6 +51,15 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return ldexp(p, (int)n);
 }
 
+// Work-group barrier that orders LDS accesses only: the waves' outstanding
+// global loads and stores are not waited for (a plain __syncthreads also
+// drains them, which would expose prefetch and store latency).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <typename T> struct Elem;
 template <> struct Elem<float> {
   static constexpr int VEC = 4;  // elements per 16-byte vector

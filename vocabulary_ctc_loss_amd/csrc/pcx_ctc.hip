@@ -29,16 +29,73 @@ namespace {
 
 constexpr int PF = 8;  // frames per emission prefetch block
 
+// The recursion is a serial chain of log-add-exps, so its FP64 exp and log
+// are written for latency: the exp polynomial is evaluated by Estrin's
+// scheme (tree of depth 4 instead of a 13-step Horner chain), and the log is
+// specialised to arguments in [1, 4).
+
+// exp(x), x <= 0: Cody-Waite reduction by ln2 (32-bit head, tail), degree-13
+// Taylor polynomial of e^r, |r| <= ln2 / 2, scale by 2^n.
+__device__ __forceinline__ double exp_nonpos_lat(double x) {
+  x = fmax(x, -746.0);
+  const double n = rint(x * 0x1.71547652b82fep+0);
+  double r = fma(-n, 0x1.62e42ff000000p-1, x);
+  r = fma(-n, -0x1.718432a1b0e26p-35, r);
+  const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
+  const double p01 = r + 1.0;
+  const double p23 = fma(r, 0x1.5555555555555p-3, 0.5);                    // 1/3!, 1/2!
+  const double p45 = fma(r, 0x1.1111111111111p-7, 0x1.5555555555555p-5);   // 1/5!, 1/4!
+  const double p67 = fma(r, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10); // 1/7!, 1/6!
+  const double p89 = fma(r, 0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16); // 1/9!, 1/8!
+  const double pab = fma(r, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22); // 1/11!, 1/10!
+  const double pcd = fma(r, 0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29); // 1/13!, 1/12!
+  const double q0 = fma(r2, p23, p01), q1 = fma(r2, p67, p45), q2 = fma(r2, pab, p89);
+  const double s0 = fma(r4, q1, q0), s1 = fma(r4, pcd, q2);
+  return ldexp(fma(r8, s1, s0), (int)n);
+}
+
+// log(x), 1 <= x < 4: x = 2^e f with f in [sqrt(1/2), sqrt(2)), and
+// log f = 2 atanh(u), u = (f - 1) / (f + 1), |u| <= 0.172, by its odd series
+// through u^23 (truncation < 1e-18).
+__device__ __forceinline__ double log_1to4(double x) {
+  int e = 0;
+  double f = frexp(x, &e);
+  if (f < 0.70710678118654752440) {
+    f *= 2.0;
+    e -= 1;
+  }
+  // u = (f - 1) / (f + 1): hardware reciprocal refined by two Newton steps
+  const double den = f + 1.0;
+  double rc = __builtin_amdgcn_rcp(den);
+  rc = fma(rc, fma(-den, rc, 1.0), rc);
+  rc = fma(rc, fma(-den, rc, 1.0), rc);
+  const double u = (f - 1.0) * rc;
+  const double u2 = u * u, u4 = u2 * u2, u8 = u4 * u4;
+  const double a = fma(u2, 1.0 / 5, 1.0 / 3), b = fma(u2, 1.0 / 9, 1.0 / 7);
+  const double c = fma(u2, 1.0 / 13, 1.0 / 11), d = fma(u2, 1.0 / 17, 1.0 / 15);
+  const double g = fma(u2, 1.0 / 21, 1.0 / 19);
+  const double ab = fma(u4, b, a), cd = fma(u4, d, c), gh = fma(u4, 1.0 / 23, g);
+  const double p = fma(u8, fma(u8, gh, cd), ab);
+  const double lf = fma(2.0 * u * u2, p, 2.0 * u);
+  return fma((double)e, 0x1.62e42fefa39efp-1, lf);  // + e ln2
+}
+
+// log(e^a + e^b + e^c) = m + log(1 + e^(x-m) + e^(y-m)), m the largest and
+// x, y the other two (the max term contributes exactly 1).
 __device__ __forceinline__ double lse3(double a, double b, double c) {
-  const double m = fmax(a, fmax(b, c));
+  const bool am = a >= b && a >= c;
+  const bool bm = !am && b >= c;
+  const double m = am ? a : (bm ? b : c);
+  const double x = am ? b : a;
+  const double y = (am || bm) ? c : b;
   if (m == -INFINITY) return -INFINITY;
-  return m + log(exp_nonpos(a - m) + exp_nonpos(b - m) + exp_nonpos(c - m));
+  return m + log_1to4(1.0 + exp_nonpos_lat(x - m) + exp_nonpos_lat(y - m));
 }
 
 __device__ __forceinline__ double lse2(double a, double b) {
-  const double m = fmax(a, b);
+  const double m = fmax(a, b), x = fmin(a, b);
   if (m == -INFINITY) return -INFINITY;
-  return m + log(exp_nonpos(a - m) + exp_nonpos(b - m));
+  return m + log_1to4(1.0 + exp_nonpos_lat(x - m));
 }
 
 // Forward recursion; alpha[t][s] (including the emission at t) is stored
@@ -97,7 +154,7 @@ __global__ __launch_bounds__(1024) void k_alpha(
       out[s] = a;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int tb = 0; tb < T; tb += PF) {
     if (tb + PF < T) {
 #pragma unroll
@@ -127,7 +184,7 @@ __global__ __launch_bounds__(1024) void k_alpha(
           out[(long long)t * Sn + s] = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
@@ -200,7 +257,7 @@ __global__ __launch_bounds__(1024) void k_beta(
       out[(long long)tl * Sn + s] = b;
     }
   }
-  __syncthreads();
+  lds_barrier();
   for (int tb = 0; tb < T; tb += PF) {
     if (tb + PF < T) {
 #pragma unroll
@@ -230,7 +287,7 @@ __global__ __launch_bounds__(1024) void k_beta(
           out[(long long)t * Sn + s] = v;
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
@@ -269,7 +326,7 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   int* s_next = s_y + Lcap;                                // L ints
   int* s_lead = s_next + Lcap;                             // L ints
   for (int i = threadIdx.x; i < L; i += blockDim.x) s_y[i] = tgt_rel[y0 + i];
-  __syncthreads();
+  lds_barrier();
   for (int i = threadIdx.x; i < L; i += blockDim.x) {
     const int c = s_y[i];
     int lead = 1;
@@ -287,7 +344,7 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     s_lead[i] = lead;
     s_next[i] = nx;
   }
-  __syncthreads();
+  lds_barrier();
   const double logP = utt_logp[n];
   const double* A = alpha + dp_off[n];
   const double* B = beta + dp_off[n];
@@ -305,13 +362,13 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     }
     s_bl[threadIdx.x] = bl;
     s_tot[threadIdx.x] = tot;
-    __syncthreads();
+    lds_barrier();
     for (int stride = OCC_THREADS / 2; stride > 0; stride >>= 1) {
       if ((int)threadIdx.x < stride) {
         s_bl[threadIdx.x] += s_bl[threadIdx.x + stride];
         s_tot[threadIdx.x] += s_tot[threadIdx.x + stride];
       }
-      __syncthreads();
+      lds_barrier();
     }
     for (int i = threadIdx.x; i < L; i += blockDim.x) {
       if (s_lead[i]) {
@@ -324,7 +381,7 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
       Gam[row] = (float)s_bl[0];  // blank is U[0]
       g[row] = s_tot[0];
     }
-    __syncthreads();
+    lds_barrier();
   }
 }
 

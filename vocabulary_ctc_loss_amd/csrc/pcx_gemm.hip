@@ -299,7 +299,7 @@ __device__ __forceinline__ void gemm_tile_impl(Prefetch<C, AK, BK_>& p,
   const int nk = (k_end - k_begin + C::BK - 1) / C::BK;
   SA::store(As, p.ra);
   SB::store(Bs, p.rb);
-  __syncthreads();
+  lds_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
     // The last step reloads its own (in-bounds) stage into the idle buffer,
@@ -315,7 +315,7 @@ __device__ __forceinline__ void gemm_tile_impl(Prefetch<C, AK, BK_>& p,
     mma_stage<C, SA::COL, SB::COL>(As + cur * C::OPA, Bs + cur * C::OPB, acc, wm, wn);
     SA::store(As + (cur ^ 1) * C::OPA, p.ra);
     SB::store(Bs + (cur ^ 1) * C::OPB, p.rb);
-    __syncthreads();
+    lds_barrier();
   }
 }
 
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
       s_sel[threadIdx.x] = cur_sel;
       s_bias[threadIdx.x] = cur_bias;
     }
-    __syncthreads();
+    lds_barrier();
     const int ncol = min(BN, c_end - n0);
     const int cb = cg * CPT, ce = min(cb + CPT, ncol);
     if (ce > cb) {
@@ -527,7 +527,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
 #pragma unroll
       for (int j = 0; j < 4; ++j) lse_fold(run_m[j], run_s[j], mx[j], sum[j]);
     }
-    __syncthreads();
+    lds_barrier();
   }
   // fold the RG column groups of every row, in group order
   float* f_m = reinterpret_cast<float*>(smem);
@@ -537,7 +537,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     f_m[cg * BM + r0 + j] = run_m[j];
     f_s[cg * BM + r0 + j] = run_s[j];
   }
-  __syncthreads();
+  lds_barrier();
   for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
     const int m = m0 + rr;
     if (m >= M) continue;
@@ -672,7 +672,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     cs += __shfl_xor(cs, 32, 64);
     if (lane < 32) s_db[wm][col] = cs;
   }
-  __syncthreads();
+  lds_barrier();
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
     if (v < c1) {
@@ -777,7 +777,7 @@ __global__ __launch_bounds__(256) void k_db_reduce(const float* __restrict__ dbp
   if (c < cols)
     for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
   part[q][lc] = s;
-  __syncthreads();
+  lds_barrier();
   if (q == 0 && c < cols)
     db[col_base + c] = Elem<T>::from_f32(((part[0][lc] + part[1][lc]) + part[2][lc]) + part[3][lc]);
 }
@@ -793,7 +793,7 @@ __global__ void k_transpose(const T* __restrict__ src, int rows, int D, T* __res
     const int rr = r0 + r, dd = d0 + tx;
     t[r][tx] = (rr < rows && dd < D) ? src[(long long)rr * D + dd] : T(0);
   }
-  __syncthreads();
+  lds_barrier();
   for (int d = ty; d < 64; d += 4) {
     const int dd = d0 + d, rr = r0 + tx;
     if (dd < D && rr < rows) dst[(long long)dd * ldd + rr] = t[tx][d];
