@@ -71,9 +71,13 @@ __device__ __forceinline__ void grouped_tile(int lin, int mtiles, int ntiles, in
 // Tile configuration of one GEMM kernel: a BM x BN work-group tile computed
 // by (BM/WM) x (BN/WN) wavefronts of WM x WN, each a grid of MFMA 32 x 32
 // blocks; KB bytes of every operand row are staged per k step.
-template <typename T, int BM_, int BN_, int WM_, int WN_, int KB_, int MINWG_>
+template <typename T, int BM_, int BN_, int WM_, int WN_, int KB_, int MINWG_, int DEPTH_ = 1>
 struct Cfg {
   using type = T;
+  // Stages in flight between global memory and LDS: 1 = the next stage is
+  // loaded during this stage's MFMAs; 2 = the one after it (for short MFMA
+  // phases, where one stage of matrix work does not cover the load latency).
+  static constexpr int DEPTH = DEPTH_;
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int WGM = BM / WM, WGN = BN / WN;
   static constexpr int WAVES = WGM * WGN;
@@ -231,25 +235,31 @@ __device__ __forceinline__ void mma_stage(const typename C::type* __restrict__ A
     // bf16 (row layout only): lane half h feeds k in [h*BK/2, (h+1)*BK/2),
     // eight per v_mfma_f32_32x32x16_bf16.
     static_assert(!ACOL && !BCOL, "bf16 operands use the row layout");
+    // All fragments of the stage are read before its MFMAs: the short bf16
+    // MFMA phase cannot cover one LDS round trip per k step.
+    constexpr int KS = C::BK / 16;
+    bf16x8 a[KS][C::FM], b[KS][C::FN];
 #pragma unroll
-    for (int j = 0; j < C::BK / 16; ++j) {
-      bf16x8 a[C::FM], b[C::FN];
+    for (int j = 0; j < KS; ++j) {
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi)
-        a[fi] = __builtin_bit_cast(
+        a[j][fi] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(As + (wm * C::WM + fi * 32 + i) * C::LDK +
                                                     h * (C::BK / 2) + j * 8));
 #pragma unroll
       for (int fj = 0; fj < C::FN; ++fj)
-        b[fj] = __builtin_bit_cast(
+        b[j][fj] = __builtin_bit_cast(
             bf16x8, *reinterpret_cast<const uint4*>(Bs + (wn * C::WN + fj * 32 + i) * C::LDK +
                                                     h * (C::BK / 2) + j * 8));
+    }
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
         for (int fj = 0; fj < C::FN; ++fj)
-          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[fi], b[fj], acc[fi][fj], 0, 0, 0);
-    }
+          acc[fi][fj] =
+              __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][fi], b[j][fj], acc[fi][fj], 0, 0, 0);
   }
 }
 
@@ -299,6 +309,33 @@ __device__ __forceinline__ void gemm_tile_impl(Prefetch<C, AK, BK_>& p,
   const int nk = (k_end - k_begin + C::BK - 1) / C::BK;
   SA::store(As, p.ra);
   SB::store(Bs, p.rb);
+  if constexpr (C::DEPTH == 2) {
+    // Two register stages alternate; stage indices past the end are clamped
+    // (harmless reloads into a buffer that is never read).
+    Vec16 qa[SA::Q], qb[SB::Q];
+    auto kof = [&](int kt) { return k_begin + min(kt, nk - 1) * C::BK; };
+    SA::template load<FULL>(A, lda, m0, m_lim, kof(1), k_end, a_vec, p.ra);
+    SB::template load<FULL>(B, ldb, n0, n_lim, kof(1), k_end, b_vec, p.rb);
+    lds_barrier();
+    for (int kt = 0; kt < nk; kt += 2) {
+      SA::template load<FULL>(A, lda, m0, m_lim, kof(kt + 2), k_end, a_vec, qa);
+      SB::template load<FULL>(B, ldb, n0, n_lim, kof(kt + 2), k_end, b_vec, qb);
+      asm volatile("" ::: "memory");
+      mma_stage<C, SA::COL, SB::COL>(As, Bs, acc, wm, wn);
+      SA::store(As + C::OPA, p.ra);
+      SB::store(Bs + C::OPB, p.rb);
+      lds_barrier();
+      if (kt + 1 >= nk) break;
+      SA::template load<FULL>(A, lda, m0, m_lim, kof(kt + 3), k_end, a_vec, p.ra);
+      SB::template load<FULL>(B, ldb, n0, n_lim, kof(kt + 3), k_end, b_vec, p.rb);
+      asm volatile("" ::: "memory");
+      mma_stage<C, SA::COL, SB::COL>(As + C::OPA, Bs + C::OPB, acc, wm, wn);
+      SA::store(As, qa);
+      SB::store(Bs, qb);
+      lds_barrier();
+    }
+    return;
+  }
   lds_barrier();
   for (int kt = 0; kt < nk; ++kt) {
     const int cur = kt & 1;
@@ -406,13 +443,15 @@ __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double
 }
 
 
-// Tile configurations of the four head products (fp32 choices from a sweep
-// of tile / wave shapes on the V = 180k head: 128 x 128 work-group tiles,
-// 16-k stages; the dX product prefers eight 64 x 32 wavefronts).
+// Tile configurations of the four head products, chosen by sweeps of tile /
+// wave shapes on the V = 180k (fp32) and LLM (bf16) heads.  fp32: 128 x 128
+// work-group tiles with 16-k stages; the dX product prefers eight 64 x 32
+// wavefronts.
 using CfgF32 = Cfg<float, 128, 128, 64, 64, 64, 2>;
 using CfgF32Dx = Cfg<float, 128, 128, 64, 32, 128, 2>;
 using CfgB16 = Cfg<bf16_t, 128, 128, 64, 64, 128, 2>;
 using CfgB16W8 = Cfg<bf16_t, 128, 128, 32, 64, 128, 2>;
+using CfgB16Wide = Cfg<bf16_t, 128, 256, 64, 128, 64, 2>;
 template <typename T> struct Pick;
 template <> struct Pick<float> {
   using fwd = CfgF32;
@@ -420,9 +459,13 @@ template <> struct Pick<float> {
   using dx = CfgF32Dx;
   using dw = CfgF32;
 };
+// bf16: the forward kernel's LDS epilogue tile limits it to 128 x 128; the
+// recompute product takes 128 x 256 tiles of four 64 x 128 wavefronts (fewer
+// LDS bytes per MFMA at the bf16 rate); dX, whose epilogue is a fp32
+// accumulator update, runs eight 32 x 64 wavefronts.
 template <> struct Pick<bf16_t> {
   using fwd = CfgB16;
-  using rec = CfgB16W8;
+  using rec = CfgB16Wide;
   using dx = CfgB16W8;
   using dw = CfgB16;
 };
