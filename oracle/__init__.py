@@ -41,29 +41,20 @@ def build(force: bool = False) -> str:
     return _LIB
 
 
-_lib = None
-
-
-def _load():
-    global _lib
-    if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
-        P = ctypes.c_void_p
-        I = ctypes.c_int
-        lib.oracle_select.argtypes = [I, I, I, P, P, P, P, P, P]
-        lib.oracle_select.restype = I
-        lib.oracle_ctc_logits.argtypes = [I, I, I, P, P, I, ctypes.c_double,
-                                          P, P, P, P, P]
-        lib.oracle_ctc_logits.restype = I
-        lib.oracle_pcx.argtypes = [I, I, I, I, I, P, P, P, P, P, P,
-                                   ctypes.c_double, P, P, P, P, I, P, P, P,
-                                   P, P, P]
-        lib.oracle_pcx.restype = I
-        lib.oracle_num_threads.argtypes = []
-        lib.oracle_num_threads.restype = I
-        _lib = lib
-    return _lib
+def _bind(path):
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    I = ctypes.c_int
+    lib.oracle_select.argtypes = [I, I, I, P, P, P, P, P, P]
+    lib.oracle_select.restype = I
+    lib.oracle_ctc_logits.argtypes = [I, I, I, P, P, I, ctypes.c_double, P, P, P, P, P]
+    lib.oracle_ctc_logits.restype = I
+    lib.oracle_pcx.argtypes = [I, I, I, I, I, P, P, P, P, P, P, ctypes.c_double, P, P, P, P,
+                               I, P, P, P, P, P, P]
+    lib.oracle_pcx.restype = I
+    lib.oracle_num_threads.argtypes = []
+    lib.oracle_num_threads.restype = I
+    return lib
 
 
 def _ptr(a):
@@ -78,83 +69,125 @@ def _f64(a):
     return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
 
 
+class Oracle:
+    """The oracle's functions bound to one compiled copy of ctc_oracle.c."""
+
+    def __init__(self, path):
+        self.lib = _bind(path)
+
+    def num_threads(self) -> int:
+        return int(self.lib.oracle_num_threads())
+
+    def select(self, V, blank, frame_counts, tgt_off, tgt):
+        """Selected classes U (blank first, then ascending distinct labels),
+        relabelled targets and structural-alignability flags."""
+        fc, off, y = _i32(frame_counts), _i32(tgt_off), _i32(tgt)
+        N = fc.shape[0]
+        U = np.zeros(max(1, min(V, y.shape[0] + 1)), dtype=np.int32)
+        rel = np.zeros(max(1, y.shape[0]), dtype=np.int32)
+        flags = np.zeros(max(1, N), dtype=np.uint8)
+        K = self.lib.oracle_select(N, V, blank, _ptr(fc), _ptr(off), _ptr(y), _ptr(U),
+                                   _ptr(rel), _ptr(flags))
+        if K < 0:
+            raise ValueError("oracle_select rejected the batch (code %d)" % -K)
+        return U[:K].copy(), rel[: y.shape[0]].copy(), flags[:N].astype(bool)
+
+    def ctc_logits(self, Z, y, blank, grad=1.0, want_grad=True):
+        """CTC of one utterance from its raw logits Z (T x V)."""
+        Z = _f64(Z)
+        T, V = Z.shape
+        y = _i32(y)
+        loss = ctypes.c_double(0.0)
+        st = ctypes.c_int(0)
+        lam = np.zeros(T)
+        dZ = np.zeros((T, V)) if want_grad else None
+        gam = np.zeros((T, V)) if want_grad else None
+        rc = self.lib.oracle_ctc_logits(T, V, blank, _ptr(Z), _ptr(y) if y.size else None,
+                                        int(y.shape[0]), float(grad), ctypes.byref(loss),
+                                        ctypes.byref(st), _ptr(lam), _ptr(dZ), _ptr(gam))
+        if rc != 0:
+            raise ValueError("oracle_ctc_logits failed (code %d)" % rc)
+        return {"loss": loss.value, "status": st.value, "lambda": lam, "dZ": dZ, "gamma": gam}
+
+    def pcx(self, X, W, b, frame_counts, tgt_off, tgt, blank, grad=1.0, cols=None,
+            want_dX=True, want_dW=True, want_db=True, want_gamma=False, want_lambda=True):
+        """Full path: head projection, summed CTC loss and gradients in FP64.
+
+        X (M x D), W (V x D), b (V or None) are upcast exactly to FP64.  Returns
+        a dict with loss, utt_loss, status, lambda, logp_cols/gamma_cols (at the
+        columns ``cols``), dX, dW and db.
+        """
+        X, W = _f64(X), _f64(W)
+        bb = None if b is None else _f64(b)
+        M, D = X.shape
+        V = W.shape[0]
+        fc, off, y = _i32(frame_counts), _i32(tgt_off), _i32(tgt)
+        N = fc.shape[0]
+        cols = _i32(cols if cols is not None else [])
+        nc = int(cols.shape[0])
+        loss = ctypes.c_double(0.0)
+        utt = np.zeros(max(1, N))
+        st = np.zeros(max(1, N), dtype=np.int32)
+        lam = np.zeros(max(1, M)) if want_lambda else None
+        lpc = np.zeros((max(1, M), max(1, nc))) if nc else None
+        gmc = np.zeros((max(1, M), max(1, nc))) if (nc and want_gamma) else None
+        dX = np.zeros((M, D)) if want_dX else None
+        dW = np.zeros((V, D)) if want_dW else None
+        db = np.zeros(V) if want_db else None
+        rc = self.lib.oracle_pcx(N, M, D, V, blank, _ptr(X), _ptr(W), _ptr(bb), _ptr(fc),
+                                 _ptr(off), _ptr(y) if y.size else _ptr(np.zeros(1, np.int32)),
+                                 float(grad), ctypes.byref(loss), _ptr(utt), _ptr(st),
+                                 _ptr(lam), nc, _ptr(cols) if nc else None, _ptr(lpc),
+                                 _ptr(gmc), _ptr(dX), _ptr(dW), _ptr(db))
+        if rc != 0:
+            raise ValueError("oracle_pcx failed (code %d)" % rc)
+        out = {"loss": loss.value, "utt_loss": utt[:N].copy(), "status": st[:N].copy(),
+               "dX": dX, "dW": dW, "db": db}
+        out["lambda"] = lam[:M].copy() if want_lambda else None
+        out["logp_cols"] = lpc[:M, :nc].copy() if nc else None
+        out["gamma_cols"] = gmc[:M, :nc].copy() if gmc is not None else None
+        return out
+
+
+_default = None
+
+
+def _oracle() -> Oracle:
+    global _default
+    if _default is None:
+        _default = Oracle(build())
+    return _default
+
+
+def compile_variant(src_text: str, out_path: str) -> str:
+    """Compile a (test-modified) copy of the oracle source; used by the tests
+    that check the pins reject planted mistakes."""
+    src = out_path + ".c"
+    with open(src, "w") as f:
+        f.write(src_text)
+    subprocess.run(["gcc", "-O2", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-o", out_path, src, "-lm"], check=True)
+    return out_path
+
+
+def source_text() -> str:
+    return open(_SRC).read()
+
+
 def num_threads() -> int:
-    return int(_load().oracle_num_threads())
+    return _oracle().num_threads()
 
 
 def select(V, blank, frame_counts, tgt_off, tgt):
-    """Selected classes U (blank first, then ascending distinct labels),
-    relabelled targets and structural-alignability flags."""
-    lib = _load()
-    fc, off, y = _i32(frame_counts), _i32(tgt_off), _i32(tgt)
-    N = fc.shape[0]
-    U = np.zeros(max(1, min(V, y.shape[0] + 1)), dtype=np.int32)
-    rel = np.zeros(max(1, y.shape[0]), dtype=np.int32)
-    flags = np.zeros(max(1, N), dtype=np.uint8)
-    K = lib.oracle_select(N, V, blank, _ptr(fc), _ptr(off), _ptr(y), _ptr(U),
-                          _ptr(rel), _ptr(flags))
-    if K < 0:
-        raise ValueError("oracle_select rejected the batch (code %d)" % -K)
-    return U[:K].copy(), rel[: y.shape[0]].copy(), flags[:N].astype(bool)
+    return _oracle().select(V, blank, frame_counts, tgt_off, tgt)
 
 
 def ctc_logits(Z, y, blank, grad=1.0, want_grad=True):
-    """CTC of one utterance from its raw logits Z (T x V)."""
-    lib = _load()
-    Z = _f64(Z)
-    T, V = Z.shape
-    y = _i32(y)
-    loss = ctypes.c_double(0.0)
-    st = ctypes.c_int(0)
-    lam = np.zeros(T)
-    dZ = np.zeros((T, V)) if want_grad else None
-    gam = np.zeros((T, V)) if want_grad else None
-    rc = lib.oracle_ctc_logits(T, V, blank, _ptr(Z), _ptr(y) if y.size else None,
-                               int(y.shape[0]), float(grad), ctypes.byref(loss),
-                               ctypes.byref(st), _ptr(lam), _ptr(dZ), _ptr(gam))
-    if rc != 0:
-        raise ValueError("oracle_ctc_logits failed (code %d)" % rc)
-    return {"loss": loss.value, "status": st.value, "lambda": lam, "dZ": dZ,
-            "gamma": gam}
+    return _oracle().ctc_logits(Z, y, blank, grad=grad, want_grad=want_grad)
 
 
-def pcx(X, W, b, frame_counts, tgt_off, tgt, blank, grad=1.0, cols=None,
-        want_dX=True, want_dW=True, want_db=True, want_gamma=False,
-        want_lambda=True):
-    """Full path: head projection, summed CTC loss and gradients in FP64.
-
-    X (M x D), W (V x D), b (V or None) are upcast exactly to FP64.  Returns a
-    dict with loss, utt_loss, status, lambda, logp_cols/gamma_cols (at the
-    columns ``cols``), dX, dW and db.
-    """
-    lib = _load()
-    X, W = _f64(X), _f64(W)
-    bb = None if b is None else _f64(b)
-    M, D = X.shape
-    V = W.shape[0]
-    fc, off, y = _i32(frame_counts), _i32(tgt_off), _i32(tgt)
-    N = fc.shape[0]
-    cols = _i32(cols if cols is not None else [])
-    nc = int(cols.shape[0])
-    loss = ctypes.c_double(0.0)
-    utt = np.zeros(max(1, N))
-    st = np.zeros(max(1, N), dtype=np.int32)
-    lam = np.zeros(max(1, M)) if want_lambda else None
-    lpc = np.zeros((max(1, M), max(1, nc))) if nc else None
-    gmc = np.zeros((max(1, M), max(1, nc))) if (nc and want_gamma) else None
-    dX = np.zeros((M, D)) if want_dX else None
-    dW = np.zeros((V, D)) if want_dW else None
-    db = np.zeros(V) if want_db else None
-    rc = lib.oracle_pcx(N, M, D, V, blank, _ptr(X), _ptr(W), _ptr(bb), _ptr(fc),
-                        _ptr(off), _ptr(y) if y.size else _ptr(np.zeros(1, np.int32)),
-                        float(grad), ctypes.byref(loss), _ptr(utt), _ptr(st),
-                        _ptr(lam), nc, _ptr(cols) if nc else None, _ptr(lpc),
-                        _ptr(gmc), _ptr(dX), _ptr(dW), _ptr(db))
-    if rc != 0:
-        raise ValueError("oracle_pcx failed (code %d)" % rc)
-    out = {"loss": loss.value, "utt_loss": utt[:N].copy(), "status": st[:N].copy(),
-           "dX": dX, "dW": dW, "db": db}
-    out["lambda"] = lam[:M].copy() if want_lambda else None
-    out["logp_cols"] = lpc[:M, :nc].copy() if nc else None
-    out["gamma_cols"] = gmc[:M, :nc].copy() if gmc is not None else None
-    return out
+def pcx(X, W, b, frame_counts, tgt_off, tgt, blank, grad=1.0, cols=None, want_dX=True,
+        want_dW=True, want_db=True, want_gamma=False, want_lambda=True):
+    return _oracle().pcx(X, W, b, frame_counts, tgt_off, tgt, blank, grad=grad, cols=cols,
+                         want_dX=want_dX, want_dW=want_dW, want_db=want_db,
+                         want_gamma=want_gamma, want_lambda=want_lambda)

@@ -1,0 +1,110 @@
+"""The pins must be able to fail: planted mistakes in the oracle are caught.
+
+Each case below plants one plausible mistake in a copy of the oracle's C
+source (a dropped term, a wrong sign or index, a transposed operand, a missed
+CTC transition rule), compiles the copy with gcc and runs every pin of
+tests/test_oracle_pins.py against it.  A mutant survives only if all pins
+pass, which fails the test.  The unmodified source, compiled the same way,
+must pass every pin (the harness itself is sound).
+
+The transitions planted wrong here are the ones of the CTC recursion on the
+blank-interleaved label sequence ("Pruned CTC for Memory-Efficient
+Large-Vocabulary ASR Training", Sec. 3.1): stay, advance by one, and skip a
+blank only between two different labels; alignments start on the first blank
+or the first label and end on the last label or the final blank.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+# (name, original text, planted text); each original occurs exactly once.
+MUTANTS = [
+    ("log_add_drops_log1p", "return hi + log1p(exp(lo - hi));", "return hi + log(exp(lo - hi));"),
+    ("normalizer_drops_max", "double lam = mx + log(s);", "double lam = log(s);"),
+    ("normalizer_unshifted_exp", "s += exp(z[v] - mx);", "s += exp(z[v]);"),
+    ("skip_between_repeats", "ext[s] != blank && ext[s] != ext[s - 2]", "ext[s] != blank"),
+    ("skip_drops_a_label", "ext[s] != blank && ext[s] != ext[s - 2]",
+     "(ext[s] == blank || ext[s] != ext[s - 2])"),
+    ("beta_skip_between_repeats", "ext[s] != blank && ext[s] != ext[s + 2]", "ext[s] != blank"),
+    ("no_start_on_label", "if (S > 1) alpha[1] = logp[ext[1]];", ";"),
+    ("no_end_on_label", "if (S > 1) logP = log_add(logP, last[S - 2]);", ";"),
+    ("beta_no_end_on_label", "if (S > 1)\n      beta[(size_t)(T - 1) * S + S - 2] =",
+     "if (0)\n      beta[(size_t)(T - 1) * S + S - 2] ="),
+    ("gamma_double_emission", "beta[(size_t)t * S + s] -\n                      lp[ext[s]] - logP;",
+     "beta[(size_t)t * S + s] -\n                      logP;"),
+    ("gradient_sign", "grad * (exp(lp[v]) - gam_row[v])", "grad * (gam_row[v] - exp(lp[v]))"),
+    ("gradient_unscaled", "grad * (exp(lp[v]) - gam_row[v])", "(exp(lp[v]) - gam_row[v])"),
+    ("alignability_ignores_repeats_ctc", "if (L + r > T) {", "if (L > T) {"),
+    ("alignability_ignores_repeats_select", "flags[n] = (L + r <= frame_counts[n]) ? 1 : 0;",
+     "flags[n] = (L <= frame_counts[n]) ? 1 : 0;"),
+    ("relabel_off_by_one", "tgt_rel[i] = lo;", "tgt_rel[i] = lo - 1;"),
+    ("selection_descending", "for (int v = 0; v < V; ++v)\n    if (present[v]",
+     "for (int v = V - 1; v >= 0; --v)\n    if (present[v]"),
+    ("bias_dropped", "acc + (b ? b[v] : 0.0)", "acc"),
+    ("utterance_rows_unscaled", "const double* Xn = X + (size_t)row0 * D;",
+     "const double* Xn = X + (size_t)row0;"),
+    ("dW_transposed_operand", "const double* x = Xn + (size_t)t * D;\n            for",
+     "const double* x = W + (size_t)v * D;\n            for"),
+    ("dX_uses_X", "const double* w = W + (size_t)v * D;\n          for (int d = 0; d < D; ++d) dx[d]",
+     "const double* w = Xn + (size_t)t * D;\n          for (int d = 0; d < D; ++d) dx[d]"),
+    ("db_overwrites", "if (db) db[v] += g;", "if (db) db[v] = g;"),
+    ("loss_counts_unalignable_as_inf", "if (L + r > T) {\n    status = 1;",
+     "if (L + r > T) {\n    status = 1; loss = INFINITY;"),
+]
+
+
+def _calls():
+    """Every pin test with each of its parameter sets, as plain callables."""
+    out = []
+    for name in sorted(dir(pins)):
+        fn = getattr(pins, name)
+        if not name.startswith("test_") or not callable(fn):
+            continue
+        marks = [m for m in getattr(fn, "pytestmark", []) if m.name == "parametrize"]
+        if not marks:
+            out.append((name, fn, {}))
+            continue
+        (mark,) = marks
+        argnames = [a.strip() for a in mark.args[0].split(",")]
+        for vals in mark.args[1]:
+            vals = vals if len(argnames) > 1 else (vals,)
+            out.append((name, fn, dict(zip(argnames, vals))))
+    return out
+
+
+def _failures(lib_path):
+    saved = oracle._default
+    oracle._default = oracle.Oracle(lib_path)
+    failed = []
+    try:
+        for name, fn, kw in _calls():
+            try:
+                fn(**kw)
+            except Exception as e:  # an assertion, or the oracle rejecting its input
+                failed.append("%s%s: %s" % (name, kw or "", type(e).__name__))
+    finally:
+        oracle._default = saved
+    return failed
+
+
+@pytest.fixture(scope="module")
+def variant_dir(tmp_path_factory):
+    return tmp_path_factory.mktemp("oracle_variants")
+
+
+def test_unmodified_copy_passes_every_pin(variant_dir):
+    path = oracle.compile_variant(oracle.source_text(), os.path.join(variant_dir, "orig.so"))
+    assert _failures(path) == []
+
+
+@pytest.mark.parametrize("name,orig,planted", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(variant_dir, name, orig, planted):
+    src = oracle.source_text()
+    assert src.count(orig) == 1, "mutation anchor for %s not unique in the oracle" % name
+    path = oracle.compile_variant(src.replace(orig, planted),
+                                  os.path.join(variant_dir, name + ".so"))
+    failed = _failures(path)
+    assert failed, "no pin catches the planted mistake %s" % name
