@@ -298,8 +298,9 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
 
   if (M > 0) {
+    const int big = use_big_core(dtype, iD, chunk < iV ? chunk : iV, X, W);
     LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
-                                     (float*)ctx->S.p, (double2*)ctx->part.p, nspan));
+                                     (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big));
     LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,
                                    (double*)ctx->lam.p, (float*)ctx->lamf.p));
     LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
@@ -374,7 +375,8 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
                                  (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
                                  (float*)ctx->Gam.p, (double*)ctx->g.p));
 
-  const int mtiles = (M + rec_tile_rows(dt) - 1) / rec_tile_rows(dt);
+  const int big = use_big_core(dt, D, C, ctx->X, ctx->W);
+  const int mtiles = (M + rec_tile_rows(dt, big) - 1) / rec_tile_rows(dt, big);
   ENSURE(dZ, (size_t)M * C * esz);
   ENSURE(dbpart, (size_t)mtiles * C * sizeof(float));
   float* dxacc = nullptr;
@@ -403,10 +405,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
            launch_recompute(st, dt, ctx->X, ctx->W, ctx->b, M, D, c0, c1,
                             (const int*)ctx->col2sel.p, (const float*)ctx->lamf.p,
                             (const double*)ctx->g.p, S, (const float*)ctx->Gam.p, grad_loss,
-                            ctx->dZ.p, C, (float*)ctx->dbpart.p));
+                            ctx->dZ.p, C, (float*)ctx->dbpart.p, big));
     if (dX)
       LAUNCH(K_DX, launch_dx(st, dt, ctx->dZ.p, C, ctx->W, M, D, c0, c1, dxacc, ch == 0,
-                             ctx->wt.p));
+                             ctx->wt.p, big));
     if (dW) {
       LAUNCH(K_DW, launch_dw(st, dt, ctx->dZ.p, C, ctx->X, M, D, c0, c1,
                              (float*)ctx->dwpart.p, splitk));

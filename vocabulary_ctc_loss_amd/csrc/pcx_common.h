@@ -107,10 +107,15 @@ hipError_t launch_prepare(hipStream_t st, int N, int M, int V, int blank, long l
                           int* row_off, uint8_t* flags, long long* dp_off,
                           int* col2sel, int* U, int* tgt_rel, Meta* meta);
 
+// Whether a bf16 head runs on the 256 x 256 GEMM core: head dimension and
+// chunk width multiples of 64, 16-byte aligned X and W (the same answer for
+// the forward and the backward pass of one call).
+int use_big_core(int dtype, int D, int chunk, const void* X, const void* W);
+
 // Forward head (pcx_gemm.hip).
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W,
                           const void* b, int M, int D, int V, const int* col2sel,
-                          float* Zsel, double2* part, int nspan);
+                          float* Zsel, double2* part, int nspan, int big);
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan,
                          double* lam, float* lamf);
 hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int M);
@@ -120,14 +125,14 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const void* b, int M, int D, int c0, int c1,
                             const int* col2sel, const float* lamf, const double* g,
                             const float* S, const float* Gam, double grad,
-                            void* dZ, int ldz, float* dbpart);
+                            void* dZ, int ldz, float* dbpart, int big);
 // wt: D x ldz scratch for the transposed weight chunk (bf16 only).
 // Rows of the recompute tile (one bias-gradient partial per row tile) and
 // the number of output tiles of one dW product.
-int rec_tile_rows(int dtype);
+int rec_tile_rows(int dtype, int big);
 int dw_tiles(int dtype, int C, int D);
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
-                     int M, int D, int c0, int c1, float* dXacc, int first, void* wt);
+                     int M, int D, int c0, int c1, float* dXacc, int first, void* wt, int big);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
 hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk,

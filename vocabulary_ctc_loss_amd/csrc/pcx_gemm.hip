@@ -825,10 +825,11 @@ __global__ __launch_bounds__(256) void k_db_reduce(const float* __restrict__ dbp
     db[col_base + c] = Elem<T>::from_f32(((part[0][lc] + part[1][lc]) + part[2][lc]) + part[3][lc]);
 }
 
-// dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS).
+// dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS);
+// columns c in [rows, rows_pad) of dst are written as zeros.
 template <typename T>
-__global__ void k_transpose(const T* __restrict__ src, int rows, int D, T* __restrict__ dst,
-                            int ldd) {
+__global__ void k_transpose(const T* __restrict__ src, int rows, int rows_pad, int D,
+                            T* __restrict__ dst, int ldd) {
   __shared__ T t[64][65];
   const int r0 = blockIdx.y * 64, d0 = blockIdx.x * 64;
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
@@ -839,7 +840,7 @@ __global__ void k_transpose(const T* __restrict__ src, int rows, int D, T* __res
   lds_barrier();
   for (int d = ty; d < 64; d += 4) {
     const int dd = d0 + d, rr = r0 + tx;
-    if (dd < D && rr < rows) dst[(long long)dd * ldd + rr] = t[tx][d];
+    if (dd < D && rr < rows_pad) dst[(long long)dd * ldd + rr] = t[tx][d];
   }
 }
 
@@ -847,6 +848,428 @@ __global__ void k_cast_bf16(const float* __restrict__ src, bf16_t* __restrict__ 
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x)
     dst[i] = f32_to_bf16(src[i]);
+}
+
+// ------------------------------------------------ bf16 core for 256 x 256 tiles
+// A second GEMM core for bf16 heads whose reduction length is a multiple of
+// 64 (the LLM head): a 256 x 256 work-group tile of eight wavefronts, WGM x
+// WGN of them, both operands K-contiguous.  Each k stage holds 64 values (128
+// bytes) of all 256 rows of both operands, double buffered in LDS (128 KiB),
+// and is filled by 16-byte global->LDS loads that need no staging registers:
+// one wave-wide load writes 1 KiB of LDS, lane l at byte 16 l.  The loads of
+// stage s + 1 are issued at the start of stage s; a work-group barrier (after
+// each wave's own loads have landed) separates the stages.
+//
+// LDS layout: row r at byte 128 r, its 16-byte chunk c (k values 8c..8c+7) at
+// chunk position c ^ ((r / 2) % 8).  A 16-byte fragment read is served for
+// 16 lanes at a time over 64 four-byte banks; the 16 rows one such group
+// reads sit two per 256-byte bank window, and the permutation gives the rows
+// sharing a window slot distinct chunk positions, so each group touches
+// every bank once.  The loads write whole 1 KiB blocks, so they place row r's
+// chunk c by choosing which global chunk each lane fetches.
+//
+// Within a stage, lane half h feeds the MFMA k values 32h..32h+31, eight per
+// v_mfma_f32_32x32x16_bf16 (the same relabelling of k for both operands).
+template <int WGM_, int WGN_>
+struct CfgBig {
+  using type = bf16_t;
+  static constexpr int BM = 256, BN = 256;
+  static constexpr int WGM = WGM_, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  static constexpr int BK = 64, ROWB = 128, CH = 8, KS = BK / 16;
+  static constexpr int TILEB = 256 * ROWB;            // one operand stage
+  static constexpr int STAGEB = 2 * TILEB;            // both operands
+  static constexpr int LDS_BYTES = 2 * STAGEB;        // double buffered
+  static constexpr int NLD = TILEB / 1024 / WAVES;    // 1 KiB loads per wave and operand
+  static constexpr int MINWG = 1;
+  static_assert(TILEB % (1024 * WAVES) == 0 && WM % 32 == 0 && WN % 32 == 0, "big tile");
+};
+using CfgBigB16 = CfgBig<2, 4>;
+
+#define PCX_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
+
+// Global->LDS loads of one operand stage: rows r0.. (clamped to rlim - 1;
+// those rows only feed accumulator rows the callers discard), k0..k0+63.
+template <class C>
+__device__ __forceinline__ void big_stage(const bf16_t* __restrict__ G, long long ld, int r0,
+                                          int rlim, int k0, char* dst) {
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+#pragma unroll
+  for (int q = 0; q < C::NLD; ++q) {
+    const int u = w * C::NLD + q;  // 1 KiB block: rows 8u..8u+7
+    const int row = u * 8 + (l >> 3);
+    const int c = (l & 7) ^ big_swz(row);
+    const int gr = min(r0 + row, rlim - 1);
+    __builtin_amdgcn_global_load_lds((const void*)(G + (long long)gr * ld + k0 + c * 8),
+                                     PCX_LDS_PTR(dst + u * 1024), 16, 0, 0);
+  }
+}
+
+// Barrier of the big core: this wave's LDS reads are complete and at most N
+// of its global->LDS loads are in flight, then all waves meet.  (A release
+// fence would also wait for every outstanding global->LDS load.)
+template <int N>
+__device__ __forceinline__ void big_barrier() {
+  static_assert(N >= 0 && N < 16, "vmcnt");
+  __builtin_amdgcn_s_waitcnt(N | (7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <class C>
+__device__ __forceinline__ void big_frags(const char* buf, int j, int wm, int wn,
+                                          bf16x8 (&a)[C::FM], bf16x8 (&b)[C::FN]) {
+  const int lane = threadIdx.x & 63, i = lane & 31, h = lane >> 5;
+  const int c = h * C::KS + j;
+#pragma unroll
+  for (int f = 0; f < C::FM; ++f) {
+    const int r = wm * C::WM + f * 32 + i;
+    a[f] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(buf + r * C::ROWB + ((c ^ big_swz(r)) << 4)));
+  }
+#pragma unroll
+  for (int f = 0; f < C::FN; ++f) {
+    const int r = wn * C::WN + f * 32 + i;
+    b[f] = __builtin_bit_cast(
+        bf16x8, *reinterpret_cast<const uint4*>(buf + C::TILEB + r * C::ROWB +
+                                                ((c ^ big_swz(r)) << 4)));
+  }
+}
+
+// acc = A[m0:m0+256, k] . B[n0:n0+256, k]^T over k in [0, K); K % 64 == 0,
+// K > 0, lda and ldb multiples of 8, A and B 16-byte aligned, m_lim and
+// n_lim >= 1.  Ends with a barrier (smem may be reused right away).
+template <class C>
+__device__ __forceinline__ void gemm_big(const bf16_t* __restrict__ A, long long lda, int m0,
+                                         int m_lim, const bf16_t* __restrict__ B, long long ldb,
+                                         int n0, int n_lim, int K, f32x16 (&acc)[C::FM][C::FN],
+                                         char* smem) {
+  const int w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
+  const int nk = K / C::BK;
+#pragma unroll
+  for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[fi][fj][r] = 0.f;
+  big_stage<C>(A, lda, m0, m_lim, 0, smem);
+  big_stage<C>(B, ldb, n0, n_lim, 0, smem + C::TILEB);
+  big_barrier<0>();
+  bf16x8 fa[2][C::FM], fb[2][C::FN];
+  big_frags<C>(smem, 0, wm, wn, fa[0], fb[0]);
+  for (int s = 0; s < nk; ++s) {
+    const char* cur = smem + (s & 1) * C::STAGEB;
+    char* nxt = smem + ((s + 1) & 1) * C::STAGEB;
+    // the last stage reloads itself into the idle buffer (no branch)
+    const int kn = min(s + 1, nk - 1) * C::BK;
+    big_stage<C>(A, lda, m0, m_lim, kn, nxt);
+    big_stage<C>(B, ldb, n0, n_lim, kn, nxt + C::TILEB);
+#pragma unroll
+    for (int j = 0; j < C::KS; ++j) {
+      if (j + 1 < C::KS) {
+        big_frags<C>(cur, j + 1, wm, wn, fa[(j + 1) & 1], fb[(j + 1) & 1]);
+      } else {
+        big_barrier<0>();
+        big_frags<C>(nxt, 0, wm, wn, fa[(j + 1) & 1], fb[(j + 1) & 1]);
+      }
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int fj = 0; fj < C::FN; ++fj)
+          acc[fi][fj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[j & 1][fi], fb[j & 1][fj],
+                                                                acc[fi][fj], 0, 0, 0);
+      // one fragment read between consecutive MFMAs, so the reads of the
+      // next k step overlap this step's matrix work
+#pragma unroll
+      for (int q = 0; q < C::FM + C::FN; ++q) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN - C::FM - C::FN, 0);
+    }
+  }
+  big_barrier<0>();
+}
+
+// Forward on the big core, computed transposed: the tile is 256 vocabulary
+// rows (operand A = W) by 256 frames (operand B = X), so every lane holds 64
+// vocabulary values of each of its FN frames and the per-frame log-sum-exp
+// of a tile needs no cross-lane step.  One work-group: 256 frames x one
+// LSE_SPAN-wide vocabulary span in 256-row tiles.  Per tile and frame, each
+// lane folds max and FP64 sum of exp(z - max) over its 64 values into its
+// running partial; at the end of the span the partials of the two lane
+// halves and of the WGM wave rows are folded in a fixed order.  Selected
+// vocabulary rows are gathered into Zsel (class-major, K x M), 32 frames per
+// coalesced store.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
+    int M, int D, int V, const int* __restrict__ col2sel, float* __restrict__ Zsel,
+    double2* __restrict__ part, int nspan, int ftiles) {
+  // One LDS object for everything: with a second one, the compiler makes
+  // every fragment read wait for all outstanding global->LDS loads.
+  constexpr int O_SEL = C::LDS_BYTES, O_BIAS = O_SEL + 2 * C::BM * 4;
+  constexpr int O_FM = O_BIAS + 2 * C::BM * 4, O_FS = O_FM + C::WGM * C::BN * 4;
+  __shared__ __attribute__((aligned(16))) char smem[O_FS + C::WGM * C::BN * 8];
+  int (*s_sel)[C::BM] = reinterpret_cast<int (*)[C::BM]>(smem + O_SEL);
+  float (*s_bias)[C::BM] = reinterpret_cast<float (*)[C::BM]>(smem + O_BIAS);
+  float (*f_m)[C::BN] = reinterpret_cast<float (*)[C::BN]>(smem + O_FM);
+  double (*f_s)[C::BN] = reinterpret_cast<double (*)[C::BN]>(smem + O_FS);
+  int ft, sp;
+  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
+  const int f0 = ft * C::BN;
+  const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  float run_m[C::FN];
+  double run_s[C::FN];
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    run_m[fj] = -INFINITY;
+    run_s[fj] = 0.0;
+  }
+  int par = 0;
+  for (int v0 = c_begin; v0 < c_end; v0 += C::BM, par ^= 1) {
+    // this tile's row data; visible after the core's barriers, and the
+    // buffer written here was last read two tiles ago
+    for (int r = threadIdx.x; r < C::BM; r += C::THREADS) {
+      const int v = v0 + r;
+      s_sel[par][r] = v < c_end ? col2sel[v] : -2;  // -2: past the span
+      s_bias[par][r] = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+    }
+    f32x16 acc[C::FM][C::FN];
+    gemm_big<C>(W, D, v0, c_end, X, D, f0, M, D, acc, smem);
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int frame = f0 + acc_col<C>(fj);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = acc_row<C>(fi, 4 * q);
+          const int4 sel4 = *reinterpret_cast<const int4*>(&s_sel[par][r0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_bias[par][r0]);
+          const int sl[4] = {sel4.x, sel4.y, sel4.z, sel4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[fi][fj][4 * q + e] + b4[e];
+            acc[fi][fj][4 * q + e] = sl[e] >= -1 ? z : -INFINITY;
+            mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
+            if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      double sum = 0.0;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int fi = 0; fi < C::FM; ++fi) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sum += exp_nonpos((double)acc[fi][fj][r] - (double)mx);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      lse_fold(run_m[fj], run_s[fj], mx, sum);
+    }
+  }
+  // lane halves (lower half first), then wave rows in order
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    const float om = __shfl_xor(run_m[fj], 32, 64);
+    const double os = __shfl_xor(run_s[fj], 32, 64);
+    float m1 = lane < 32 ? run_m[fj] : om;
+    double s1 = lane < 32 ? run_s[fj] : os;
+    lse_fold(m1, s1, lane < 32 ? om : run_m[fj], lane < 32 ? os : run_s[fj]);
+    if (lane < 32) {
+      f_m[wm][acc_col<C>(fj)] = m1;
+      f_s[wm][acc_col<C>(fj)] = s1;
+    }
+  }
+  lds_barrier();
+  for (int c = threadIdx.x; c < C::BN; c += C::THREADS) {
+    const int frame = f0 + c;
+    if (frame >= M) continue;
+    float fm = f_m[0][c];
+    double fs = f_s[0][c];
+#pragma unroll
+    for (int q = 1; q < C::WGM; ++q) lse_fold(fm, fs, f_m[q][c], f_s[q][c]);
+    part[(long long)frame * nspan + sp] = make_double2((double)fm, fs);
+  }
+}
+
+// Backward recompute on the big core (frames x vocabulary, as k_recompute):
+// the same per-element formulas; in addition the chunk block's columns
+// between the chunk end and the next multiple of 64 are written as zeros,
+// because the dX product on the big core reduces over whole 64-column steps.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
+    const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
+    int M, int D, int c0, int c1, const int* __restrict__ col2sel,
+    const float* __restrict__ lamf, const double* __restrict__ g, const float* __restrict__ S,
+    const float* __restrict__ Gam, double grad, bf16_t* __restrict__ dZ, int ldz,
+    float* __restrict__ dbpart, int mtiles) {
+  constexpr int BM = C::BM, BN = C::BN;
+  constexpr float LOG2E = 1.44269504088896340736f;
+  // one LDS object (see k_fwd_lse_big)
+  constexpr int O_G = C::LDS_BYTES, O_SEL = O_G + BM * 8, O_BIAS = O_SEL + BN * 4;
+  constexpr int O_LAM = O_BIAS + BN * 4, O_RS = O_LAM + BM * 4, O_DB = O_RS + BM * 4;
+  __shared__ __attribute__((aligned(16))) char smem[O_DB + C::WGM * BN * 4];
+  double* s_g = reinterpret_cast<double*>(smem + O_G);
+  int* s_sel = reinterpret_cast<int*>(smem + O_SEL);
+  float* s_bias = reinterpret_cast<float*>(smem + O_BIAS);
+  float* s_lam2 = reinterpret_cast<float*>(smem + O_LAM);
+  float* s_rs = reinterpret_cast<float*>(smem + O_RS);
+  float (*s_db)[BN] = reinterpret_cast<float (*)[BN]>(smem + O_DB);
+  int mt, nt;
+  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
+  const int m0 = mt * BM, n0 = c0 + nt * BN;
+  const int c_pad = c0 + ((c1 - c0 + 63) & ~63);
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) {
+    const int v = n0 + c;
+    s_sel[c] = v < c1 ? col2sel[v] : -1;
+    s_bias[c] = (bias != nullptr && v < c1) ? bf16_to_f32(bias[v]) : 0.f;
+  }
+  for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
+    const int mm = m0 + rr;
+    const double gm = mm < M ? g[mm] : 0.0;
+    s_g[rr] = gm;
+    s_rs[rr] = (float)(grad * gm);
+    s_lam2[rr] = mm < M ? lamf[mm] * LOG2E : 0.f;
+  }
+  f32x16 acc[C::FM][C::FN];
+  gemm_big<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  const bool rows_full = m0 + BM <= M;
+  // Column roles: 0 = unselected class (formula below), 1 = padding up to
+  // the next multiple of 64 (zero), 2 = selected class or past the padding
+  // (left to the pass after this one / not written).
+  int csel[C::FN], crole[C::FN];
+  float cbv[C::FN], cs[C::FN];
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    const int col = acc_col<C>(fj);
+    const int v = n0 + col;
+    csel[fj] = s_sel[col];
+    cbv[fj] = s_bias[col];
+    crole[fj] = v < c1 ? (csel[fj] < 0 ? 0 : 2) : (v < c_pad ? 1 : 2);
+    cs[fj] = 0.f;
+  }
+  // Unselected classes: every lane its own accumulators, four rows at a time.
+#pragma unroll
+  for (int fi = 0; fi < C::FM; ++fi) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row0 = acc_row<C>(fi, 4 * q);
+      const f32x4 rs4 = *reinterpret_cast<const f32x4*>(s_rs + row0);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(s_lam2 + row0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + e;
+        const bool in = rows_full || m0 + row < M;
+#pragma unroll
+        for (int fj = 0; fj < C::FN; ++fj) {
+          float dz =
+              rs4[e] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
+          if (crole[fj] == 1) dz = 0.f;
+          if (in && crole[fj] != 2) {
+            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = f32_to_bf16(dz);
+            cs[fj] += dz;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    cs[fj] += __shfl_xor(cs[fj], 32, 64);
+    if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
+  }
+  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g, so
+  // each selected column of this wavefront is done by all 64 lanes, two of
+  // the wavefront's 128 rows each; the column sum is a fixed-order wave sum.
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    unsigned long long todo = __ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0);
+    while (todo) {
+      const int src = __ffsll((long long)todo) - 1;
+      todo &= todo - 1;
+      const int sel = __shfl(csel[fj], src, 64);
+      const int col = (w % C::WGN) * C::WN + fj * 32 + src;
+      const float* Sp = S + (long long)sel * M + m0;
+      const float* Gp = Gam + (long long)sel * M + m0;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int row = wm * C::WM + 2 * lane + t;
+        if (m0 + row < M) {
+          // S <= 0 (a log-probability)
+          const float dz =
+              (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
+          dZ[(long long)(m0 + row) * ldz + (n0 + col - c0)] = f32_to_bf16(dz);
+          sum += dz;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) s_db[wm][col] = sum;
+    }
+  }
+  lds_barrier();
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) {
+    const int v = n0 + c;
+    if (v < c1) {
+      float t = s_db[0][c];
+#pragma unroll
+      for (int q = 1; q < C::WGM; ++q) t += s_db[q][c];
+      dbpart[(long long)mt * ldz + (v - c0)] = t;
+    }
+  }
+}
+
+// dXacc (+)= dZ_c . W_c on the big core: dZ_c (frames x Kp, leading
+// dimension ldz) and the transposed chunk Wt (D x Kp, leading dimension ldz),
+// both zero in the columns past the chunk end; Kp = chunk width rounded up to
+// a multiple of 64.
+template <class C>
+__global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restrict__ dZ,
+                                                          const bf16_t* __restrict__ Wt, int ldz,
+                                                          int M, int D, int Kp,
+                                                          float* __restrict__ dXacc, int first) {
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
+  const int ntiles = (D + C::BN - 1) / C::BN;
+  const int lin = xcd_tile(blockIdx.x, gridDim.x);
+  const int nt = lin % ntiles, mt = lin / ntiles;
+  const int m0 = mt * C::BM, n0 = nt * C::BN;
+  f32x16 acc[C::FM][C::FN];
+  gemm_big<C>(dZ, ldz, m0, M, Wt, ldz, n0, D, Kp, acc, smem);
+  // Read-modify-write of the fp32 accumulator, one block of 16 rows at a
+  // time with all of the block's loads issued before its stores (in program
+  // order: the compiler cannot tell the addresses apart).
+#pragma unroll
+  for (int fi = 0; fi < C::FM; ++fi) {
+    float old[C::FN][16];
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = n0 + acc_col<C>(fj);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = m0 + acc_row<C>(fi, rr);
+        old[fj][rr] = (!first && row < M && col < D) ? dXacc[(long long)row * D + col] : 0.f;
+      }
+    }
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = n0 + acc_col<C>(fj);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int row = m0 + acc_row<C>(fi, rr);
+        if (row < M && col < D) dXacc[(long long)row * D + col] = old[fj][rr] + acc[fi][fj][rr];
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 int grid_cap(long long n, int threads, int cap = 8192) {
@@ -877,9 +1300,17 @@ hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b
 
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                           int M, int D, int V, const int* col2sel, float* Zsel, double2* part,
-                          int nspan) {
-  return dtype == 0 ? fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan)
-                    : fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
+                          int nspan, int big) {
+  if (dtype == 0) return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
+  if (!big) return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
+  using C = CfgBigB16;
+  const int ftiles = ceil_div(M, C::BN);
+  const int grid = ftiles * nspan;
+  if (grid == 0) return hipSuccess;
+  k_fwd_lse_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
+                                                 (const bf16_t*)b, M, D, V, col2sel, Zsel, part,
+                                                 nspan, ftiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan, double* lam,
@@ -915,15 +1346,26 @@ hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void*
 hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                             int M, int D, int c0, int c1, const int* col2sel, const float* lamf,
                             const double* g, const float* S, const float* Gam, double grad,
-                            void* dZ, int ldz, float* dbpart) {
-  return dtype == 0 ? recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam,
-                                         grad, dZ, ldz, dbpart)
-                    : recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam,
-                                          grad, dZ, ldz, dbpart);
+                            void* dZ, int ldz, float* dbpart, int big) {
+  if (dtype == 0)
+    return recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ, ldz,
+                              dbpart);
+  if (!big)
+    return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
+                               ldz, dbpart);
+  using C = CfgBigB16;
+  const int mtiles = ceil_div(M, C::BM);
+  const int grid = mtiles * ceil_div(c1 - c0, C::BN);
+  if (grid == 0) return hipSuccess;
+  k_recompute_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
+                                                   (const bf16_t*)b, M, D, c0, c1, col2sel, lamf,
+                                                   g, S, Gam, grad, (bf16_t*)dZ, ldz, dbpart,
+                                                   mtiles);
+  return hipGetLastError();
 }
 
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W, int M,
-                     int D, int c0, int c1, float* dXacc, int first, void* wt) {
+                     int D, int c0, int c1, float* dXacc, int first, void* wt, int big) {
   const int Cc = c1 - c0;
   if (dtype == 0) {
     using C = Pick<float>::dx;
@@ -937,14 +1379,24 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
                                                 first, mtiles, av, bv);
   } else {
     // bf16: stage W_c^T (D x Cc, leading dimension ldz) so both operands are
-    // K-contiguous.
+    // K-contiguous; for the big core its rows up to the next multiple of 64
+    // are zero.
+    const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
+    const int Kp = big ? (Cc + 63) & ~63 : Cc;
+    dim3 tg(ceil_div(D, 64), ceil_div(Kp, 64));
+    k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+    if (big) {
+      using C = CfgBigB16;
+      const int grid = ceil_div(M, C::BM) * ceil_div(D, C::BN);
+      if (grid == 0) return hipSuccess;
+      k_dx_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)dZ, (const bf16_t*)wt, ldz, M, D,
+                                                Kp, dXacc, first);
+      return hipGetLastError();
+    }
     using C = Pick<bf16_t>::dx;
     const int mtiles = ceil_div(M, C::BM);
     const int grid = mtiles * ceil_div(D, C::BN);
     if (grid == 0) return hipSuccess;
-    const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
-    dim3 tg(ceil_div(D, 64), ceil_div(Cc, 64));
-    k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, D, (bf16_t*)wt, ldz);
     const int av = (ldz % 8 == 0) && aligned16(dZ);
     const int bv = (ldz % 8 == 0) && aligned16(wt);
     k_dx<C, true><<<grid, C::THREADS, 0, st>>>((const bf16_t*)dZ, ldz, (const bf16_t*)wt, ldz, M,
@@ -975,7 +1427,14 @@ hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const v
                     : dw_t<bf16_t>(st, dZ, ldz, X, M, D, c0, c1, part, splitk);
 }
 
-int rec_tile_rows(int dtype) { return dtype == 0 ? Pick<float>::rec::BM : Pick<bf16_t>::rec::BM; }
+int rec_tile_rows(int dtype, int big) {
+  if (dtype == 0) return Pick<float>::rec::BM;
+  return big ? CfgBigB16::BM : Pick<bf16_t>::rec::BM;
+}
+
+int use_big_core(int dtype, int D, int chunk, const void* X, const void* W) {
+  return dtype != 0 && D > 0 && D % 64 == 0 && chunk % 64 == 0 && aligned16(X) && aligned16(W);
+}
 
 int dw_tiles(int dtype, int C, int D) {
   if (dtype == 0)
