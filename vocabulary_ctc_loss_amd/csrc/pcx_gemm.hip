@@ -664,56 +664,80 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   f32x16 acc[C::FM][C::FN];
   gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
+  const bool rows_full = m0 + BM <= M;
+  // Unselected classes on the accumulators, four rows at a time; selected
+  // classes (role 2) and columns past the chunk (role 3) are skipped here.
+  int csel[C::FN], crole[C::FN];
+  float cbv[C::FN], cs[C::FN];
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
     const int col = acc_col<C>(fj);
-    const int v = n0 + col;
-    const bool cval = v < c1;
-    const int sel = s_sel[col];
-    const float bv = s_bias[col];
-    T* out = dZ + (v - c0);
-    float cs = 0.f;
-    if (sel < 0) {
+    csel[fj] = s_sel[col];
+    cbv[fj] = s_bias[col];
+    crole[fj] = n0 + col < c1 ? (csel[fj] < 0 ? 0 : 2) : 3;
+    cs[fj] = 0.f;
+  }
 #pragma unroll
-      for (int fi = 0; fi < C::FM; ++fi)
+  for (int fi = 0; fi < C::FM; ++fi) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(fi, r);
+    for (int q = 0; q < 4; ++q) {
+      const int row0 = acc_row<C>(fi, 4 * q);
+      const f32x4 rs4 = *reinterpret_cast<const f32x4*>(s_rs + row0);
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(s_lam2 + row0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int row = row0 + e;
+        const bool in = rows_full || m0 + row < M;
+#pragma unroll
+        for (int fj = 0; fj < C::FN; ++fj) {
           const float dz =
-              s_rs[row] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][r] + bv, LOG2E, -s_lam2[row]));
-          if (cval && m0 + row < M) {
-            out[(long long)(m0 + row) * ldz] = Elem<T>::from_f32(dz);
-            cs += dz;
-          }
-        }
-    } else {
-      const float* Sp = S + (long long)sel * M + m0;
-      const float* Gp = Gam + (long long)sel * M + m0;
-#pragma unroll
-      for (int fi = 0; fi < C::FM; ++fi) {
-        float sv[16], gv[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(fi, r);
-          const bool in = m0 + row < M;
-          sv[r] = in ? Sp[row] : 0.f;
-          gv[r] = in ? Gp[row] : 0.f;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(fi, r);
-          const float dz = (float)(grad * (s_g[row] * exp((double)sv[r]) - (double)gv[r]));
-          if (cval && m0 + row < M) {
-            out[(long long)(m0 + row) * ldz] = Elem<T>::from_f32(dz);
-            cs += dz;
+              rs4[e] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
+          if (in && crole[fj] == 0) {
+            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
+            cs[fj] += dz;
           }
         }
       }
     }
-    // column sum: the two lane halves hold the same column, then the waves
-    // stacked along M; both combined in a fixed order.
-    cs += __shfl_xor(cs, 32, 64);
-    if (lane < 32) s_db[wm][col] = cs;
+  }
+  // column sum: the two lane halves hold the same column, then the waves
+  // stacked along M; both combined in a fixed order.
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    cs[fj] += __shfl_xor(cs[fj], 32, 64);
+    if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
+  }
+  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g, so
+  // each selected column of this wavefront is done by all 64 lanes (WM / 64
+  // of the wavefront's rows each); the column sum is a fixed-order wave sum.
+  constexpr int RPL = C::WM / 64;
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    unsigned long long todo = __ballot(lane < 32 && crole[fj] == 2);
+    while (todo) {
+      const int src = __ffsll((long long)todo) - 1;
+      todo &= todo - 1;
+      const int sel = __shfl(csel[fj], src, 64);
+      const int col = (w % C::WGN) * C::WN + fj * 32 + src;
+      const float* Sp = S + (long long)sel * M + m0;
+      const float* Gp = Gam + (long long)sel * M + m0;
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < RPL; ++t) {
+        const int row = wm * C::WM + RPL * lane + t;
+        if (m0 + row < M) {
+          // S <= 0 (a log-probability)
+          const float dz =
+              (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
+          dZ[(long long)(m0 + row) * ldz + (n0 + col - c0)] = Elem<T>::from_f32(dz);
+          sum += dz;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) s_db[wm][col] = sum;
+    }
   }
   lds_barrier();
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
