@@ -409,25 +409,6 @@ __device__ __forceinline__ int acc_col(int fj) {
   return (w % C::WGN) * C::WN + fj * 32 + (lane & 31);
 }
 
-// Write the accumulator tile to LDS column-major: Zt[col * ld + row].
-template <class C>
-__device__ __forceinline__ void acc_to_lds(const f32x16 (&acc)[C::FM][C::FN],
-                                           float* __restrict__ Zt, int ld) {
-#pragma unroll
-  for (int fi = 0; fi < C::FM; ++fi)
-#pragma unroll
-    for (int fj = 0; fj < C::FN; ++fj) {
-      const int col = acc_col<C>(fj);
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int row = acc_row<C>(fi, rg * 4);
-        f32x4 v = {acc[fi][fj][rg * 4 + 0], acc[fi][fj][rg * 4 + 1], acc[fi][fj][rg * 4 + 2],
-                   acc[fi][fj][rg * 4 + 3]};
-        *reinterpret_cast<f32x4*>(Zt + col * ld + row) = v;
-      }
-    }
-}
-
 // (m1, s1) <- fold of two log-sum-exp partials (max, sum of exp(z - max)).
 __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double s2) {
   if (m2 == -INFINITY) return;
@@ -459,7 +440,7 @@ template <> struct Pick<float> {
   using dx = CfgF32Dx;
   using dw = CfgF32;
 };
-// bf16: the forward kernel's LDS epilogue tile limits it to 128 x 128; the
+// bf16 (heads the 256 x 256 core does not take): the
 // recompute product takes 128 x 256 tiles of four 64 x 128 wavefronts (fewer
 // LDS bytes per MFMA at the bf16 rate); dX, whose epilogue is a fp32
 // accumulator update, runs eight 32 x 64 wavefronts.
@@ -470,124 +451,111 @@ template <> struct Pick<bf16_t> {
   using dw = CfgB16;
 };
 
-template <class C>
-struct EpiSmem {
-  static constexpr int TL = C::BM + 4;  // accumulator tile in LDS, [col][row]
-  static constexpr int BYTES = cmax(C::STAGE_BYTES, C::BN * TL * 4);
-};
-
 // ------------------------------------------------------------- forward
-// One work-group: BM frames x one LSE_SPAN-wide vocabulary span, walked in
-// BN-column tiles.  Per tile: MFMA logits, + bias, then per row the FP64 sum
-// of exp(z - row max over the tile) folded into the row's running partial,
-// and a gather of the selected columns into Zsel (class-major, K x M).
-// Epilogue mapping: each thread owns 4 consecutive rows (one 16-byte LDS
-// read per column) and a group of CPT columns; the RG = THREADS / (BM / 4)
-// column groups of a row are folded in order at the end of the span.
+// The forward tile is computed transposed: BM vocabulary rows (operand A =
+// W) by BN frames (operand B = X), so each lane holds FM x 16 vocabulary
+// values of each of its FN frames and the per-frame log-sum-exp of a tile
+// needs no cross-lane step.  One work-group: BN frames x one LSE_SPAN-wide
+// vocabulary span, walked in BM-row tiles, the next tile's first k stage
+// loaded before the current tile's epilogue.  Per tile and frame each lane
+// folds the max and the FP64 sum of exp(z - max) over its values into a
+// running partial; at the end of the span the two lane halves and the WGM
+// wave rows are folded in a fixed order.  Selected vocabulary rows are
+// gathered into Zsel (class-major, K x M), 32 frames per coalesced store.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
     const typename C::type* __restrict__ bias, int M, int D, int V,
     const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
-    int nspan, int mtiles, int vec_ok) {
+    int nspan, int ftiles, int vec_ok) {
   using T = typename C::type;
-  constexpr int BM = C::BM, BN = C::BN, TL = EpiSmem<C>::TL;
-  constexpr int RQ = BM / 4;              // row quads
-  constexpr int RG = C::THREADS / RQ;     // column groups per row quad
-  constexpr int CPT = BN / RG;            // columns per thread
-  static_assert(C::THREADS % RQ == 0 && BN % RG == 0 && BN <= C::THREADS, "epilogue split");
-  static_assert(RG * BM * (4 + 8) <= EpiSmem<C>::BYTES, "fold scratch");
-  __shared__ __attribute__((aligned(16))) char smem[EpiSmem<C>::BYTES];
-  __shared__ int s_sel[BN];
-  __shared__ float s_bias[BN];
-  int mt, sp;
-  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, nspan, mt, sp);
-  const int m0 = mt * BM;
+  __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) int s_sel[2][C::BM];
+  __shared__ __attribute__((aligned(16))) float s_bias[2][C::BM];
+  __shared__ float f_m[C::WGM][C::BN];
+  __shared__ double f_s[C::WGM][C::BN];
+  int ft, sp;
+  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
+  const int f0 = ft * C::BN;
   const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
-  const int rq = threadIdx.x % RQ, cg = threadIdx.x / RQ;
-  const int r0 = 4 * rq;
-  float run_m[4];
-  double run_s[4];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  float run_m[C::FN];
+  double run_s[C::FN];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    run_m[j] = -INFINITY;
-    run_s[j] = 0.0;
+  for (int fj = 0; fj < C::FN; ++fj) {
+    run_m[fj] = -INFINITY;
+    run_s[fj] = 0.0;
   }
-  float* Zt = reinterpret_cast<float*>(smem);
-  // Tiles are walked with the next tile's first k stage and column data
-  // loaded before the current tile's epilogue.
   Prefetch<C, true, true> pf;
-  gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, c_begin, c_end, 0, D, vec_ok, vec_ok);
-  int nsel = -1;
-  float nbias = 0.f;
-  if (threadIdx.x < BN) {
-    const int v = c_begin + threadIdx.x;
-    nsel = v < c_end ? col2sel[v] : -1;
-    nbias = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
-  }
-  for (int n0 = c_begin; n0 < c_end; n0 += BN) {
+  gemm_prefetch<C, true, true>(pf, W, D, c_begin, c_end, X, D, f0, M, 0, D, vec_ok, vec_ok);
+  int par = 0;
+  for (int v0 = c_begin; v0 < c_end; v0 += C::BM, par ^= 1) {
+    // this tile's row data: visible after the GEMM's barriers; the buffer
+    // written here was last read two tiles ago
+    for (int r = threadIdx.x; r < C::BM; r += C::THREADS) {
+      const int v = v0 + r;
+      s_sel[par][r] = v < c_end ? col2sel[v] : -2;  // -2: past the span
+      s_bias[par][r] = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
+    }
     f32x16 acc[C::FM][C::FN];
-    gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c_end, 0, D, vec_ok, vec_ok, acc,
+    gemm_tile_run<C, true, true>(pf, W, D, v0, c_end, X, D, f0, M, 0, D, vec_ok, vec_ok, acc,
                                  smem);
-    const int cur_sel = nsel;
-    const float cur_bias = nbias;
-    if (n0 + BN < c_end) {
-      gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, n0 + BN, c_end, 0, D, vec_ok, vec_ok);
-      if (threadIdx.x < BN) {
-        const int v = n0 + BN + threadIdx.x;
-        nsel = v < c_end ? col2sel[v] : -1;
-        nbias = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
-      }
-    }
-    acc_to_lds<C>(acc, Zt, TL);
-    if (threadIdx.x < BN) {
-      s_sel[threadIdx.x] = cur_sel;
-      s_bias[threadIdx.x] = cur_bias;
-    }
-    lds_barrier();
-    const int ncol = min(BN, c_end - n0);
-    const int cb = cg * CPT, ce = min(cb + CPT, ncol);
-    if (ce > cb) {
-      float mx[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      for (int c = cb; c < ce; ++c) {
-        const f32x4 z = *reinterpret_cast<const f32x4*>(Zt + c * TL + r0);
-        const float bv = s_bias[c];
+    if (v0 + C::BM < c_end)
+      gemm_prefetch<C, true, true>(pf, W, D, v0 + C::BM, c_end, X, D, f0, M, 0, D, vec_ok,
+                                   vec_ok);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) mx[j] = fmaxf(mx[j], z[j] + bv);
-      }
-      double sum[4] = {0.0, 0.0, 0.0, 0.0};
-      for (int c = cb; c < ce; ++c) {
-        const f32x4 z4 = *reinterpret_cast<const f32x4*>(Zt + c * TL + r0);
-        const float bv = s_bias[c];
-        const int sel = s_sel[c];
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int frame = f0 + acc_col<C>(fj);
+      float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float z = z4[j] + bv;
-          sum[j] += exp_nonpos((double)z - (double)mx[j]);
-          if (sel >= 0 && m0 + r0 + j < M) Zsel[(long long)sel * M + m0 + r0 + j] = z;
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = acc_row<C>(fi, 4 * q);
+          const int4 sel4 = *reinterpret_cast<const int4*>(&s_sel[par][r0]);
+          const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_bias[par][r0]);
+          const int sl[4] = {sel4.x, sel4.y, sel4.z, sel4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float z = acc[fi][fj][4 * q + e] + b4[e];
+            acc[fi][fj][4 * q + e] = sl[e] >= -1 ? z : -INFINITY;
+            mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
+            if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
+          }
         }
+      double sum = 0.0;
+      if (mx != -INFINITY) {
+#pragma unroll
+        for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            sum += exp_nonpos((double)acc[fi][fj][r] - (double)mx);
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) lse_fold(run_m[j], run_s[j], mx[j], sum[j]);
+      lse_fold(run_m[fj], run_s[fj], mx, sum);
     }
-    lds_barrier();
   }
-  // fold the RG column groups of every row, in group order
-  float* f_m = reinterpret_cast<float*>(smem);
-  double* f_s = reinterpret_cast<double*>(smem + RG * BM * 4);
+  // lane halves (lower half first), then wave rows in order
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    f_m[cg * BM + r0 + j] = run_m[j];
-    f_s[cg * BM + r0 + j] = run_s[j];
+  for (int fj = 0; fj < C::FN; ++fj) {
+    const float om = __shfl_xor(run_m[fj], 32, 64);
+    const double os = __shfl_xor(run_s[fj], 32, 64);
+    float m1 = lane < 32 ? run_m[fj] : om;
+    double s1 = lane < 32 ? run_s[fj] : os;
+    lse_fold(m1, s1, lane < 32 ? om : run_m[fj], lane < 32 ? os : run_s[fj]);
+    if (lane < 32) {
+      f_m[wm][acc_col<C>(fj)] = m1;
+      f_s[wm][acc_col<C>(fj)] = s1;
+    }
   }
   lds_barrier();
-  for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
-    const int m = m0 + rr;
-    if (m >= M) continue;
-    float fm = f_m[rr];
-    double fs = f_s[rr];
-    for (int q = 1; q < RG; ++q) lse_fold(fm, fs, f_m[q * BM + rr], f_s[q * BM + rr]);
-    part[(long long)m * nspan + sp] = make_double2((double)fm, fs);
+  for (int c = threadIdx.x; c < C::BN; c += C::THREADS) {
+    const int frame = f0 + c;
+    if (frame >= M) continue;
+    float fm = f_m[0][c];
+    double fs = f_s[0][c];
+#pragma unroll
+    for (int q = 1; q < C::WGM; ++q) lse_fold(fm, fs, f_m[q][c], f_s[q][c]);
+    part[(long long)frame * nspan + sp] = make_double2((double)fm, fs);
   }
 }
 
@@ -1313,12 +1281,12 @@ template <typename T>
 hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                      int V, const int* col2sel, float* Zsel, double2* part, int nspan) {
   using C = typename Pick<T>::fwd;
-  const int mtiles = ceil_div(M, C::BM);
-  const int grid = mtiles * nspan;
+  const int ftiles = ceil_div(M, C::BN);
+  const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
   k_fwd_lse<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, V,
-                                             col2sel, Zsel, part, nspan, mtiles, vec);
+                                             col2sel, Zsel, part, nspan, ftiles, vec);
   return hipGetLastError();
 }
 
