@@ -44,12 +44,12 @@ struct DevBuf {
 
 // Kernel families timed by the optional event profiler.
 enum Kid {
-  K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA, K_LOSS, K_BETA, K_FILL, K_OCC,
+  K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
   K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
-    "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha", "loss_sum",
-    "ctc_beta", "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
+    "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
+    "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
     "dw_reduce", "db_reduce", "cast"};
 
 struct Pending {
@@ -293,6 +293,7 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(lamf, (size_t)M * sizeof(float));
   ENSURE(S, (size_t)K * M * sizeof(float));
   ENSURE(alpha, (size_t)hm.dp_total * sizeof(double));
+  ENSURE(beta, (size_t)hm.dp_total * sizeof(double));
   ENSURE(utt_loss, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_logp, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
@@ -305,12 +306,15 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                                    (double*)ctx->lam.p, (float*)ctx->lamf.p));
     LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
   }
-  LAUNCH(K_ALPHA, launch_alpha(st, (const float*)ctx->S.p, iM, N, hm.max_L,
-                               (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
-                               (const int*)ctx->tgt_rel.p,
-                               (const uint8_t*)ctx->flags.p, (const long long*)ctx->dp_off.p,
-                               (double*)ctx->alpha.p, (double*)ctx->utt_loss.p,
-                               (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p));
+  // The backward recursion runs here too, beside the forward one (it only
+  // reads S): on the otherwise idle compute units it costs no extra time.
+  LAUNCH(K_ALPHA_BETA,
+         launch_alpha_beta(st, (const float*)ctx->S.p, iM, N, hm.max_L,
+                           (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                           (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
+                           (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
+                           (double*)ctx->beta.p, (double*)ctx->utt_loss.p,
+                           (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p));
   LAUNCH(K_LOSS, launch_loss_sum(st, N, (const double*)ctx->utt_loss.p,
                                  (const int*)ctx->utt_status.p, dmeta));
   PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
@@ -364,11 +368,8 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   const long long* dpo = (const long long*)ctx->dp_off.p;
   const float* S = (const float*)ctx->S.p;
 
-  ENSURE(beta, (size_t)ctx->dp_total * sizeof(double));
   ENSURE(Gam, (size_t)K * M * sizeof(float));
   ENSURE(g, (size_t)M * sizeof(double));
-  LAUNCH(K_BETA, launch_beta(st, S, M, N, ctx->max_L, row_off, toff, trel, ustat, dpo,
-                             (double*)ctx->beta.p));
   LAUNCH(K_FILL, launch_fill_f32(st, (float*)ctx->Gam.p, (long long)K * M, 0.f));
   LAUNCH(K_OCC, launch_occupancy(st, S, M, N, ctx->max_T, ctx->max_L, row_off, toff, trel, ustat,
                                  (const double*)ctx->utt_logp.p, dpo,

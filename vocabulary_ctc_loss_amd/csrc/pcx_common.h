@@ -143,15 +143,13 @@ hipError_t launch_cast_out(hipStream_t st, int dtype, const float* src, void* ds
                            long long n);
 
 // Alignment DP (pcx_ctc.hip).
-hipError_t launch_alpha(hipStream_t st, const float* S, int M, int N, int max_L,
-                        const int* row_off, const int* tgt_off, const int* tgt_rel,
-                        const uint8_t* flags, const long long* dp_off, double* alpha,
-                        double* utt_loss, double* utt_logp, int* utt_status);
+// Forward and backward recursions of every utterance in one launch.
+hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
+                             const int* row_off, const int* tgt_off, const int* tgt_rel,
+                             const uint8_t* flags, const long long* dp_off, double* alpha,
+                             double* beta, double* utt_loss, double* utt_logp, int* utt_status);
 hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss,
                            const int* utt_status, Meta* meta);
-hipError_t launch_beta(hipStream_t st, const float* S, int M, int N, int max_L,
-                       const int* row_off, const int* tgt_off, const int* tgt_rel,
-                       const int* utt_status, const long long* dp_off, double* beta);
 hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int max_T,
                             int max_L, const int* row_off, const int* tgt_off,
                             const int* tgt_rel, const int* utt_status,

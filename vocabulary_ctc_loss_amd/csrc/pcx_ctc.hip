@@ -98,17 +98,15 @@ __device__ __forceinline__ double lse2(double a, double b) {
   return m + log_1to4(1.0 + exp_nonpos_lat(x - m));
 }
 
-// Forward recursion; alpha[t][s] (including the emission at t) is stored
-// for the backward pass.
+// Forward recursion of utterance n; alpha[t][s] (including the emission at
+// t) is stored for the backward pass.
 template <int SPT>
-__global__ __launch_bounds__(1024) void k_alpha(
-    const float* __restrict__ S, int M, const int* __restrict__ row_off,
+__device__ __forceinline__ void alpha_utt(
+    int n, double* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     double* __restrict__ alpha, double* __restrict__ utt_loss, double* __restrict__ utt_logp,
     int* __restrict__ utt_status) {
-  extern __shared__ double sh[];
-  const int n = blockIdx.x;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   if (!flags[n]) {
@@ -205,16 +203,16 @@ __global__ __launch_bounds__(1024) void k_alpha(
   }
 }
 
-// Backward recursion; beta[t][s] includes the emission at t.
+// Backward recursion of utterance n; beta[t][s] includes the emission at
+// t.  Run for every structurally alignable utterance (an utterance whose
+// loss turns out nonfinite gets no gradient: the occupancy pass skips it).
 template <int SPT>
-__global__ __launch_bounds__(1024) void k_beta(
-    const float* __restrict__ S, int M, const int* __restrict__ row_off,
+__device__ __forceinline__ void beta_utt(
+    int n, double* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
-    const int* __restrict__ utt_status, const long long* __restrict__ dp_off,
+    const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     double* __restrict__ beta) {
-  extern __shared__ double sh[];
-  const int n = blockIdx.x;
-  if (utt_status[n] != UTT_OK) return;
+  if (!flags[n]) return;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   const int cap = SPT * blockDim.x;
@@ -294,6 +292,26 @@ __global__ __launch_bounds__(1024) void k_beta(
 #pragma unroll
       for (int u = 0; u < PF; ++u) ecur[j][u] = enxt[j][u];
   }
+}
+
+// Both recursions in one launch: work-groups 0..N-1 run the forward
+// recursion of utterance n, work-groups N..2N-1 the backward recursion of
+// utterance n - N.  The two only read S, so they run side by side (the loss
+// pass needs the forward ones only; the backward pass reads both).
+template <int SPT>
+__global__ __launch_bounds__(1024) void k_alpha_beta(
+    const float* __restrict__ S, int M, int N, const int* __restrict__ row_off,
+    const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
+    const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
+    double* __restrict__ alpha, double* __restrict__ beta, double* __restrict__ utt_loss,
+    double* __restrict__ utt_logp, int* __restrict__ utt_status) {
+  extern __shared__ double sh[];
+  const int b = blockIdx.x;
+  if (b < N)
+    alpha_utt<SPT>(b, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, alpha, utt_loss,
+                   utt_logp, utt_status);
+  else
+    beta_utt<SPT>(b - N, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, beta);
 }
 
 // Occupancies on the selected classes for OCC_FRAMES frames of one
@@ -425,26 +443,29 @@ void dp_shape(int max_L, int& threads, int& spt) {
 
 }  // namespace
 
-hipError_t launch_alpha(hipStream_t st, const float* S, int M, int N, int max_L,
-                        const int* row_off, const int* tgt_off, const int* tgt_rel,
-                        const uint8_t* flags, const long long* dp_off, double* alpha,
-                        double* utt_loss, double* utt_logp, int* utt_status) {
+hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
+                             const int* row_off, const int* tgt_off, const int* tgt_rel,
+                             const uint8_t* flags, const long long* dp_off, double* alpha,
+                             double* beta, double* utt_loss, double* utt_logp, int* utt_status) {
   if (N == 0) return hipSuccess;
   int threads, spt;
   dp_shape(max_L, threads, spt);
   const size_t shm = 2 * (size_t)spt * threads * sizeof(double);
   switch (spt) {
     case 1:
-      k_alpha<1><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, flags, dp_off, alpha,
-                                          utt_loss, utt_logp, utt_status);
+      k_alpha_beta<1><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
+                                                   dp_off, alpha, beta, utt_loss, utt_logp,
+                                                   utt_status);
       break;
     case 2:
-      k_alpha<2><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, flags, dp_off, alpha,
-                                          utt_loss, utt_logp, utt_status);
+      k_alpha_beta<2><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
+                                                   dp_off, alpha, beta, utt_loss, utt_logp,
+                                                   utt_status);
       break;
     case 4:
-      k_alpha<4><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, flags, dp_off, alpha,
-                                          utt_loss, utt_logp, utt_status);
+      k_alpha_beta<4><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
+                                                   dp_off, alpha, beta, utt_loss, utt_logp,
+                                                   utt_status);
       break;
     default:
       return hipErrorInvalidValue;
@@ -455,32 +476,6 @@ hipError_t launch_alpha(hipStream_t st, const float* S, int M, int N, int max_L,
 hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss, const int* utt_status,
                            Meta* meta) {
   k_loss_sum<<<1, 64, 0, st>>>(N, utt_loss, utt_status, meta);
-  return hipGetLastError();
-}
-
-hipError_t launch_beta(hipStream_t st, const float* S, int M, int N, int max_L,
-                       const int* row_off, const int* tgt_off, const int* tgt_rel,
-                       const int* utt_status, const long long* dp_off, double* beta) {
-  if (N == 0) return hipSuccess;
-  int threads, spt;
-  dp_shape(max_L, threads, spt);
-  const size_t shm = 2 * (size_t)spt * threads * sizeof(double);
-  switch (spt) {
-    case 1:
-      k_beta<1><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status, dp_off,
-                                         beta);
-      break;
-    case 2:
-      k_beta<2><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status, dp_off,
-                                         beta);
-      break;
-    case 4:
-      k_beta<4><<<N, threads, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status, dp_off,
-                                         beta);
-      break;
-    default:
-      return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }
 

@@ -586,6 +586,11 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 }
 
 // ------------------------------------------------------------- backward
+// Above this many selected columns in one wavefront's tile (of 32 FN), the
+// recompute epilogue lets every lane handle its own selected columns instead
+// of sharing each selected column among all 64 lanes.
+constexpr int SEL_DENSE = 8;
+
 // Recompute one BM x BN tile of chunk logits and form the logit gradient
 //   v not selected:  dZ = (grad g_m) * exp(z - fp32(lambda_m)), evaluated in
 //                    fp32 as exp2(z log2e - fp32(lambda_m log2e)) with one
@@ -669,6 +674,35 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
       }
     }
   }
+  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g.
+  // With few of them in this wavefront (the large-vocabulary case) each is
+  // done by all 64 lanes in the pass further down; with many, every lane
+  // does its own here.
+  int nsel = 0;
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) nsel += __popcll(__ballot(lane < 32 && crole[fj] == 2));
+  const bool dense = nsel > SEL_DENSE;
+  if (dense) {
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      if (crole[fj] != 2) continue;
+      const float* Sp = S + (long long)csel[fj] * M + m0;
+      const float* Gp = Gam + (long long)csel[fj] * M + m0;
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<C>(fi, r);
+          if (rows_full || m0 + row < M) {
+            // S <= 0 (a log-probability)
+            const float dz =
+                (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
+            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
+            cs[fj] += dz;
+          }
+        }
+    }
+  }
   // column sum: the two lane halves hold the same column, then the waves
   // stacked along M; both combined in a fixed order.
 #pragma unroll
@@ -676,13 +710,13 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     cs[fj] += __shfl_xor(cs[fj], 32, 64);
     if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
   }
-  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g, so
-  // each selected column of this wavefront is done by all 64 lanes (WM / 64
-  // of the wavefront's rows each); the column sum is a fixed-order wave sum.
+  // Few selected classes: each selected column of this wavefront by all 64
+  // lanes (WM / 64 of the wavefront's rows each); the column sum is a
+  // fixed-order wave sum.
   constexpr int RPL = C::WM / 64;
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
-    unsigned long long todo = __ballot(lane < 32 && crole[fj] == 2);
+    unsigned long long todo = dense ? 0ull : __ballot(lane < 32 && crole[fj] == 2);
     while (todo) {
       const int src = __ffsll((long long)todo) - 1;
       todo &= todo - 1;
@@ -845,54 +879,64 @@ __global__ void k_cast_bf16(const float* __restrict__ src, bf16_t* __restrict__ 
 // ------------------------------------------------ bf16 core for 256 x 256 tiles
 // A second GEMM core for bf16 heads whose reduction length is a multiple of
 // 64 (the LLM head): a 256 x 256 work-group tile of eight wavefronts, WGM x
-// WGN of them, both operands K-contiguous.  Each k stage holds 64 values (128
-// bytes) of all 256 rows of both operands, double buffered in LDS (128 KiB),
-// and is filled by 16-byte global->LDS loads that need no staging registers:
-// one wave-wide load writes 1 KiB of LDS, lane l at byte 16 l.  The loads of
-// stage s + 1 are issued at the start of stage s; a work-group barrier (after
-// each wave's own loads have landed) separates the stages.
+// WGN of them, both operands K-contiguous.  Each k stage holds BK values of
+// all 256 rows of both operands; NBUF stages live in LDS (at most 128 KiB)
+// and are filled NBUF - 1 stages ahead by 16-byte global->LDS loads that need
+// no staging registers: one wave-wide load writes 1 KiB of LDS, lane l at
+// byte 16 l.  A work-group barrier (after each wave's loads of the next
+// stage have landed) separates the stages.
 //
-// LDS layout: row r at byte 128 r, its 16-byte chunk c (k values 8c..8c+7) at
-// chunk position c ^ ((r / 2) % 8).  A 16-byte fragment read is served for
-// 16 lanes at a time over 64 four-byte banks; the 16 rows one such group
-// reads sit two per 256-byte bank window, and the permutation gives the rows
-// sharing a window slot distinct chunk positions, so each group touches
-// every bank once.  The loads write whole 1 KiB blocks, so they place row r's
-// chunk c by choosing which global chunk each lane fetches.
+// LDS layout: row r at byte ROWB r (ROWB = 2 BK), its 16-byte chunk c (k
+// values 8c..8c+7) at chunk position c ^ ((r / (256 / ROWB)) % (ROWB / 16)).
+// A 16-byte fragment read is served for 16 lanes at a time over 64 four-byte
+// banks; the 16 rows one such group reads share each 256-byte bank window
+// 256 / ROWB at a time, and the permutation gives the rows sharing a window
+// slot distinct chunk positions, so each group touches every bank once.  The
+// loads write whole 1 KiB blocks, so they place row r's chunk c by choosing
+// which global chunk each lane fetches.
 //
-// Within a stage, lane half h feeds the MFMA k values 32h..32h+31, eight per
-// v_mfma_f32_32x32x16_bf16 (the same relabelling of k for both operands).
-template <int WGM_, int WGN_>
+// Within a stage, lane half h feeds the MFMA k values h BK/2 .. (h+1) BK/2 - 1,
+// eight per v_mfma_f32_32x32x16_bf16 (the same relabelling of k for both
+// operands).
+template <int WGM_, int WGN_, int BK_, int NBUF_>
 struct CfgBig {
   using type = bf16_t;
   static constexpr int BM = 256, BN = 256;
   static constexpr int WGM = WGM_, WGN = WGN_, WAVES = WGM * WGN, THREADS = 64 * WAVES;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
-  static constexpr int BK = 64, ROWB = 128, CH = 8, KS = BK / 16;
+  static constexpr int BK = BK_, ROWB = 2 * BK, CH = ROWB / 16, KS = BK / 16;
+  static constexpr int RPI = 1024 / ROWB;             // rows per 1 KiB load
+  static constexpr int RPW = 256 / ROWB;              // rows per 256-byte bank window
+  static constexpr int NBUF = NBUF_, DEPTH = NBUF - 1;
   static constexpr int TILEB = 256 * ROWB;            // one operand stage
   static constexpr int STAGEB = 2 * TILEB;            // both operands
-  static constexpr int LDS_BYTES = 2 * STAGEB;        // double buffered
+  static constexpr int LDS_BYTES = NBUF * STAGEB;
   static constexpr int NLD = TILEB / 1024 / WAVES;    // 1 KiB loads per wave and operand
+  static constexpr int INFLIGHT = (DEPTH - 1) * 2 * NLD;  // loads allowed past a barrier
   static constexpr int MINWG = 1;
   static_assert(TILEB % (1024 * WAVES) == 0 && WM % 32 == 0 && WN % 32 == 0, "big tile");
+  static_assert((BK == 32 || BK == 64) && NBUF >= 2 && LDS_BYTES <= 128 * 1024, "big stages");
 };
-using CfgBigB16 = CfgBig<2, 4>;
+using CfgBigFwd = CfgBig<2, 4, 64, 2>;
+using CfgBigRec = CfgBig<2, 4, 64, 2>;
+using CfgBigDx = CfgBig<2, 4, 64, 2>;
 
 #define PCX_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-__device__ __forceinline__ int big_swz(int r) { return (r >> 1) & 7; }
+template <class C>
+__device__ __forceinline__ int big_swz(int r) { return (r / C::RPW) % C::CH; }
 
 // Global->LDS loads of one operand stage: rows r0.. (clamped to rlim - 1;
-// those rows only feed accumulator rows the callers discard), k0..k0+63.
+// those rows only feed accumulator rows the callers discard), k0..k0+BK-1.
 template <class C>
 __device__ __forceinline__ void big_stage(const bf16_t* __restrict__ G, long long ld, int r0,
                                           int rlim, int k0, char* dst) {
   const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
 #pragma unroll
   for (int q = 0; q < C::NLD; ++q) {
-    const int u = w * C::NLD + q;  // 1 KiB block: rows 8u..8u+7
-    const int row = u * 8 + (l >> 3);
-    const int c = (l & 7) ^ big_swz(row);
+    const int u = w * C::NLD + q;  // 1 KiB block: rows RPI u .. RPI u + RPI - 1
+    const int row = u * C::RPI + l / C::CH;
+    const int c = (l % C::CH) ^ big_swz<C>(row);
     const int gr = min(r0 + row, rlim - 1);
     __builtin_amdgcn_global_load_lds((const void*)(G + (long long)gr * ld + k0 + c * 8),
                                      PCX_LDS_PTR(dst + u * 1024), 16, 0, 0);
@@ -900,12 +944,13 @@ __device__ __forceinline__ void big_stage(const bf16_t* __restrict__ G, long lon
 }
 
 // Barrier of the big core: this wave's LDS reads are complete and at most N
-// of its global->LDS loads are in flight, then all waves meet.  (A release
-// fence would also wait for every outstanding global->LDS load.)
+// of its global memory operations are in flight, then all waves meet.  (A
+// release fence would also wait for every outstanding global->LDS load.)
 template <int N>
 __device__ __forceinline__ void big_barrier() {
-  static_assert(N >= 0 && N < 16, "vmcnt");
-  __builtin_amdgcn_s_waitcnt(N | (7 << 4));  // vmcnt(N) expcnt(7) lgkmcnt(0)
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  // vmcnt(N) (bits 3:0 and 15:14), expcnt(7), lgkmcnt(0)
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
   asm volatile("s_barrier" ::: "memory");
 }
 
@@ -918,51 +963,83 @@ __device__ __forceinline__ void big_frags(const char* buf, int j, int wm, int wn
   for (int f = 0; f < C::FM; ++f) {
     const int r = wm * C::WM + f * 32 + i;
     a[f] = __builtin_bit_cast(
-        bf16x8, *reinterpret_cast<const uint4*>(buf + r * C::ROWB + ((c ^ big_swz(r)) << 4)));
+        bf16x8, *reinterpret_cast<const uint4*>(buf + r * C::ROWB + ((c ^ big_swz<C>(r)) << 4)));
   }
 #pragma unroll
   for (int f = 0; f < C::FN; ++f) {
     const int r = wn * C::WN + f * 32 + i;
     b[f] = __builtin_bit_cast(
         bf16x8, *reinterpret_cast<const uint4*>(buf + C::TILEB + r * C::ROWB +
-                                                ((c ^ big_swz(r)) << 4)));
+                                                ((c ^ big_swz<C>(r)) << 4)));
   }
 }
 
-// acc = A[m0:m0+256, k] . B[n0:n0+256, k]^T over k in [0, K); K % 64 == 0,
+// Pipeline state carried from one tile to the next by a work-group that
+// walks several tiles: the LDS buffer that holds (or will hold) the tile's
+// first k stage, and whether the loads of its first NBUF - 1 stages were
+// already issued by the previous tile (cross-tile prefetch).
+struct BigPipe {
+  int buf0 = 0;
+  bool staged = false;
+};
+
+// Operand rows of the next tile (its first stages are loaded during this
+// tile's last stages).
+struct BigNext {
+  bool valid;
+  int m0, m_lim, n0, n_lim;
+};
+
+// acc = A[m0:m0+256, k] . B[n0:n0+256, k]^T over k in [0, K); K % BK == 0,
 // K > 0, lda and ldb multiples of 8, A and B 16-byte aligned, m_lim and
-// n_lim >= 1.  Ends with a barrier (smem may be reused right away).
+// n_lim >= 1.  With next.valid, the next tile's first stages (same A, B, lda,
+// ldb, K) are loaded during this tile's last stages and `pipe` is updated for
+// the next call; without, the call ends with no load in flight.  Every call
+// starts with a barrier, so between two calls the waves may only touch LDS
+// outside the operand buffers.
 template <class C>
 __device__ __forceinline__ void gemm_big(const bf16_t* __restrict__ A, long long lda, int m0,
                                          int m_lim, const bf16_t* __restrict__ B, long long ldb,
                                          int n0, int n_lim, int K, f32x16 (&acc)[C::FM][C::FN],
-                                         char* smem) {
+                                         char* smem, BigPipe& pipe, const BigNext& next) {
   const int w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
   const int nk = K / C::BK;
+  const int b0 = pipe.buf0;
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[fi][fj][r] = 0.f;
-  big_stage<C>(A, lda, m0, m_lim, 0, smem);
-  big_stage<C>(B, ldb, n0, n_lim, 0, smem + C::TILEB);
-  big_barrier<0>();
+  // Loads of pipeline stage g: this tile's stage g, past the end the next
+  // tile's stage g - nk (clamped to its last stage), or (no next tile) a
+  // harmless reload of the last stage into a buffer no longer read.
+  auto issue = [&](int g) {
+    const bool own = g < nk, nx = !own && next.valid;
+    const int ra = nx ? next.m0 : m0, ra_lim = nx ? next.m_lim : m_lim;
+    const int rb = nx ? next.n0 : n0, rb_lim = nx ? next.n_lim : n_lim;
+    const int k = (own ? g : nx ? min(g - nk, nk - 1) : nk - 1) * C::BK;
+    char* dst = smem + ((b0 + g) % C::NBUF) * C::STAGEB;
+    big_stage<C>(A, lda, ra, ra_lim, k, dst);
+    big_stage<C>(B, ldb, rb, rb_lim, k, dst + C::TILEB);
+  };
+  if (!pipe.staged) {
+#pragma unroll
+    for (int g = 0; g < C::DEPTH; ++g) issue(g);
+  }
+  big_barrier<C::INFLIGHT>();
   bf16x8 fa[2][C::FM], fb[2][C::FN];
-  big_frags<C>(smem, 0, wm, wn, fa[0], fb[0]);
+  big_frags<C>(smem + b0 * C::STAGEB, 0, wm, wn, fa[0], fb[0]);
   for (int s = 0; s < nk; ++s) {
-    const char* cur = smem + (s & 1) * C::STAGEB;
-    char* nxt = smem + ((s + 1) & 1) * C::STAGEB;
-    // the last stage reloads itself into the idle buffer (no branch)
-    const int kn = min(s + 1, nk - 1) * C::BK;
-    big_stage<C>(A, lda, m0, m_lim, kn, nxt);
-    big_stage<C>(B, ldb, n0, n_lim, kn, nxt + C::TILEB);
+    const char* cur = smem + ((b0 + s) % C::NBUF) * C::STAGEB;
+    const char* nxt = smem + ((b0 + s + 1) % C::NBUF) * C::STAGEB;
+    issue(s + C::DEPTH);
 #pragma unroll
     for (int j = 0; j < C::KS; ++j) {
       if (j + 1 < C::KS) {
         big_frags<C>(cur, j + 1, wm, wn, fa[(j + 1) & 1], fb[(j + 1) & 1]);
       } else {
-        big_barrier<0>();
+        big_barrier<C::INFLIGHT>();
         big_frags<C>(nxt, 0, wm, wn, fa[(j + 1) & 1], fb[(j + 1) & 1]);
       }
 #pragma unroll
@@ -981,7 +1058,20 @@ __device__ __forceinline__ void gemm_big(const bf16_t* __restrict__ A, long long
       __builtin_amdgcn_sched_group_barrier(0x008, C::FM * C::FN - C::FM - C::FN, 0);
     }
   }
-  big_barrier<0>();
+  pipe.buf0 = (b0 + nk) % C::NBUF;
+  pipe.staged = next.valid;
+  if (!next.valid) big_barrier<0>();
+}
+
+// One tile, nothing carried over.
+template <class C>
+__device__ __forceinline__ void gemm_big1(const bf16_t* __restrict__ A, long long lda, int m0,
+                                          int m_lim, const bf16_t* __restrict__ B, long long ldb,
+                                          int n0, int n_lim, int K, f32x16 (&acc)[C::FM][C::FN],
+                                          char* smem) {
+  BigPipe pipe;
+  const BigNext none{false, 0, 1, 0, 1};
+  gemm_big<C>(A, lda, m0, m_lim, B, ldb, n0, n_lim, K, acc, smem, pipe, none);
 }
 
 // Forward on the big core, computed transposed: the tile is 256 vocabulary
@@ -1020,17 +1110,31 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     run_m[fj] = -INFINITY;
     run_s[fj] = 0.0;
   }
+  // the first tile's row data; later tiles' are loaded during the tile before
+  int nsel = -2;
+  float nbias = 0.f;
+  if (threadIdx.x < C::BM) {
+    const int v = c_begin + threadIdx.x;
+    nsel = v < c_end ? col2sel[v] : -2;  // -2: past the span
+    nbias = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+  }
+  BigPipe pipe;
   int par = 0;
   for (int v0 = c_begin; v0 < c_end; v0 += C::BM, par ^= 1) {
-    // this tile's row data; visible after the core's barriers, and the
-    // buffer written here was last read two tiles ago
-    for (int r = threadIdx.x; r < C::BM; r += C::THREADS) {
-      const int v = v0 + r;
-      s_sel[par][r] = v < c_end ? col2sel[v] : -2;  // -2: past the span
-      s_bias[par][r] = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+    // visible after the core's barriers; the buffer written here was last
+    // read two tiles ago
+    if (threadIdx.x < C::BM) {
+      s_sel[par][threadIdx.x] = nsel;
+      s_bias[par][threadIdx.x] = nbias;
     }
+    const BigNext next{v0 + C::BM < c_end, v0 + C::BM, c_end, f0, M};
     f32x16 acc[C::FM][C::FN];
-    gemm_big<C>(W, D, v0, c_end, X, D, f0, M, D, acc, smem);
+    gemm_big<C>(W, D, v0, c_end, X, D, f0, M, D, acc, smem, pipe, next);
+    if (next.valid && threadIdx.x < C::BM) {
+      const int v = v0 + C::BM + threadIdx.x;
+      nsel = v < c_end ? col2sel[v] : -2;
+      nbias = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+    }
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
       const int frame = f0 + acc_col<C>(fj);
@@ -1130,7 +1234,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     s_lam2[rr] = mm < M ? lamf[mm] * LOG2E : 0.f;
   }
   f32x16 acc[C::FM][C::FN];
-  gemm_big<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
+  gemm_big1<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   const bool rows_full = m0 + BM <= M;
   // Column roles: 0 = unselected class (formula below), 1 = padding up to
@@ -1173,17 +1277,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g.
+  // With few of them in this wavefront (the large-vocabulary case) each is
+  // done by all 64 lanes in the pass further down; with many, every lane
+  // does its own here.
+  int nsel = 0;
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj)
+    nsel += __popcll(__ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0));
+  const bool dense = nsel > SEL_DENSE;
+  if (dense) {
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      if (crole[fj] != 2 || csel[fj] < 0) continue;
+      const float* Sp = S + (long long)csel[fj] * M + m0;
+      const float* Gp = Gam + (long long)csel[fj] * M + m0;
+#pragma unroll
+      for (int fi = 0; fi < C::FM; ++fi) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<C>(fi, r);
+          if (rows_full || m0 + row < M) {
+            // S <= 0 (a log-probability)
+            const float dz =
+                (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
+            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = f32_to_bf16(dz);
+            cs[fj] += dz;
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  }
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
     cs[fj] += __shfl_xor(cs[fj], 32, 64);
     if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
   }
-  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g, so
-  // each selected column of this wavefront is done by all 64 lanes, two of
-  // the wavefront's 128 rows each; the column sum is a fixed-order wave sum.
+  // Few selected classes: each selected column of this wavefront by all 64
+  // lanes, two of the wavefront's 128 rows each; the column sum is a
+  // fixed-order wave sum.
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
-    unsigned long long todo = __ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0);
+    unsigned long long todo =
+        dense ? 0ull : __ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0);
     while (todo) {
       const int src = __ffsll((long long)todo) - 1;
       todo &= todo - 1;
@@ -1235,7 +1372,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
   const int nt = lin % ntiles, mt = lin / ntiles;
   const int m0 = mt * C::BM, n0 = nt * C::BN;
   f32x16 acc[C::FM][C::FN];
-  gemm_big<C>(dZ, ldz, m0, M, Wt, ldz, n0, D, Kp, acc, smem);
+  gemm_big1<C>(dZ, ldz, m0, M, Wt, ldz, n0, D, Kp, acc, smem);
   // Read-modify-write of the fp32 accumulator, one block of 16 rows at a
   // time with all of the block's loads issued before its stores (in program
   // order: the compiler cannot tell the addresses apart).
@@ -1295,7 +1432,7 @@ hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* 
                           int nspan, int big) {
   if (dtype == 0) return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
   if (!big) return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
-  using C = CfgBigB16;
+  using C = CfgBigFwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
@@ -1345,7 +1482,7 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
   if (!big)
     return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
                                ldz, dbpart);
-  using C = CfgBigB16;
+  using C = CfgBigRec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
   if (grid == 0) return hipSuccess;
@@ -1378,7 +1515,7 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
     dim3 tg(ceil_div(D, 64), ceil_div(Kp, 64));
     k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
     if (big) {
-      using C = CfgBigB16;
+      using C = CfgBigDx;
       const int grid = ceil_div(M, C::BM) * ceil_div(D, C::BN);
       if (grid == 0) return hipSuccess;
       k_dx_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)dZ, (const bf16_t*)wt, ldz, M, D,
@@ -1421,7 +1558,7 @@ hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const v
 
 int rec_tile_rows(int dtype, int big) {
   if (dtype == 0) return Pick<float>::rec::BM;
-  return big ? CfgBigB16::BM : Pick<bf16_t>::rec::BM;
+  return big ? CfgBigRec::BM : Pick<bf16_t>::rec::BM;
 }
 
 int use_big_core(int dtype, int D, int chunk, const void* X, const void* W) {
