@@ -35,6 +35,10 @@ GEMM_SRC = os.path.join(ROOT, "vocabulary_ctc_loss_amd", "csrc", "pcx_gemm.hip")
 
 # Kernel families whose work is a slice of the head GEMMs: FLOPs per step.
 GEMM_KERNELS = ("fwd_gemm_lse", "bwd_recompute_dz", "dx_gemm", "dw_gemm")
+# The CTC recursions: per (frame, extended-label state) each writes its FP64
+# value (alpha, beta: 2 x 8 B) and reads one fp32 emission (2 x 4 B).
+DP_KERNEL = "ctc_alpha_beta"
+DP_BYTES_PER_STATE = 24
 
 
 def parse():
@@ -164,6 +168,13 @@ def main():
         achieved = flops_per_launch / (dom_ms / dom_n / 1e3)
         roof = {"bound": "mfma", "achieved": achieved / 1e12, "peak": peak / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / peak,
+                "traffic": traffic_from_profiles(dom, bt.name)}
+    elif dom == DP_KERNEL:
+        L = np.diff(bt.tgt_off).astype(np.int64)
+        states = int(np.sum(bt.frame_counts.astype(np.int64) * (2 * L + 1)))
+        achieved = DP_BYTES_PER_STATE * states * args.steps / (dom_ms / 1e3)
+        roof = {"bound": "hbm", "achieved": achieved / 1e9, "peak": HBM_PEAK / 1e9,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK,
                 "traffic": traffic_from_profiles(dom, bt.name)}
     else:
         roof = {"bound": "alu", "achieved": None, "peak": None, "unit": None, "frac": None,
