@@ -917,9 +917,10 @@ struct CfgBig {
   static_assert(TILEB % (1024 * WAVES) == 0 && WM % 32 == 0 && WN % 32 == 0, "big tile");
   static_assert((BK == 32 || BK == 64) && NBUF >= 2 && LDS_BYTES <= 128 * 1024, "big stages");
 };
-using CfgBigFwd = CfgBig<2, 4, 64, 2>;
-using CfgBigRec = CfgBig<2, 4, 64, 2>;
-using CfgBigDx = CfgBig<2, 4, 64, 2>;
+// Eight 64 x 128 wavefronts (4 x 2): measured ahead of 2 x 4 on the LLM head.
+using CfgBigFwd = CfgBig<4, 2, 64, 2>;
+using CfgBigRec = CfgBig<4, 2, 64, 2>;
+using CfgBigDx = CfgBig<4, 2, 64, 2>;
 
 #define PCX_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
@@ -1315,8 +1316,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
   }
   // Few selected classes: each selected column of this wavefront by all 64
-  // lanes, two of the wavefront's 128 rows each; the column sum is a
+  // lanes (WM / 64 of the wavefront's rows each); the column sum is a
   // fixed-order wave sum.
+  static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
+  constexpr int RPL = C::WM / 64;
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
     unsigned long long todo =
@@ -1330,8 +1333,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       const float* Gp = Gam + (long long)sel * M + m0;
       float sum = 0.f;
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int row = wm * C::WM + 2 * lane + t;
+      for (int t = 0; t < RPL; ++t) {
+        const int row = wm * C::WM + RPL * lane + t;
         if (m0 + row < M) {
           // S <= 0 (a log-probability)
           const float dz =
