@@ -51,6 +51,33 @@ __device__ __forceinline__ double exp_nonpos(double x) {
   return ldexp(p, (int)n);
 }
 
+// Table entry j of exp_nonpos_tab: 2^(j/64) = 2 exp((j - 64) ln2 / 64),
+// j = 0..63 (within one ulp).
+__device__ __forceinline__ double exp_tab_entry(int j) {
+  return 2.0 * exp_nonpos((double)(j - 64) * 0x1.62e42fefa39efp-7);
+}
+
+// exp(x) for x <= 0 in IEEE double with a 64-entry table of 2^(j/64):
+// x = (64 q + j) ln2 / 64 + r with |r| <= ln2 / 128 (Cody-Waite, ln2 / 64
+// split into head and tail), exp(x) = 2^q 2^(j/64) e^r, e^r by its degree-5
+// Taylor polynomial (truncation < 4e-17 relative).  Within about 2 ulp over
+// the normal range; 0 below it.  About half the double-precision operations
+// of exp_nonpos.
+__device__ __forceinline__ double exp_nonpos_tab(double x, const double* __restrict__ tab) {
+  x = fmax(x, -746.0);
+  const double kd = rint(x * 0x1.71547652b82fep+6);  // x * 64 / ln2
+  double r = fma(-kd, 0x1.62e42ff000000p-7, x);      // ln2/64 head
+  r = fma(-kd, -0x1.718432a1b0e26p-41, r);           // ln2/64 tail
+  const int k = (int)kd;
+  double p = 0x1.1111111111111p-7;                   // 1/5!
+  p = fma(p, r, 0x1.5555555555555p-5);               // 1/4!
+  p = fma(p, r, 0x1.5555555555555p-3);               // 1/3!
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(tab[k & 63] * p, k >> 6);
+}
+
 // Work-group barrier that orders LDS accesses only: the waves' outstanding
 // global loads and stores are not waited for (a plain __syncthreads also
 // drains them, which would expose prefetch and store latency).

@@ -474,6 +474,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   __shared__ __attribute__((aligned(16))) float s_bias[2][C::BM];
   __shared__ float f_m[C::WGM][C::BN];
   __shared__ double f_s[C::WGM][C::BN];
+
   int ft, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
   const int f0 = ft * C::BN;
@@ -1094,11 +1095,14 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
   // every fragment read wait for all outstanding global->LDS loads.
   constexpr int O_SEL = C::LDS_BYTES, O_BIAS = O_SEL + 2 * C::BM * 4;
   constexpr int O_FM = O_BIAS + 2 * C::BM * 4, O_FS = O_FM + C::WGM * C::BN * 4;
-  __shared__ __attribute__((aligned(16))) char smem[O_FS + C::WGM * C::BN * 8];
+  constexpr int O_EXP = O_FS + C::WGM * C::BN * 8;
+  __shared__ __attribute__((aligned(16))) char smem[O_EXP + 64 * 8];
   int (*s_sel)[C::BM] = reinterpret_cast<int (*)[C::BM]>(smem + O_SEL);
   float (*s_bias)[C::BM] = reinterpret_cast<float (*)[C::BM]>(smem + O_BIAS);
   float (*f_m)[C::BN] = reinterpret_cast<float (*)[C::BN]>(smem + O_FM);
   double (*f_s)[C::BN] = reinterpret_cast<double (*)[C::BN]>(smem + O_FS);
+  double* s_exp = reinterpret_cast<double*>(smem + O_EXP);  // 2^(j/64)
+  if (threadIdx.x < 64) s_exp[threadIdx.x] = exp_tab_entry(threadIdx.x);
   int ft, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
   const int f0 = ft * C::BN;
@@ -1163,7 +1167,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
         for (int fi = 0; fi < C::FM; ++fi) {
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            sum += exp_nonpos((double)acc[fi][fj][r] - (double)mx);
+            sum += exp_nonpos_tab((double)acc[fi][fj][r] - (double)mx, s_exp);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
