@@ -171,8 +171,9 @@ def test_grad_scaling_and_skipped_outputs():
     assert rel_fro(got["db"], ref["db"]) <= 1e-5
 
 
-def test_deterministic_bitwise():
-    bt = case("spans")
+@pytest.mark.parametrize("name", ["spans", "bf16_big_spans", "bf16_head"])
+def test_deterministic_bitwise(name):
+    bt = case(name)
     a = run_pcx(bt, getters=False)
     b = run_pcx(bt, getters=False)
     assert a["loss"] == b["loss"]
@@ -180,14 +181,20 @@ def test_deterministic_bitwise():
         assert np.array_equal(a[k], b[k]), k
 
 
-def test_chunk_width_changes_only_rounding():
-    bt = case("tiles")
+@pytest.mark.parametrize("name,other,tol", [
+    ("tiles", 700, 1e-6),
+    # bf16: 1000 is not a multiple of 64, so the backward products leave the
+    # 256 x 256 core while the forward stays on it
+    ("bf16_big_spans", 1000, 2e-2),
+])
+def test_chunk_width_changes_only_rounding(name, other, tol):
+    bt = case(name)
     a = run_pcx(bt, getters=False)
     import dataclasses
-    b = run_pcx(dataclasses.replace(bt, chunk=700), getters=False)
+    b = run_pcx(dataclasses.replace(bt, chunk=other), getters=False)
     assert a["loss"] == b["loss"]  # forward does not depend on C
     for k in ("dX", "dW", "db"):
-        assert rel_fro(b[k], a[k]) <= 1e-6, k
+        assert rel_fro(b[k], a[k]) <= tol, k
 
 
 def test_context_reuse_and_repeated_backward():

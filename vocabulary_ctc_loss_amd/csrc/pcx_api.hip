@@ -299,7 +299,7 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
 
   if (M > 0) {
-    const int big = use_big_core(dtype, iD, chunk < iV ? chunk : iV, X, W);
+    const int big = use_big_fwd(dtype, iD, X, W);
     LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
                                      (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big));
     LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,

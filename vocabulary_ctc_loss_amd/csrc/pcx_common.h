@@ -134,9 +134,11 @@ hipError_t launch_prepare(hipStream_t st, int N, int M, int V, int blank, long l
                           int* row_off, uint8_t* flags, long long* dp_off,
                           int* col2sel, int* U, int* tgt_rel, Meta* meta);
 
-// Whether a bf16 head runs on the 256 x 256 GEMM core: head dimension and
-// chunk width multiples of 64, 16-byte aligned X and W (the same answer for
-// the forward and the backward pass of one call).
+// Whether a bf16 head runs on the 256 x 256 GEMM core: the forward needs a
+// head dimension that is a multiple of 64 and 16-byte aligned X and W (so it
+// does not depend on the chunk width); the backward products also need a
+// chunk width that is a multiple of 64.
+int use_big_fwd(int dtype, int D, const void* X, const void* W);
 int use_big_core(int dtype, int D, int chunk, const void* X, const void* W);
 
 // Forward head (pcx_gemm.hip).

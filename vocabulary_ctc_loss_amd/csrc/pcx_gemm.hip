@@ -1568,8 +1568,12 @@ int rec_tile_rows(int dtype, int big) {
   return big ? CfgBigRec::BM : Pick<bf16_t>::rec::BM;
 }
 
+int use_big_fwd(int dtype, int D, const void* X, const void* W) {
+  return dtype != 0 && D > 0 && D % 64 == 0 && aligned16(X) && aligned16(W);
+}
+
 int use_big_core(int dtype, int D, int chunk, const void* X, const void* W) {
-  return dtype != 0 && D > 0 && D % 64 == 0 && chunk % 64 == 0 && aligned16(X) && aligned16(W);
+  return use_big_fwd(dtype, D, X, W) && chunk % 64 == 0;
 }
 
 int dw_tiles(int dtype, int C, int D) {
