@@ -131,6 +131,22 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W,
 pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
                         void* db, void* stream);
 
+/*
+ * Gradient of the summed loss with respect to a scalar offset eta added to
+ * the blank logit of every frame, b = b_pre + eta e_blank ("Pruned CTC for
+ * Memory-Efficient Large-Vocabulary ASR Training", Sec. 4: the frozen LLM
+ * head keeps its weights and learns only this blank offset):
+ *   d_eta = grad_loss * sum_m (g_m p_blank(m) - gamma_blank(m)),
+ * i.e. db[blank] without the V-wide db output or any GEMM.  Computed in FP64
+ * from S and the occupancies (a fixed-order sum); runs the occupancy pass
+ * itself, so it needs only a successful pcx_forward.
+ *   grad_loss  as for pcx_backward.
+ *   d_eta      host out.
+ * Synchronises the stream once.
+ */
+pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta,
+                                 void* stream);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* pcx_last_error(void);
 

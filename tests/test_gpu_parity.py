@@ -110,13 +110,18 @@ def case(name):
         return workloads.make_random(18, N=3, T_lo=100, T_hi=200, V=5000, D=128, blank=4999,
                                      chunk=1024, dtype="bf16", llm_head=True, len_div=3.0,
                                      zipf_s=1.05)
+    # the 14B LLM head width (D = 5120)
+    if name == "bf16_big_d5120":
+        return workloads.make_random(19, N=3, T_lo=60, T_hi=120, V=2000, D=5120, blank=1999,
+                                     chunk=1024, dtype="bf16", llm_head=True, len_div=3.0,
+                                     zipf_s=1.05)
     raise KeyError(name)
 
 
 CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
          "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
          "long_targets", "one_utt", "bf16_llm", "bf16_head", "bf16_big_ragged",
-         "bf16_big_grads", "bf16_big_dense", "bf16_big_spans"]
+         "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -195,6 +200,31 @@ def test_chunk_width_changes_only_rounding(name, other, tol):
     assert a["loss"] == b["loss"]  # forward does not depend on C
     for k in ("dX", "dW", "db"):
         assert rel_fro(b[k], a[k]) <= tol, k
+
+
+@pytest.mark.parametrize("name", ["readme", "blank_mid", "unalignable_mix", "bf16_llm"])
+def test_blank_offset_grad_matches_db_at_blank(name):
+    """d(loss)/d(eta) for a blank-logit offset equals the oracle's db[blank]."""
+    import oracle
+    bt = case(name)
+    ref = oracle.pcx(bt.X, bt.W, bt.b, bt.frame_counts, bt.tgt_off, bt.tgt, bt.blank,
+                     grad=0.75, want_dX=False, want_dW=False, want_db=True, want_lambda=False)
+    want = ref["db"][bt.blank]
+    import torch
+    from pcx_harness import to_device
+    from vocabulary_ctc_loss_amd import Context
+    X, W, b, off, tgt, fc = to_device(bt)
+    ctx = Context()
+    try:
+        ctx.forward(X, W, b, off, tgt, fc, bt.blank, bt.chunk)
+        # without a pcx_backward before it, then after one
+        got = ctx.blank_offset_grad(0.75)
+        ctx.backward(0.75, torch.empty_like(X))
+        again = ctx.blank_offset_grad(0.75)
+    finally:
+        ctx.close()
+    assert got == again
+    assert abs(got - want) <= tolerance(bt) * max(abs(want), 1e-3), (got, want)
 
 
 def test_context_reuse_and_repeated_backward():

@@ -102,6 +102,14 @@ class Context:
         check(self._lib.pcx_backward(self._h, float(grad_loss), _ptr(dX), _ptr(dW), _ptr(db),
                                      _stream_handle(stream)))
 
+    def blank_offset_grad(self, grad_loss: float = 1.0, stream=None) -> float:
+        """d(loss)/d(eta) for an offset eta added to the blank logit of every
+        frame (db[blank] without computing db); see pcx_blank_offset_grad."""
+        out = ctypes.c_double(0.0)
+        check(self._lib.pcx_blank_offset_grad(self._h, float(grad_loss), ctypes.byref(out),
+                                              _stream_handle(stream)))
+        return out.value
+
     # -------------------------------------------------------------- getters
     def _get(self, fn, n, dtype):
         out = np.zeros(max(1, n), dtype=dtype)

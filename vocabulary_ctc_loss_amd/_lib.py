@@ -31,6 +31,7 @@ SIGNATURES = {
     "pcx_forward": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _I64, _P,
                            _I32, _I32, _P, ctypes.POINTER(_D), _P]),
     "pcx_backward": (_I32, [_P, _D, _P, _P, _P, _P]),
+    "pcx_blank_offset_grad": (_I32, [_P, _D, ctypes.POINTER(_D), _P]),
     "pcx_last_error": (ctypes.c_char_p, []),
     "pcx_get_selected": (_I32, [_P, _P, _I64]),
     "pcx_get_relabeled": (_I32, [_P, _P, _I64]),

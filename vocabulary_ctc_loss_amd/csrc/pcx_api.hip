@@ -45,12 +45,12 @@ struct DevBuf {
 // Kernel families timed by the optional event profiler.
 enum Kid {
   K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
-  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_COUNT
+  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
     "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
     "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
-    "dw_reduce", "db_reduce", "cast"};
+    "dw_reduce", "db_reduce", "cast", "blank_offset_grad"};
 
 struct Pending {
   int kid;
@@ -63,7 +63,7 @@ struct pcx_ctx {
   // workspace
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
-  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt;
+  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta;
   Meta* host_meta = nullptr;  // pinned
   // forward state kept for backward / getters
   bool fwd_ok = false;
@@ -90,7 +90,7 @@ size_t total_bytes(const pcx_ctx* c) {
   const DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                           &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
-                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt};
+                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -345,6 +345,45 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   return PCX_OK;
 }
 
+// Occupancies Gamma on U and their row sums g for the last forward pass
+// (they need the backward recursion, run during the forward call).
+static pcx_status run_occupancy(pcx_ctx* ctx, hipStream_t st) {
+  const int M = ctx->M, N = ctx->N, K = ctx->K;
+  ENSURE(Gam, (size_t)K * M * sizeof(float));
+  ENSURE(g, (size_t)M * sizeof(double));
+  LAUNCH(K_FILL, launch_fill_f32(st, (float*)ctx->Gam.p, (long long)K * M, 0.f));
+  LAUNCH(K_OCC, launch_occupancy(st, (const float*)ctx->S.p, M, N, ctx->max_T, ctx->max_L,
+                                 (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                                 (const int*)ctx->tgt_rel.p, (const int*)ctx->utt_status.p,
+                                 (const double*)ctx->utt_logp.p, (const long long*)ctx->dp_off.p,
+                                 (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
+                                 (float*)ctx->Gam.p, (double*)ctx->g.p));
+  return PCX_OK;
+}
+
+pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta, void* stream) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (!d_eta) return fail(PCX_ERR_ARG, "d_eta is NULL");
+  if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "pcx_blank_offset_grad needs a successful pcx_forward");
+  hipStream_t st = (hipStream_t)stream;
+  if (ctx->M == 0) {
+    *d_eta = 0.0;
+    return PCX_OK;
+  }
+  {
+    const pcx_status s_ = run_occupancy(ctx, st);
+    if (s_ != PCX_OK) return s_;
+  }
+  ENSURE(eta, sizeof(double));
+  LAUNCH(K_BLANK, launch_blank_grad(st, (const float*)ctx->S.p, (const float*)ctx->Gam.p,
+                                    (const double*)ctx->g.p, ctx->M, grad_loss,
+                                    (double*)ctx->eta.p));
+  PCX_HIP(hipStreamSynchronize(st));
+  PCX_HIP(hipMemcpy(d_eta, ctx->eta.p, sizeof(double), hipMemcpyDeviceToHost));
+  return PCX_OK;
+}
+
 pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void* db,
                         void* stream) {
   g_last_error.clear();
@@ -361,20 +400,12 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     if (db) PCX_HIP(hipMemsetAsync(db, 0, (size_t)V * esz, st));
     return PCX_OK;
   }
-  const int* row_off = (const int*)ctx->row_off.p;
-  const int* toff = (const int*)ctx->tgt_off.p;
-  const int* trel = (const int*)ctx->tgt_rel.p;
-  const int* ustat = (const int*)ctx->utt_status.p;
-  const long long* dpo = (const long long*)ctx->dp_off.p;
   const float* S = (const float*)ctx->S.p;
 
-  ENSURE(Gam, (size_t)K * M * sizeof(float));
-  ENSURE(g, (size_t)M * sizeof(double));
-  LAUNCH(K_FILL, launch_fill_f32(st, (float*)ctx->Gam.p, (long long)K * M, 0.f));
-  LAUNCH(K_OCC, launch_occupancy(st, S, M, N, ctx->max_T, ctx->max_L, row_off, toff, trel, ustat,
-                                 (const double*)ctx->utt_logp.p, dpo,
-                                 (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
-                                 (float*)ctx->Gam.p, (double*)ctx->g.p));
+  {
+    const pcx_status s_ = run_occupancy(ctx, st);
+    if (s_ != PCX_OK) return s_;
+  }
 
   const int big = use_big_core(dt, D, C, ctx->X, ctx->W);
   const int mtiles = (M + rec_tile_rows(dt, big) - 1) / rec_tile_rows(dt, big);

@@ -185,6 +185,9 @@ hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int ma
                             const double* utt_logp, const long long* dp_off,
                             const double* alpha, const double* beta, float* Gam,
                             double* g);
+// d_eta (device double) = grad * sum_m (g_m exp(S[0][m]) - Gamma[0][m]).
+hipError_t launch_blank_grad(hipStream_t st, const float* S, const float* Gam, const double* g,
+                             int M, double grad, double* out);
 hipError_t launch_fill_f32(hipStream_t st, float* p, long long n, float v);
 
 }  // namespace pcx

@@ -403,6 +403,26 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   }
 }
 
+// out = grad * sum_m (g_m exp(S[0][m]) - Gamma[0][m]): the blank is U[0], so
+// this is the column sum of dZ at the blank (the gradient of a blank-logit
+// offset).  FP64, strided per-thread sums then a fixed-order tree.
+__global__ __launch_bounds__(256) void k_blank_grad(const float* __restrict__ S,
+                                                    const float* __restrict__ Gam,
+                                                    const double* __restrict__ g, int M,
+                                                    double grad, double* __restrict__ out) {
+  __shared__ double part[256];
+  double s = 0.0;
+  for (int m = threadIdx.x; m < M; m += 256)
+    s += g[m] * exp_nonpos((double)S[m]) - (double)Gam[m];  // S <= 0
+  part[threadIdx.x] = s;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = grad * part[0];
+}
+
 __global__ void k_loss_sum(int N, const double* __restrict__ utt_loss,
                            const int* __restrict__ utt_status, Meta* __restrict__ meta) {
   if (threadIdx.x != 0 || blockIdx.x != 0) return;
@@ -490,6 +510,12 @@ hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int ma
   dim3 grid(N, (max_T + OCC_FRAMES - 1) / OCC_FRAMES);
   k_occupancy<<<grid, OCC_THREADS, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status,
                                               utt_logp, dp_off, alpha, beta, Gam, g, Lcap);
+  return hipGetLastError();
+}
+
+hipError_t launch_blank_grad(hipStream_t st, const float* S, const float* Gam, const double* g,
+                             int M, double grad, double* out) {
+  k_blank_grad<<<1, 256, 0, st>>>(S, Gam, g, M, grad, out);
   return hipGetLastError();
 }
 
