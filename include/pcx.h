@@ -31,13 +31,16 @@ extern "C" {
 /* Element type shared by X, W and b (and the gradients written back). */
 typedef enum {
   PCX_F32 = 0,  /* IEEE binary32 */
-  PCX_BF16 = 1  /* bfloat16; float16 is not supported (README constraints) */
+  PCX_BF16 = 1, /* bfloat16; float16 is not supported (README constraints) */
+  PCX_F32_BF16W = 2 /* X fp32; W and b stored bf16 and widened to fp32 one
+                       chunk at a time for an fp32 projection (the pages'
+                       frozen-LLM-head setting, App. C.3) */
 } pcx_dtype;
 
 typedef enum {
   PCX_OK = 0,
   PCX_ERR_ARG = 1,     /* null pointer, negative or inconsistent size      */
-  PCX_ERR_DTYPE = 2,   /* dtype other than PCX_F32 / PCX_BF16              */
+  PCX_ERR_DTYPE = 2,   /* dtype other than the three of pcx_dtype           */
   PCX_ERR_TARGET = 3,  /* label outside [0, V), blank inside a target,     */
                        /* target offsets not monotone or not ending at L   */
   PCX_ERR_LENGTHS = 4, /* a frame count <= 0, or the counts do not sum to M */
@@ -79,7 +82,10 @@ void pcx_destroy(pcx_ctx* ctx);
  *                 after those of utterances 0..n-1 (Sec. 3.1).
  *   W             device, V x D row-major (nn.Linear weight layout).
  *   b             device, V entries, or NULL for a zero bias.
- *   dtype         PCX_F32 or PCX_BF16, the element type of X, W and b.
+ *   dtype         PCX_F32 or PCX_BF16 (the element type of X, W and b), or
+ *                 PCX_F32_BF16W (X fp32, W and b bf16; the projections run in
+ *                 fp32 on W widened chunk by chunk, C rows at a time in the
+ *                 backward pass and whole 2048-row spans in the forward).
  *   M, D, V, N    frames, head width, vocabulary size, utterances (N >= 0,
  *                 M >= 0, D >= 1, V >= 1).
  *   tgt_off       device int32, N + 1 monotone offsets into tgt, tgt_off[0]
@@ -122,9 +128,9 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W,
  *
  *   grad_loss  upstream gradient of the summed loss (any scaling, e.g. a
  *              division by the target-token count, goes here).
- *   dX         device, M x D in the input dtype, or NULL to skip.
- *   dW         device, V x D in the input dtype, or NULL to skip.
- *   db         device, V in the input dtype, or NULL to skip.
+ *   dX         device, M x D in the dtype of X, or NULL to skip.
+ *   dW         device, V x D in the dtype of W, or NULL to skip.
+ *   db         device, V in the dtype of b (that of W), or NULL to skip.
  * Outputs are overwritten, not accumulated.  Rows of excluded utterances get
  * exact zeros.  May be called more than once per forward.  No host sync.
  */

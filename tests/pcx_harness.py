@@ -10,10 +10,12 @@ import workloads
 
 def to_device(bt: workloads.Batch, dev="cuda:0"):
     import torch
-    dt = torch.float32 if bt.dtype == "f32" else torch.bfloat16
-    X = torch.from_numpy(bt.X).to(dev).to(dt)
-    W = torch.from_numpy(bt.W).to(dev).to(dt)
-    b = None if bt.b is None else torch.from_numpy(bt.b).to(dev).to(dt)
+    # "f32_bf16w": fp32 encoder states with a bf16-stored head
+    xt = torch.bfloat16 if bt.dtype == "bf16" else torch.float32
+    wt = torch.float32 if bt.dtype == "f32" else torch.bfloat16
+    X = torch.from_numpy(bt.X).to(dev).to(xt)
+    W = torch.from_numpy(bt.W).to(dev).to(wt)
+    b = None if bt.b is None else torch.from_numpy(bt.b).to(dev).to(wt)
     off = torch.from_numpy(np.ascontiguousarray(bt.tgt_off, np.int32)).to(dev)
     tgt = torch.from_numpy(np.ascontiguousarray(bt.tgt, np.int32)).to(dev)
     fc = torch.from_numpy(np.ascontiguousarray(bt.frame_counts, np.int32)).to(dev)
@@ -64,5 +66,6 @@ def rel_fro(got, want):
 
 
 def tolerance(bt: workloads.Batch) -> float:
-    # fp32 inputs: relative error 1e-5 on loss and gradients; bf16 inputs: 2e-2.
-    return 1e-5 if bt.dtype == "f32" else 2e-2
+    # fp32 products (fp32 inputs, or fp32 states with a bf16-stored head whose
+    # values both sides see exactly): 1e-5 on loss and gradients; bf16: 2e-2.
+    return 2e-2 if bt.dtype == "bf16" else 1e-5

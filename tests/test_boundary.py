@@ -70,7 +70,7 @@ def test_null_context_is_rejected(lib):
 def test_argument_validation_before_device_work(lib):
     h = _ctx(lib)
     try:
-        assert _fwd(lib, h, dtype=2) == 2          # fp16 unsupported
+        assert _fwd(lib, h, dtype=3) == 2          # no such dtype (fp16 has no code)
         assert b"dtype" in lib.pcx_last_error()
         assert _fwd(lib, h, dtype=7) == 2
         assert _fwd(lib, h, M=-1) == 1

@@ -115,13 +115,23 @@ def case(name):
         return workloads.make_random(19, N=3, T_lo=60, T_hi=120, V=2000, D=5120, blank=1999,
                                      chunk=1024, dtype="bf16", llm_head=True, len_div=3.0,
                                      zipf_s=1.05)
+    # fp32 states with a bf16-stored head (fp32 projections on W widened one
+    # chunk or 2048-class span at a time): several spans and chunks, ragged
+    if name == "f32_bf16w_head":
+        return workloads.make_random(20, N=4, T_lo=40, T_hi=110, V=5000, D=64, chunk=1024,
+                                     dtype="f32_bf16w")
+    if name == "f32_bf16w_llm":
+        return workloads.make_random(21, N=3, T_lo=50, T_hi=100, V=3000, D=128, blank=2999,
+                                     chunk=4096, dtype="f32_bf16w", llm_head=True,
+                                     len_div=3.0, zipf_s=1.05)
     raise KeyError(name)
 
 
 CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
          "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
          "long_targets", "one_utt", "bf16_llm", "bf16_head", "bf16_big_ragged",
-         "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120"]
+         "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120",
+         "f32_bf16w_head", "f32_bf16w_llm"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -145,7 +155,7 @@ def test_parity_with_oracle(name):
         (got["loss"], ref["loss"])
     assert rel_fro(got["utt_loss"], ref["utt_loss"]) <= tol
     # intermediates
-    if bt.dtype == "f32":
+    if bt.dtype != "bf16":
         np.testing.assert_allclose(got["lam"], ref["lambda"], rtol=0, atol=2e-5)
         np.testing.assert_allclose(got["S"], ref["logp_cols"].T, rtol=0, atol=2e-5)
         np.testing.assert_allclose(got["Gam"], ref["gamma_cols"].T, rtol=0, atol=1e-5)
@@ -154,12 +164,13 @@ def test_parity_with_oracle(name):
         # accumulation of the D products
         np.testing.assert_allclose(got["lam"], ref["lambda"], rtol=0, atol=2e-4)
         np.testing.assert_allclose(got["S"], ref["logp_cols"].T, rtol=0, atol=2e-4)
-    # gradients
+    # gradients (dW and db of a bf16-stored head are bf16 outputs)
     for k in ("dX", "dW", "db"):
         if ref[k] is None or got[k] is None:
             continue
         e = rel_fro(got[k], ref[k])
-        assert e <= tol, (k, e)
+        kt = 2e-2 if (bt.dtype == "f32_bf16w" and k != "dX") else tol
+        assert e <= kt, (k, e)
     # excluded utterances: exact zeros in their dX rows
     row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
     for n in range(bt.N):

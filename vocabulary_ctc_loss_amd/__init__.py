@@ -14,7 +14,7 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PcxError, check,  # noqa: F401
+from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PCX_F32_BF16W, PcxError, check,  # noqa: F401
                    load)
 
 __all__ = ["Context", "PcxError", "pruned_ctc_loss", "pack_targets", "load", "LIB_PATH"]
@@ -25,13 +25,18 @@ def _torch():
     return torch
 
 
-def _dtype_code(t) -> int:
+def _dtype_code(X, W) -> int:
+    """pcx_dtype of an (X, W) pair: both fp32, both bf16, or fp32 X with a
+    bf16-stored head; anything else is passed through for the library to
+    reject."""
     torch = _torch()
-    if t.dtype == torch.float32:
+    if X.dtype == torch.float32 and W.dtype == torch.float32:
         return PCX_F32
-    if t.dtype == torch.bfloat16:
+    if X.dtype == torch.bfloat16 and W.dtype == torch.bfloat16:
         return PCX_BF16
-    return 2 if t.dtype == torch.float16 else 99  # rejected by the library
+    if X.dtype == torch.float32 and W.dtype == torch.bfloat16:
+        return PCX_F32_BF16W
+    return 99
 
 
 def _ptr(t) -> Optional[int]:
@@ -91,7 +96,7 @@ class Context:
         loss = ctypes.c_double(0.0)
         info = FwdInfo()
         check(self._lib.pcx_forward(
-            self._h, _ptr(X), _ptr(W), _ptr(b), _dtype_code(X), M, D, V, N, _ptr(tgt_off),
+            self._h, _ptr(X), _ptr(W), _ptr(b), _dtype_code(X, W), M, D, V, N, _ptr(tgt_off),
             _ptr(tgt) if L_tot else None, L_tot, _ptr(frame_counts), int(blank), int(chunk),
             _stream_handle(stream), ctypes.byref(loss), ctypes.byref(info)))
         self.info = {f: getattr(info, f) for f, _ in FwdInfo._fields_}

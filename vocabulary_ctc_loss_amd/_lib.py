@@ -14,6 +14,7 @@ LIB_PATH = os.path.join(_HERE, "libpcx.so")
 
 PCX_F32 = 0
 PCX_BF16 = 1
+PCX_F32_BF16W = 2
 
 STATUS_NAMES = {
     0: "PCX_OK", 1: "PCX_ERR_ARG", 2: "PCX_ERR_DTYPE", 3: "PCX_ERR_TARGET",

@@ -45,12 +45,12 @@ struct DevBuf {
 // Kernel families timed by the optional event profiler.
 enum Kid {
   K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
-  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_COUNT
+  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
     "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
     "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
-    "dw_reduce", "db_reduce", "cast", "blank_offset_grad"};
+    "dw_reduce", "db_reduce", "cast", "blank_offset_grad", "widen_head"};
 
 struct Pending {
   int kid;
@@ -63,7 +63,7 @@ struct pcx_ctx {
   // workspace
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
-  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta;
+  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32;
   Meta* host_meta = nullptr;  // pinned
   // forward state kept for backward / getters
   bool fwd_ok = false;
@@ -90,7 +90,8 @@ size_t total_bytes(const pcx_ctx* c) {
   const DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                           &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
-                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta};
+                          &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta,
+                          &c->w32, &c->b32};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -227,8 +228,9 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
   ctx->fwd_ok = false;
   ctx->bwd_done = false;
-  if (dtype != PCX_F32 && dtype != PCX_BF16)
-    return fail(PCX_ERR_DTYPE, "dtype %d is not supported (fp32 or bf16 only)", (int)dtype);
+  if (dtype != PCX_F32 && dtype != PCX_BF16 && dtype != PCX_F32_BF16W)
+    return fail(PCX_ERR_DTYPE, "dtype %d is not supported (fp32, bf16 or fp32 with a bf16 head)",
+                (int)dtype);
   if (M < 0 || D < 1 || V < 1 || N < 0 || L_tot < 0)
     return fail(PCX_ERR_ARG, "bad sizes M=%lld D=%lld V=%lld N=%d L_tot=%lld", (long long)M,
                 (long long)D, (long long)V, (int)N, (long long)L_tot);
@@ -298,10 +300,33 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(utt_logp, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
 
-  if (M > 0) {
+  if (M > 0 && dtype == PCX_F32_BF16W) {
+    // fp32 projection of a bf16 head: whole 2048-class spans of W (about C
+    // rows) widened to fp32 at a time.
+    const int eff_chunk = chunk < iV ? chunk : iV;
+    const int fspans = eff_chunk / LSE_SPAN > 1 ? eff_chunk / LSE_SPAN : 1;
+    const int Cf = fspans * LSE_SPAN;
+    ENSURE(w32, (size_t)Cf * D * sizeof(float));
+    if (b) ENSURE(b32, (size_t)Cf * sizeof(float));
+    for (int c0 = 0; c0 < iV; c0 += Cf) {
+      const int c1 = (c0 + Cf < iV) ? c0 + Cf : iV;
+      LAUNCH(K_WIDEN, launch_widen(st, (const uint16_t*)W + (long long)c0 * D, (float*)ctx->w32.p,
+                                   (long long)(c1 - c0) * D));
+      if (b)
+        LAUNCH(K_WIDEN, launch_widen(st, (const uint16_t*)b + c0, (float*)ctx->b32.p, c1 - c0));
+      LAUNCH(K_FWD_LSE, launch_fwd_lse(st, PCX_F32, X, ctx->w32.p, b ? ctx->b32.p : nullptr, iM,
+                                       iD, c1 - c0, (const int*)ctx->col2sel.p + c0,
+                                       (float*)ctx->S.p, (double2*)ctx->part.p,
+                                       (c1 - c0 + LSE_SPAN - 1) / LSE_SPAN, 0, c0 / LSE_SPAN,
+                                       nspan));
+    }
+  } else if (M > 0) {
     const int big = use_big_fwd(dtype, iD, X, W);
     LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
-                                     (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big));
+                                     (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big, 0,
+                                     nspan));
+  }
+  if (M > 0) {
     LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,
                                    (double*)ctx->lam.p, (float*)ctx->lamf.p));
     LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
@@ -390,14 +415,19 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
   if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "pcx_backward needs a successful pcx_forward");
   hipStream_t st = (hipStream_t)stream;
-  const int M = ctx->M, D = ctx->D, V = ctx->V, N = ctx->N, K = ctx->K, dt = ctx->dtype;
+  const int M = ctx->M, D = ctx->D, V = ctx->V, dt = ctx->dtype;
   const int C = ctx->chunk;
-  const size_t esz = dt == PCX_F32 ? 4 : 2;
+  // compute dtype of the products, and dtype of the head-shaped outputs
+  const bool widen = dt == PCX_F32_BF16W;
+  const int cdt = widen ? PCX_F32 : dt;
+  const int wdt = widen ? PCX_BF16 : dt;
+  const size_t esz = cdt == PCX_F32 ? 4 : 2;
+  const size_t wesz = wdt == PCX_F32 ? 4 : 2;
   if (!dX && !dW && !db) return PCX_OK;
   if (M == 0) {
     // No frames: every head gradient is zero.
-    if (dW) PCX_HIP(hipMemsetAsync(dW, 0, (size_t)V * D * esz, st));
-    if (db) PCX_HIP(hipMemsetAsync(db, 0, (size_t)V * esz, st));
+    if (dW) PCX_HIP(hipMemsetAsync(dW, 0, (size_t)V * D * wesz, st));
+    if (db) PCX_HIP(hipMemsetAsync(db, 0, (size_t)V * wesz, st));
     return PCX_OK;
   }
   const float* S = (const float*)ctx->S.p;
@@ -407,13 +437,13 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     if (s_ != PCX_OK) return s_;
   }
 
-  const int big = use_big_core(dt, D, C, ctx->X, ctx->W);
-  const int mtiles = (M + rec_tile_rows(dt, big) - 1) / rec_tile_rows(dt, big);
+  const int big = use_big_core(cdt, D, C, ctx->X, ctx->W);
+  const int mtiles = (M + rec_tile_rows(cdt, big) - 1) / rec_tile_rows(cdt, big);
   ENSURE(dZ, (size_t)M * C * esz);
   ENSURE(dbpart, (size_t)mtiles * C * sizeof(float));
   float* dxacc = nullptr;
   if (dX) {
-    if (dt == PCX_F32) {
+    if (cdt == PCX_F32) {
       dxacc = (float*)dX;
     } else {
       ENSURE(dXacc, (size_t)M * D * sizeof(float));
@@ -421,9 +451,13 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       dxacc = (float*)ctx->dXacc.p;
     }
   }
+  if (widen) {
+    ENSURE(w32, (size_t)C * D * sizeof(float));
+    if (ctx->b) ENSURE(b32, (size_t)C * sizeof(float));
+  }
   // Split of the frame reduction of dW: enough work-groups to fill the chip,
   // at least 1024 frames per split; fixed for a given shape.
-  const int wtiles = dw_tiles(dt, C, D);
+  const int wtiles = dw_tiles(cdt, C, D);
   int splitk = (1024 + wtiles - 1) / wtiles;
   const int maxsplit = (M + 1023) / 1024;
   if (splitk > maxsplit) splitk = maxsplit;
@@ -432,27 +466,43 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
 
   const int nchunks = (V + C - 1) / C;
   for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * C, c1 = (c0 + C < V) ? c0 + C : V;
+    const int c0 = ch * C, c1 = (c0 + C < V) ? c0 + C : V, Cc = c1 - c0;
+    // The products see the chunk's head rows as rows [w0, w0 + Cc) of Wk
+    // (the head itself, or its fp32 copy for a bf16-stored head).
+    const void* Wk = ctx->W;
+    const void* bk = ctx->b;
+    const int* sel = (const int*)ctx->col2sel.p;
+    int w0 = c0;
+    if (widen) {
+      LAUNCH(K_WIDEN, launch_widen(st, (const uint16_t*)ctx->W + (long long)c0 * D,
+                                   (float*)ctx->w32.p, (long long)Cc * D));
+      if (ctx->b)
+        LAUNCH(K_WIDEN, launch_widen(st, (const uint16_t*)ctx->b + c0, (float*)ctx->b32.p, Cc));
+      Wk = ctx->w32.p;
+      bk = ctx->b ? ctx->b32.p : nullptr;
+      sel += c0;
+      w0 = 0;
+    }
     LAUNCH(K_RECOMPUTE,
-           launch_recompute(st, dt, ctx->X, ctx->W, ctx->b, M, D, c0, c1,
-                            (const int*)ctx->col2sel.p, (const float*)ctx->lamf.p,
-                            (const double*)ctx->g.p, S, (const float*)ctx->Gam.p, grad_loss,
-                            ctx->dZ.p, C, (float*)ctx->dbpart.p, big));
+           launch_recompute(st, cdt, ctx->X, Wk, bk, M, D, w0, w0 + Cc, sel,
+                            (const float*)ctx->lamf.p, (const double*)ctx->g.p, S,
+                            (const float*)ctx->Gam.p, grad_loss, ctx->dZ.p, C,
+                            (float*)ctx->dbpart.p, big));
     if (dX)
-      LAUNCH(K_DX, launch_dx(st, dt, ctx->dZ.p, C, ctx->W, M, D, c0, c1, dxacc, ch == 0,
+      LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, C, Wk, M, D, w0, w0 + Cc, dxacc, ch == 0,
                              ctx->wt.p, big));
     if (dW) {
-      LAUNCH(K_DW, launch_dw(st, dt, ctx->dZ.p, C, ctx->X, M, D, c0, c1,
+      LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, C, ctx->X, M, D, w0, w0 + Cc,
                              (float*)ctx->dwpart.p, splitk));
-      LAUNCH(K_DW_REDUCE, launch_dw_reduce(st, dt, (const float*)ctx->dwpart.p, splitk, c1 - c0,
-                                           D, dW, c0));
+      LAUNCH(K_DW_REDUCE, launch_dw_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc, D,
+                                           dW, c0));
     }
     if (db)
-      LAUNCH(K_DB_REDUCE, launch_db_reduce(st, dt, (const float*)ctx->dbpart.p, mtiles, c1 - c0,
-                                           C, db, c0));
+      LAUNCH(K_DB_REDUCE, launch_db_reduce(st, wdt, (const float*)ctx->dbpart.p, mtiles, Cc, C,
+                                           db, c0));
   }
-  if (dX && dt != PCX_F32)
-    LAUNCH(K_CAST, launch_cast_out(st, dt, dxacc, dX, (long long)M * D));
+  if (dX && cdt != PCX_F32)
+    LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;
   return PCX_OK;
 }

@@ -142,9 +142,12 @@ int use_big_fwd(int dtype, int D, const void* X, const void* W);
 int use_big_core(int dtype, int D, int chunk, const void* X, const void* W);
 
 // Forward head (pcx_gemm.hip).
+// span0 / part_ld: the launch covers the 2048-class spans span0.. of a
+// partial array with part_ld spans per frame (fp32 only; bf16: 0 / nspan).
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W,
                           const void* b, int M, int D, int V, const int* col2sel,
-                          float* Zsel, double2* part, int nspan, int big);
+                          float* Zsel, double2* part, int nspan, int big, int span0,
+                          int part_ld);
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan,
                          double* lam, float* lamf);
 hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int M);
@@ -170,6 +173,8 @@ hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int 
                             int cols, int ld, void* db, long long col_base);
 hipError_t launch_cast_out(hipStream_t st, int dtype, const float* src, void* dst,
                            long long n);
+// dst[i] = fp32(src[i]) for n bf16 values.
+hipError_t launch_widen(hipStream_t st, const void* src, float* dst, long long n);
 
 // Alignment DP (pcx_ctc.hip).
 // Forward and backward recursions of every utterance in one launch.

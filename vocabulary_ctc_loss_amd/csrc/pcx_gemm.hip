@@ -467,7 +467,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
     const typename C::type* __restrict__ bias, int M, int D, int V,
     const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
-    int nspan, int ftiles, int vec_ok) {
+    int nspan, int ftiles, int vec_ok, int span0, int part_ld) {
   using T = typename C::type;
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int s_sel[2][C::BM];
@@ -556,7 +556,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     double fs = f_s[0][c];
 #pragma unroll
     for (int q = 1; q < C::WGM; ++q) lse_fold(fm, fs, f_m[q][c], f_s[q][c]);
-    part[(long long)frame * nspan + sp] = make_double2((double)fm, fs);
+    part[(long long)frame * part_ld + span0 + sp] = make_double2((double)fm, fs);
   }
 }
 
@@ -1408,6 +1408,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
   }
 }
 
+__global__ void k_widen_bf16(const bf16_t* __restrict__ src, float* __restrict__ dst, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    dst[i] = bf16_to_f32(src[i]);
+}
+
 int grid_cap(long long n, int threads, int cap = 8192) {
   long long g = (n + threads - 1) / threads;
   if (g < 1) g = 1;
@@ -1423,22 +1429,27 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 template <typename T>
 hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
-                     int V, const int* col2sel, float* Zsel, double2* part, int nspan) {
+                     int V, const int* col2sel, float* Zsel, double2* part, int nspan, int span0,
+                     int part_ld) {
   using C = typename Pick<T>::fwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
   k_fwd_lse<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, V,
-                                             col2sel, Zsel, part, nspan, ftiles, vec);
+                                             col2sel, Zsel, part, nspan, ftiles, vec, span0,
+                                             part_ld);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                           int M, int D, int V, const int* col2sel, float* Zsel, double2* part,
-                          int nspan, int big) {
-  if (dtype == 0) return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
-  if (!big) return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan);
+                          int nspan, int big, int span0, int part_ld) {
+  if (dtype == 0)
+    return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, span0, part_ld);
+  if (span0 != 0 || part_ld != nspan) return hipErrorInvalidValue;  // bf16: whole vocabulary
+  if (!big)
+    return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, 0, nspan);
   using C = CfgBigFwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
@@ -1604,6 +1615,12 @@ hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int 
   else
     k_db_reduce<bf16_t><<<ceil_div(cols, 64), 256, 0, st>>>(dbpart, mtiles, cols, ld,
                                                             (bf16_t*)db, col_base);
+  return hipGetLastError();
+}
+
+hipError_t launch_widen(hipStream_t st, const void* src, float* dst, long long n) {
+  if (n == 0) return hipSuccess;
+  k_widen_bf16<<<grid_cap(n, 256), 256, 0, st>>>((const bf16_t*)src, dst, n);
   return hipGetLastError();
 }
 

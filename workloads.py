@@ -97,7 +97,7 @@ def _head(rng, V, D, dtype, llm_head):
         a = np.float32(1.0 / np.sqrt(D))
         W = rng.uniform(-a, a, size=(V, D)).astype(np.float32)
         b = rng.uniform(-a, a, size=V).astype(np.float32)
-    if dtype == "bf16":
+    if dtype in ("bf16", "f32_bf16w"):
         W = round_bf16(W)
         b = round_bf16(b)
     return W, b
