@@ -49,6 +49,24 @@ typedef enum {
   PCX_ERR_LIMIT = 7    /* a target longer than PCX_MAX_TARGET_LEN labels   */
 } pcx_status;
 
+/* How the normalizer and the gradient of the unselected classes are formed
+ * ("Pruned CTC for Memory-Efficient Large-Vocabulary ASR Training", Sec. 3.2
+ * Eq. 4 and App. B.1 Eq. 11).  Both give the same loss and gradients in exact
+ * arithmetic (Proposition 1); they differ only in rounding.
+ *   DIRECT   lambda_m is the online log-sum-exp over the whole vocabulary;
+ *            an unselected class v gets grad g_m exp(z_mv - lambda_m).
+ *   GROUPED  the projection's log-sum-exp covers the unselected classes only,
+ *            giving the "other" column o_m; lambda_m is the log-sum-exp of
+ *            the grouped logits R_m = [Z[m][U], o_m] (o_m left out when every
+ *            class is selected); the other column's gradient
+ *            grad g_m exp(o_m - lambda_m) reaches class v with the weight
+ *            exp(z_mv - o_m).  A cross-check of the direct path, at the same
+ *            cost up to two small per-frame passes. */
+typedef enum {
+  PCX_FORM_DIRECT = 0,
+  PCX_FORM_GROUPED = 1
+} pcx_formulation;
+
 /* Longest target (in labels) the alignment kernels accept. */
 #define PCX_MAX_TARGET_LEN 2047
 
@@ -153,6 +171,13 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
 pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta,
                                  void* stream);
 
+/*
+ * Formulation used by the following pcx_forward calls of this context
+ * (PCX_FORM_DIRECT by default); pcx_backward follows the formulation of the
+ * forward pass it differentiates.  PCX_ERR_ARG for any other value.
+ */
+pcx_status pcx_set_formulation(pcx_ctx* ctx, int32_t form);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char* pcx_last_error(void);
 
@@ -169,6 +194,9 @@ const char* pcx_last_error(void);
  *   normalizer  M double: lambda_m (Eq. 1).
  *   scores      K x M float, class-major: S[j][m] = fp32(Z[m][U[j]] - lambda_m).
  *   occupancy   K x M float, class-major: gamma_{U[j]}(m) (after a backward).
+ *   other       M double: the other column o_m = log sum over the unselected
+ *               classes of exp z_mv (-inf when every class is selected);
+ *               PCX_ERR_STATE unless the last forward was PCX_FORM_GROUPED.
  */
 pcx_status pcx_get_selected(pcx_ctx* ctx, int32_t* out, int64_t capacity);
 pcx_status pcx_get_relabeled(pcx_ctx* ctx, int32_t* out, int64_t capacity);
@@ -178,6 +206,7 @@ pcx_status pcx_get_utt_status(pcx_ctx* ctx, int32_t* out, int64_t capacity);
 pcx_status pcx_get_normalizer(pcx_ctx* ctx, double* out, int64_t capacity);
 pcx_status pcx_get_scores(pcx_ctx* ctx, float* out, int64_t capacity);
 pcx_status pcx_get_occupancy(pcx_ctx* ctx, float* out, int64_t capacity);
+pcx_status pcx_get_other(pcx_ctx* ctx, double* out, int64_t capacity);
 
 /*
  * Optional per-kernel timing.  While enabled, every kernel the context

@@ -23,12 +23,13 @@ def to_device(bt: workloads.Batch, dev="cuda:0"):
 
 
 def run_pcx(bt: workloads.Batch, grad=1.0, want_dX=True, want_dW=True, want_db=True,
-            getters=True, ctx=None):
+            getters=True, ctx=None, grouped=False):
     import torch
     from vocabulary_ctc_loss_amd import Context
     X, W, b, off, tgt, fc = to_device(bt)
     own = ctx is None
     c = Context() if own else ctx
+    c.set_formulation(grouped)
     loss, info = c.forward(X, W, b, off, tgt, fc, bt.blank, bt.chunk)
     dX = torch.full_like(X, float("nan")) if want_dX else None
     dW = torch.full_like(W, float("nan")) if want_dW else None
@@ -41,6 +42,8 @@ def run_pcx(bt: workloads.Batch, grad=1.0, want_dX=True, want_dW=True, want_db=T
                    utt_loss=c.utt_losses(), status=c.utt_status())
         if getters != "light":
             out.update(lam=c.normalizer(), S=c.scores(), Gam=c.occupancy())
+        if grouped:
+            out["other"] = c.other()
     for k, t in (("dX", dX), ("dW", dW), ("db", db)):
         out[k] = None if t is None else t.double().cpu().numpy()
     if own:

@@ -107,3 +107,18 @@ def test_profile_api_without_device(lib):
         assert lib.pcx_profile_read(h, 999, None, None, None) == 1
     finally:
         lib.pcx_destroy(h)
+
+
+def test_formulation_switch_without_device(lib):
+    h = _ctx(lib)
+    try:
+        assert lib.pcx_set_formulation(None, 1) == 1
+        assert lib.pcx_set_formulation(h, 2) == 1      # neither direct nor grouped
+        assert b"formulation" in lib.pcx_last_error()
+        assert lib.pcx_set_formulation(h, -1) == 1
+        assert lib.pcx_set_formulation(h, 1) == 0
+        assert lib.pcx_set_formulation(h, 0) == 0
+        buf = (ctypes.c_double * 8)()
+        assert lib.pcx_get_other(h, buf, 8) == 5       # no forward yet
+    finally:
+        lib.pcx_destroy(h)

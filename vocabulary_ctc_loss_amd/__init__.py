@@ -14,7 +14,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PCX_F32_BF16W, PcxError, check,  # noqa: F401
+from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PCX_F32_BF16W, PCX_FORM_DIRECT,  # noqa: F401
+                   PCX_FORM_GROUPED, PcxError, check,
                    load)
 
 __all__ = ["Context", "PcxError", "pruned_ctc_loss", "pack_targets", "load", "LIB_PATH"]
@@ -83,6 +84,12 @@ class Context:
             pass
 
     # -------------------------------------------------------------- calls
+    def set_formulation(self, grouped: bool):
+        """Direct (default) or grouped ("other"-column) normalizer and
+        complement gradient for the following forward calls."""
+        check(self._lib.pcx_set_formulation(self._h, PCX_FORM_GROUPED if grouped
+                                            else PCX_FORM_DIRECT))
+
     def forward(self, X, W, b, tgt_off, tgt, frame_counts, blank: int = 0,
                 chunk: int = 4096, stream=None):
         """Run pcx_forward; returns (summed loss as float, info dict)."""
@@ -138,6 +145,10 @@ class Context:
 
     def normalizer(self):
         return self._get(self._lib.pcx_get_normalizer, self._shape["M"], np.float64)
+
+    def other(self):
+        """The other column o_m of the last (grouped) forward pass."""
+        return self._get(self._lib.pcx_get_other, self._shape["M"], np.float64)
 
     def scores(self):
         K, M = self._shape["K"], self._shape["M"]

@@ -16,6 +16,9 @@ PCX_F32 = 0
 PCX_BF16 = 1
 PCX_F32_BF16W = 2
 
+PCX_FORM_DIRECT = 0
+PCX_FORM_GROUPED = 1
+
 STATUS_NAMES = {
     0: "PCX_OK", 1: "PCX_ERR_ARG", 2: "PCX_ERR_DTYPE", 3: "PCX_ERR_TARGET",
     4: "PCX_ERR_LENGTHS", 5: "PCX_ERR_STATE", 6: "PCX_ERR_HIP", 7: "PCX_ERR_LIMIT",
@@ -33,6 +36,7 @@ SIGNATURES = {
                            _I32, _I32, _P, ctypes.POINTER(_D), _P]),
     "pcx_backward": (_I32, [_P, _D, _P, _P, _P, _P]),
     "pcx_blank_offset_grad": (_I32, [_P, _D, ctypes.POINTER(_D), _P]),
+    "pcx_set_formulation": (_I32, [_P, _I32]),
     "pcx_last_error": (ctypes.c_char_p, []),
     "pcx_get_selected": (_I32, [_P, _P, _I64]),
     "pcx_get_relabeled": (_I32, [_P, _P, _I64]),
@@ -42,6 +46,7 @@ SIGNATURES = {
     "pcx_get_normalizer": (_I32, [_P, _P, _I64]),
     "pcx_get_scores": (_I32, [_P, _P, _I64]),
     "pcx_get_occupancy": (_I32, [_P, _P, _I64]),
+    "pcx_get_other": (_I32, [_P, _P, _I64]),
     "pcx_profile_enable": (_I32, [_P, _I32]),
     "pcx_profile_reset": (_I32, [_P]),
     "pcx_profile_count": (_I32, []),

@@ -45,12 +45,13 @@ struct DevBuf {
 // Kernel families timed by the optional event profiler.
 enum Kid {
   K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
-  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_COUNT
+  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_ROWSCALE,
+  K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
     "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
     "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
-    "dw_reduce", "db_reduce", "cast", "blank_offset_grad", "widen_head"};
+    "dw_reduce", "db_reduce", "cast", "blank_offset_grad", "widen_head", "grouped_rowscale"};
 
 struct Pending {
   int kid;
@@ -63,7 +64,7 @@ struct pcx_ctx {
   // workspace
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
-  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32;
+  DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32, other, gu, ou;
   Meta* host_meta = nullptr;  // pinned
   // forward state kept for backward / getters
   bool fwd_ok = false;
@@ -73,6 +74,8 @@ struct pcx_ctx {
   const void* W = nullptr;
   const void* b = nullptr;
   int dtype = 0;
+  int form = PCX_FORM_DIRECT;      // for the next forward
+  int fwd_form = PCX_FORM_DIRECT;  // of the last forward
   int M = 0, D = 0, V = 0, N = 0, blank = 0, chunk = 1, K = 0, max_L = 0, max_T = 0;
   long long L_tot = 0, dp_total = 0;
   int nspan = 0;
@@ -91,7 +94,7 @@ size_t total_bytes(const pcx_ctx* c) {
                           &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
                           &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta,
-                          &c->w32, &c->b32};
+                          &c->w32, &c->b32, &c->other, &c->gu, &c->ou};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -207,7 +210,8 @@ void pcx_destroy(pcx_ctx* c) {
   DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                     &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha, &c->beta,
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
-                    &c->dXacc, &c->dwpart, &c->dbpart, &c->wt};
+                    &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta, &c->w32, &c->b32,
+                    &c->other, &c->gu, &c->ou};
   for (DevBuf* b : bufs)
     if (b->p) (void)hipFree(b->p);
   for (Pending& p : c->pending) {
@@ -290,6 +294,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
 
   const int nspan = (iV + LSE_SPAN - 1) / LSE_SPAN;
   ctx->nspan = nspan;
+  // Grouped form: the projection's log-sum-exp covers the unselected classes
+  // only, giving the other column o; lambda then comes from [Z[:, U], o].
+  const int grouped = ctx->form == PCX_FORM_GROUPED;
+  if (grouped) ENSURE(other, (size_t)M * sizeof(double));
   ENSURE(part, (size_t)M * nspan * sizeof(double2));
   ENSURE(lam, (size_t)M * sizeof(double));
   ENSURE(lamf, (size_t)M * sizeof(float));
@@ -318,17 +326,22 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                                        iD, c1 - c0, (const int*)ctx->col2sel.p + c0,
                                        (float*)ctx->S.p, (double2*)ctx->part.p,
                                        (c1 - c0 + LSE_SPAN - 1) / LSE_SPAN, 0, c0 / LSE_SPAN,
-                                       nspan));
+                                       nspan, grouped));
     }
   } else if (M > 0) {
     const int big = use_big_fwd(dtype, iD, X, W);
     LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
                                      (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big, 0,
-                                     nspan));
+                                     nspan, grouped));
   }
   if (M > 0) {
     LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,
-                                   (double*)ctx->lam.p, (float*)ctx->lamf.p));
+                                   grouped ? (double*)ctx->other.p : (double*)ctx->lam.p,
+                                   (float*)ctx->lamf.p));
+    if (grouped)
+      LAUNCH(K_LAMBDA, launch_lambda_grouped(st, (const float*)ctx->S.p,
+                                             (const double*)ctx->other.p, K, iM,
+                                             (double*)ctx->lam.p, (float*)ctx->lamf.p));
     LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
   }
   // The backward recursion runs here too, beside the forward one (it only
@@ -351,6 +364,7 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ctx->W = W;
   ctx->b = b;
   ctx->dtype = dtype;
+  ctx->fwd_form = grouped ? PCX_FORM_GROUPED : PCX_FORM_DIRECT;
   ctx->M = iM;
   ctx->D = iD;
   ctx->V = iV;
@@ -437,6 +451,21 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     if (s_ != PCX_OK) return s_;
   }
 
+  // Grouped form: the unselected classes take the other column's gradient
+  // through the log-sum-exp that formed it.
+  const double* gu = nullptr;
+  const float* ou = nullptr;
+  if (ctx->fwd_form == PCX_FORM_GROUPED) {
+    ENSURE(gu, (size_t)M * sizeof(double));
+    ENSURE(ou, (size_t)M * sizeof(float));
+    LAUNCH(K_ROWSCALE, launch_grouped_rowscale(st, (const double*)ctx->g.p,
+                                               (const double*)ctx->other.p,
+                                               (const double*)ctx->lam.p, M,
+                                               (double*)ctx->gu.p, (float*)ctx->ou.p));
+    gu = (const double*)ctx->gu.p;
+    ou = (const float*)ctx->ou.p;
+  }
+
   const int big = use_big_core(cdt, D, C, ctx->X, ctx->W);
   const int mtiles = (M + rec_tile_rows(cdt, big) - 1) / rec_tile_rows(cdt, big);
   ENSURE(dZ, (size_t)M * C * esz);
@@ -487,7 +516,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
            launch_recompute(st, cdt, ctx->X, Wk, bk, M, D, w0, w0 + Cc, sel,
                             (const float*)ctx->lamf.p, (const double*)ctx->g.p, S,
                             (const float*)ctx->Gam.p, grad_loss, ctx->dZ.p, C,
-                            (float*)ctx->dbpart.p, big));
+                            (float*)ctx->dbpart.p, big, gu, ou));
     if (dX)
       LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, C, Wk, M, D, w0, w0 + Cc, dxacc, ch == 0,
                              ctx->wt.p, big));
@@ -504,6 +533,15 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (dX && cdt != PCX_F32)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;
+  return PCX_OK;
+}
+
+pcx_status pcx_set_formulation(pcx_ctx* ctx, int32_t form) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (form != PCX_FORM_DIRECT && form != PCX_FORM_GROUPED)
+    return fail(PCX_ERR_ARG, "formulation %d is not supported (direct or grouped)", (int)form);
+  ctx->form = form;
   return PCX_OK;
 }
 
@@ -570,6 +608,11 @@ pcx_status pcx_get_utt_status(pcx_ctx* ctx, int32_t* out, int64_t capacity) {
 }
 pcx_status pcx_get_normalizer(pcx_ctx* ctx, double* out, int64_t capacity) {
   return get_copy(ctx, ctx ? ctx->lam : DevBuf(), ctx ? ctx->M : 0, 8, out, capacity, false);
+}
+pcx_status pcx_get_other(pcx_ctx* ctx, double* out, int64_t capacity) {
+  if (ctx && ctx->fwd_ok && ctx->fwd_form != PCX_FORM_GROUPED)
+    return fail(PCX_ERR_STATE, "the last forward pass did not use the grouped formulation");
+  return get_copy(ctx, ctx ? ctx->other : DevBuf(), ctx ? ctx->M : 0, 8, out, capacity, false);
 }
 pcx_status pcx_get_scores(pcx_ctx* ctx, float* out, int64_t capacity) {
   return get_copy(ctx, ctx ? ctx->S : DevBuf(), ctx ? (size_t)ctx->K * ctx->M : 0, 4, out,

@@ -144,12 +144,21 @@ int use_big_core(int dtype, int D, int chunk, const void* X, const void* W);
 // Forward head (pcx_gemm.hip).
 // span0 / part_ld: the launch covers the 2048-class spans span0.. of a
 // partial array with part_ld spans per frame (fp32 only; bf16: 0 / nspan).
+// masked: the log-sum-exp partials cover the unselected classes only (the
+// grouped form's other column); Zsel is written either way.
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W,
                           const void* b, int M, int D, int V, const int* col2sel,
                           float* Zsel, double2* part, int nspan, int big, int span0,
-                          int part_ld);
+                          int part_ld, int masked);
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan,
                          double* lam, float* lamf);
+// Grouped form: lambda from the K gathered logits and the other column.
+hipError_t launch_lambda_grouped(hipStream_t st, const float* Zsel, const double* other, int K,
+                                 int M, double* lam, float* lamf);
+// Grouped backward: gu_m = g_m exp(o_m - lambda_m) and the fp32 shift
+// ou_m = o_m (0 where the complement is empty).
+hipError_t launch_grouped_rowscale(hipStream_t st, const double* g, const double* other,
+                                   const double* lam, int M, double* gu, float* ou);
 hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int M);
 
 // Backward head (pcx_gemm.hip).
@@ -157,7 +166,8 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const void* b, int M, int D, int c0, int c1,
                             const int* col2sel, const float* lamf, const double* g,
                             const float* S, const float* Gam, double grad,
-                            void* dZ, int ldz, float* dbpart, int big);
+                            void* dZ, int ldz, float* dbpart, int big,
+                            const double* gu = nullptr, const float* ou = nullptr);
 // wt: D x ldz scratch for the transposed weight chunk (bf16 only).
 // Rows of the recompute tile (one bias-gradient partial per row tile) and
 // the number of output tiles of one dW product.

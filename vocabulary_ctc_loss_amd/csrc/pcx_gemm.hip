@@ -467,7 +467,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
     const typename C::type* __restrict__ bias, int M, int D, int V,
     const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
-    int nspan, int ftiles, int vec_ok, int span0, int part_ld) {
+    int nspan, int ftiles, int vec_ok, int span0, int part_ld, int masked) {
   using T = typename C::type;
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int s_sel[2][C::BM];
@@ -519,7 +519,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = acc[fi][fj][4 * q + e] + b4[e];
-            acc[fi][fj][4 * q + e] = sl[e] >= -1 ? z : -INFINITY;
+            // in the sum: every vocabulary row of the span, or (masked)
+            // only the unselected ones
+            acc[fi][fj][4 * q + e] = (masked ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
             if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
@@ -576,6 +578,38 @@ __global__ void k_lambda(const double2* __restrict__ part, int M, int nspan,
   lamf[m] = (float)l;
 }
 
+// Grouped logits R = [Z[:, U], o] with o_m = log sum over the unselected
+// classes of exp Z[m][v] ("other" column, Eq. 4): lambda_m = log-sum-exp of
+// the K + 1 entries of R_m (FP64; the selected logits are the fp32 values
+// gathered in Zsel).  o_m = -inf when every class is selected.
+__global__ void k_lambda_grouped(const float* __restrict__ Zsel, const double* __restrict__ other,
+                                 int K, int M, double* __restrict__ lam,
+                                 float* __restrict__ lamf) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  double mx = other[m];
+  for (int j = 0; j < K; ++j) mx = fmax(mx, (double)Zsel[(long long)j * M + m]);
+  double s = other[m] == -INFINITY ? 0.0 : exp_nonpos(other[m] - mx);
+  for (int j = 0; j < K; ++j) s += exp_nonpos((double)Zsel[(long long)j * M + m] - mx);
+  const double l = mx + log(s);
+  lam[m] = l;
+  lamf[m] = (float)l;
+}
+
+// Row factor of the unselected classes in the grouped backward: the "other"
+// column's gradient grad * g_m * p_other(m) (its occupancy is zero), spread
+// over the unselected classes by the log-sum-exp Jacobian exp(z - o_m)
+// (App. B.1, Eq. 11); gu_m = g_m exp(o_m - lambda_m).
+__global__ void k_grouped_rowscale(const double* __restrict__ g, const double* __restrict__ other,
+                                   const double* __restrict__ lam, int M,
+                                   double* __restrict__ gu, float* __restrict__ ou) {
+  const int m = blockIdx.x * blockDim.x + threadIdx.x;
+  if (m >= M) return;
+  const bool empty = other[m] == -INFINITY;  // no unselected class
+  gu[m] = empty ? 0.0 : g[m] * exp_nonpos(other[m] - lam[m]);
+  ou[m] = empty ? 0.f : (float)other[m];
+}
+
 // S[j][m] = fp32(Zsel[j][m] - lambda_m), subtraction in FP64, one rounding.
 __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, int K, int M) {
   const long long n = (long long)K * M;
@@ -608,7 +642,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const int* __restrict__ col2sel, const float* __restrict__ lamf,
     const double* __restrict__ g, const float* __restrict__ S, const float* __restrict__ Gam,
     double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
-    int mtiles, int vec_ok) {
+    int mtiles, int vec_ok, const double* __restrict__ gu, const float* __restrict__ lamu) {
   using T = typename C::type;
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
@@ -632,8 +666,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const int mm = m0 + rr;
     const double gm = mm < M ? g[mm] : 0.0;
     s_g[rr] = gm;
-    s_rs[rr] = (float)(grad * gm);
-    s_lam2[rr] = mm < M ? lamf[mm] * LOG2E : 0.f;
+    // unselected classes: dZ = rs * exp(z - shift); rs = grad g_m and shift =
+    // lambda_m, or in the grouped form grad gu_m and the other column o_m
+    s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
+    s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
   }
   f32x16 acc[C::FM][C::FN];
   gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
@@ -1090,7 +1126,7 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
     int M, int D, int V, const int* __restrict__ col2sel, float* __restrict__ Zsel,
-    double2* __restrict__ part, int nspan, int ftiles) {
+    double2* __restrict__ part, int nspan, int ftiles, int masked) {
   // One LDS object for everything: with a second one, the compiler makes
   // every fragment read wait for all outstanding global->LDS loads.
   constexpr int O_SEL = C::LDS_BYTES, O_BIAS = O_SEL + 2 * C::BM * 4;
@@ -1155,7 +1191,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = acc[fi][fj][4 * q + e] + b4[e];
-            acc[fi][fj][4 * q + e] = sl[e] >= -1 ? z : -INFINITY;
+            // in the sum: every vocabulary row of the span, or (masked)
+            // only the unselected ones
+            acc[fi][fj][4 * q + e] = (masked ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
             if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
@@ -1209,7 +1247,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     int M, int D, int c0, int c1, const int* __restrict__ col2sel,
     const float* __restrict__ lamf, const double* __restrict__ g, const float* __restrict__ S,
     const float* __restrict__ Gam, double grad, bf16_t* __restrict__ dZ, int ldz,
-    float* __restrict__ dbpart, int mtiles) {
+    float* __restrict__ dbpart, int mtiles, const double* __restrict__ gu,
+    const float* __restrict__ lamu) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
   // one LDS object (see k_fwd_lse_big)
@@ -1235,8 +1274,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const int mm = m0 + rr;
     const double gm = mm < M ? g[mm] : 0.0;
     s_g[rr] = gm;
-    s_rs[rr] = (float)(grad * gm);
-    s_lam2[rr] = mm < M ? lamf[mm] * LOG2E : 0.f;
+    // unselected classes: dZ = rs * exp(z - shift); rs = grad g_m and shift =
+    // lambda_m, or in the grouped form grad gu_m and the other column o_m
+    s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
+    s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
   }
   f32x16 acc[C::FM][C::FN];
   gemm_big1<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
@@ -1430,7 +1471,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 template <typename T>
 hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                      int V, const int* col2sel, float* Zsel, double2* part, int nspan, int span0,
-                     int part_ld) {
+                     int part_ld, int masked) {
   using C = typename Pick<T>::fwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
@@ -1438,25 +1479,27 @@ hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
   k_fwd_lse<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, V,
                                              col2sel, Zsel, part, nspan, ftiles, vec, span0,
-                                             part_ld);
+                                             part_ld, masked);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                           int M, int D, int V, const int* col2sel, float* Zsel, double2* part,
-                          int nspan, int big, int span0, int part_ld) {
+                          int nspan, int big, int span0, int part_ld, int masked) {
   if (dtype == 0)
-    return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, span0, part_ld);
+    return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, span0, part_ld,
+                            masked);
   if (span0 != 0 || part_ld != nspan) return hipErrorInvalidValue;  // bf16: whole vocabulary
   if (!big)
-    return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, 0, nspan);
+    return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, 0, nspan,
+                             masked);
   using C = CfgBigFwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
   k_fwd_lse_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
                                                  (const bf16_t*)b, M, D, V, col2sel, Zsel, part,
-                                                 nspan, ftiles);
+                                                 nspan, ftiles, masked);
   return hipGetLastError();
 }
 
@@ -1464,6 +1507,20 @@ hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan, 
                          float* lamf) {
   if (M == 0) return hipSuccess;
   k_lambda<<<ceil_div(M, 256), 256, 0, st>>>(part, M, nspan, lam, lamf);
+  return hipGetLastError();
+}
+
+hipError_t launch_lambda_grouped(hipStream_t st, const float* Zsel, const double* other, int K,
+                                 int M, double* lam, float* lamf) {
+  if (M == 0) return hipSuccess;
+  k_lambda_grouped<<<ceil_div(M, 256), 256, 0, st>>>(Zsel, other, K, M, lam, lamf);
+  return hipGetLastError();
+}
+
+hipError_t launch_grouped_rowscale(hipStream_t st, const double* g, const double* other,
+                                   const double* lam, int M, double* gu, float* ou) {
+  if (M == 0) return hipSuccess;
+  k_grouped_rowscale<<<ceil_div(M, 256), 256, 0, st>>>(g, other, lam, M, gu, ou);
   return hipGetLastError();
 }
 
@@ -1478,7 +1535,7 @@ template <typename T>
 hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                        int c0, int c1, const int* col2sel, const float* lamf, const double* g,
                        const float* S, const float* Gam, double grad, void* dZ, int ldz,
-                       float* dbpart) {
+                       float* dbpart, const double* gu, const float* lamu) {
   using C = typename Pick<T>::rec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
@@ -1486,20 +1543,21 @@ hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void*
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
   k_recompute<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, c0, c1,
                                                col2sel, lamf, g, S, Gam, grad, (T*)dZ, ldz,
-                                               dbpart, mtiles, vec);
+                                               dbpart, mtiles, vec, gu, lamu);
   return hipGetLastError();
 }
 
 hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                             int M, int D, int c0, int c1, const int* col2sel, const float* lamf,
                             const double* g, const float* S, const float* Gam, double grad,
-                            void* dZ, int ldz, float* dbpart, int big) {
+                            void* dZ, int ldz, float* dbpart, int big, const double* gu,
+                            const float* lamu) {
   if (dtype == 0)
     return recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ, ldz,
-                              dbpart);
+                              dbpart, gu, lamu);
   if (!big)
     return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
-                               ldz, dbpart);
+                               ldz, dbpart, gu, lamu);
   using C = CfgBigRec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
@@ -1507,7 +1565,7 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
   k_recompute_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
                                                    (const bf16_t*)b, M, D, c0, c1, col2sel, lamf,
                                                    g, S, Gam, grad, (bf16_t*)dZ, ldz, dbpart,
-                                                   mtiles);
+                                                   mtiles, gu, lamu);
   return hipGetLastError();
 }
 
