@@ -462,12 +462,12 @@ template <> struct Pick<bf16_t> {
 // running partial; at the end of the span the two lane halves and the WGM
 // wave rows are folded in a fixed order.  Selected vocabulary rows are
 // gathered into Zsel (class-major, K x M), 32 frames per coalesced store.
-template <class C>
+template <class C, bool MASKED>
 __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
     const typename C::type* __restrict__ bias, int M, int D, int V,
     const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
-    int nspan, int ftiles, int vec_ok, int span0, int part_ld, int masked) {
+    int nspan, int ftiles, int vec_ok, int span0, int part_ld) {
   using T = typename C::type;
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int s_sel[2][C::BM];
@@ -521,7 +521,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
             const float z = acc[fi][fj][4 * q + e] + b4[e];
             // in the sum: every vocabulary row of the span, or (masked)
             // only the unselected ones
-            acc[fi][fj][4 * q + e] = (masked ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
+            acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
             if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
@@ -562,20 +562,35 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   }
 }
 
-// lambda_m = max + log(sum_spans s * exp(m_span - max)), spans in order.
-__global__ void k_lambda(const double2* __restrict__ part, int M, int nspan,
-                         double* __restrict__ lam, float* __restrict__ lamf) {
-  const int m = blockIdx.x * blockDim.x + threadIdx.x;
-  if (m >= M) return;
-  const double2* p = part + (long long)m * nspan;
+// lambda_m = max + log(sum_spans s * exp(m_span - max)).  Eight lanes per
+// frame: lane j takes the spans j, j + 8, ... (the eight lanes of a frame
+// read 128 consecutive bytes at a time); the maximum is exact in any order
+// and the eight partial sums are added in a fixed butterfly (IEEE addition is
+// commutative, so both lanes of a pair hold the same sum).
+constexpr int LAM_LANES = 8;
+__global__ __launch_bounds__(256) void k_lambda(const double2* __restrict__ part, int M,
+                                                int nspan, double* __restrict__ lam,
+                                                float* __restrict__ lamf) {
+  const long long gt = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int m = (int)(gt / LAM_LANES), j = (int)(gt % LAM_LANES);
+  const bool in = m < M;
+  const double2* p = part + (long long)(in ? m : 0) * nspan;
   double mx = -INFINITY;
-  for (int i = 0; i < nspan; ++i) mx = fmax(mx, p[i].x);
+  if (in)
+    for (int i = j; i < nspan; i += LAM_LANES) mx = fmax(mx, p[i].x);
+#pragma unroll
+  for (int o = 1; o < LAM_LANES; o <<= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
   double s = 0.0;
-  for (int i = 0; i < nspan; ++i)
-    if (p[i].x != -INFINITY) s += p[i].y * exp_nonpos(p[i].x - mx);
-  const double l = mx + log(s);
-  lam[m] = l;
-  lamf[m] = (float)l;
+  if (in)
+    for (int i = j; i < nspan; i += LAM_LANES)
+      if (p[i].x != -INFINITY) s += p[i].y * exp_nonpos(p[i].x - mx);
+#pragma unroll
+  for (int o = 1; o < LAM_LANES; o <<= 1) s += __shfl_xor(s, o, 64);
+  if (in && j == 0) {
+    const double l = mx + log(s);
+    lam[m] = l;
+    lamf[m] = (float)l;
+  }
 }
 
 // Grouped logits R = [Z[:, U], o] with o_m = log sum over the unselected
@@ -868,24 +883,33 @@ __global__ void k_dw_reduce(const float* __restrict__ part, int splitk, int rows
   }
 }
 
-// db[col] = sum over row tiles of dbpart[tile][col]: four fixed quarters of
-// the tiles per column, combined in order.
+// db[col] = sum over row tiles of dbpart[tile][col]: sixteen fixed groups of
+// consecutive tiles per column (one wavefront each, 64 columns per block),
+// the group sums then added in group order.
+constexpr int DB_GROUPS = 16;
 template <typename T>
-__global__ __launch_bounds__(256) void k_db_reduce(const float* __restrict__ dbpart, int mtiles,
-                                                   int cols, int ld, T* __restrict__ db,
-                                                   long long col_base) {
-  __shared__ float part[4][64];
+__global__ __launch_bounds__(64 * DB_GROUPS) void k_db_reduce(const float* __restrict__ dbpart,
+                                                              int mtiles, int cols, int ld,
+                                                              T* __restrict__ db,
+                                                              long long col_base) {
+  __shared__ float part[DB_GROUPS][64];
   const int lc = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int c = blockIdx.x * 64 + lc;
-  const int per = (mtiles + 3) / 4;
+  const int per = (mtiles + DB_GROUPS - 1) / DB_GROUPS;
   const int k1 = min(mtiles, (q + 1) * per);
   float s = 0.f;
-  if (c < cols)
+  if (c < cols) {
+#pragma unroll 8
     for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
+  }
   part[q][lc] = s;
   lds_barrier();
-  if (q == 0 && c < cols)
-    db[col_base + c] = Elem<T>::from_f32(((part[0][lc] + part[1][lc]) + part[2][lc]) + part[3][lc]);
+  if (q == 0 && c < cols) {
+    float t = part[0][lc];
+#pragma unroll
+    for (int g = 1; g < DB_GROUPS; ++g) t += part[g][lc];
+    db[col_base + c] = Elem<T>::from_f32(t);
+  }
 }
 
 // dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS);
@@ -1122,11 +1146,11 @@ __device__ __forceinline__ void gemm_big1(const bf16_t* __restrict__ A, long lon
 // halves and of the WGM wave rows are folded in a fixed order.  Selected
 // vocabulary rows are gathered into Zsel (class-major, K x M), 32 frames per
 // coalesced store.
-template <class C>
+template <class C, bool MASKED>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
     int M, int D, int V, const int* __restrict__ col2sel, float* __restrict__ Zsel,
-    double2* __restrict__ part, int nspan, int ftiles, int masked) {
+    double2* __restrict__ part, int nspan, int ftiles) {
   // One LDS object for everything: with a second one, the compiler makes
   // every fragment read wait for all outstanding global->LDS loads.
   constexpr int O_SEL = C::LDS_BYTES, O_BIAS = O_SEL + 2 * C::BM * 4;
@@ -1193,7 +1217,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
             const float z = acc[fi][fj][4 * q + e] + b4[e];
             // in the sum: every vocabulary row of the span, or (masked)
             // only the unselected ones
-            acc[fi][fj][4 * q + e] = (masked ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
+            acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
             if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
@@ -1477,9 +1501,14 @@ hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b
   const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
-  k_fwd_lse<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, V,
-                                             col2sel, Zsel, part, nspan, ftiles, vec, span0,
-                                             part_ld, masked);
+  if (masked)
+    k_fwd_lse<C, true><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D,
+                                                    V, col2sel, Zsel, part, nspan, ftiles, vec,
+                                                    span0, part_ld);
+  else
+    k_fwd_lse<C, false><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M,
+                                                     D, V, col2sel, Zsel, part, nspan, ftiles,
+                                                     vec, span0, part_ld);
   return hipGetLastError();
 }
 
@@ -1497,16 +1526,21 @@ hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* 
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
   if (grid == 0) return hipSuccess;
-  k_fwd_lse_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
-                                                 (const bf16_t*)b, M, D, V, col2sel, Zsel, part,
-                                                 nspan, ftiles, masked);
+  if (masked)
+    k_fwd_lse_big<C, true><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
+                                                        (const bf16_t*)b, M, D, V, col2sel, Zsel,
+                                                        part, nspan, ftiles);
+  else
+    k_fwd_lse_big<C, false><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
+                                                         (const bf16_t*)b, M, D, V, col2sel,
+                                                         Zsel, part, nspan, ftiles);
   return hipGetLastError();
 }
 
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan, double* lam,
                          float* lamf) {
   if (M == 0) return hipSuccess;
-  k_lambda<<<ceil_div(M, 256), 256, 0, st>>>(part, M, nspan, lam, lamf);
+  k_lambda<<<ceil_div((long long)M * LAM_LANES, 256), 256, 0, st>>>(part, M, nspan, lam, lamf);
   return hipGetLastError();
 }
 
@@ -1668,11 +1702,11 @@ hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int 
                             int ld, void* db, long long col_base) {
   if (cols == 0) return hipSuccess;
   if (dtype == 0)
-    k_db_reduce<float><<<ceil_div(cols, 64), 256, 0, st>>>(dbpart, mtiles, cols, ld, (float*)db,
-                                                           col_base);
+    k_db_reduce<float><<<ceil_div(cols, 64), 64 * DB_GROUPS, 0, st>>>(dbpart, mtiles, cols, ld,
+                                                                      (float*)db, col_base);
   else
-    k_db_reduce<bf16_t><<<ceil_div(cols, 64), 256, 0, st>>>(dbpart, mtiles, cols, ld,
-                                                            (bf16_t*)db, col_base);
+    k_db_reduce<bf16_t><<<ceil_div(cols, 64), 64 * DB_GROUPS, 0, st>>>(dbpart, mtiles, cols, ld,
+                                                                       (bf16_t*)db, col_base);
   return hipGetLastError();
 }
 

@@ -40,6 +40,8 @@ __device__ long long block_exclusive_scan(long long v, long long* total, long lo
 }
 
 // Per-utterance checks, repeat pairs, flags and prefix sums (one block).
+// The repeat pairs of one utterance are counted by one wavefront, its lanes
+// reading consecutive labels.
 __global__ __launch_bounds__(1024) void k_prepare_utts(
     int N, int M, long long L_tot, const int* __restrict__ tgt_off,
     const int* __restrict__ tgt, const int* __restrict__ frame_counts,
@@ -54,6 +56,26 @@ __global__ __launch_bounds__(1024) void k_prepare_utts(
     if (tgt_off[0] != 0 || (long long)tgt_off[N] != L_tot) s_err |= ERRBIT_TARGET;
   }
   __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int n = wid; n < N; n += nw) {
+    const int Tn = frame_counts[n];
+    const int a = tgt_off[n], e = tgt_off[n + 1];
+    const bool ok = a >= 0 && e >= a && (long long)e <= L_tot;
+    int r = 0;
+    if (ok)
+      for (int i = a + lane; i + 1 < e; i += 64) r += (tgt[i] == tgt[i + 1]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) r += __shfl_xor(r, o, 64);
+    if (lane == 0) {
+      if (!ok) atomicOr(&s_err, ERRBIT_TARGET);
+      if (Tn <= 0) atomicOr(&s_err, ERRBIT_LENGTHS);
+      const int L = ok ? e - a : 0;
+      flags[n] = (Tn > 0 && ok && L + r <= Tn) ? 1 : 0;
+      atomicMax(&s_maxL, L);
+      atomicMax(&s_maxT, Tn);
+    }
+  }
+  __syncthreads();
   long long rows = 0, dps = 0;
   for (int base = 0; base < N; base += blockDim.x) {
     const int n = base + threadIdx.x;
@@ -62,17 +84,9 @@ __global__ __launch_bounds__(1024) void k_prepare_utts(
       const int Tn = frame_counts[n];
       const int a = tgt_off[n], e = tgt_off[n + 1];
       const bool ok = a >= 0 && e >= a && (long long)e <= L_tot;
-      if (!ok) atomicOr(&s_err, ERRBIT_TARGET);
-      if (Tn <= 0) atomicOr(&s_err, ERRBIT_LENGTHS);
       const int L = ok ? e - a : 0;
-      int r = 0;
-      if (ok)
-        for (int i = a; i + 1 < e; ++i) r += (tgt[i] == tgt[i + 1]);
-      flags[n] = (Tn > 0 && ok && L + r <= Tn) ? 1 : 0;
       T = Tn > 0 ? Tn : 0;
       dp = T * (2LL * L + 1);
-      atomicMax(&s_maxL, L);
-      atomicMax(&s_maxT, Tn);
     }
     long long tot;
     const long long ex = block_exclusive_scan(T, &tot, sm);
@@ -116,27 +130,42 @@ __global__ void k_mark_labels(long long L_tot, const int* __restrict__ tgt, int 
 
 // Compaction of the marks into U (blank first, then ascending ids) and the
 // column -> selected-index map (-1 for unselected columns).  One block; each
-// thread owns a contiguous id range so the order is the id order.
+// wavefront owns a contiguous id range (a multiple of 64 ids) and walks it 64
+// consecutive ids at a time, ranking the marked ones with a ballot, so the
+// order is the id order.
 __global__ __launch_bounds__(1024) void k_select(int V, int blank, int* __restrict__ col2sel,
                                                  int* __restrict__ U, Meta* __restrict__ meta) {
   __shared__ long long sm[32];
-  const int per = (V + blockDim.x - 1) / blockDim.x;
-  const int lo = min(V, (int)threadIdx.x * per), hi = min(V, lo + per);
-  long long cnt = 0;
-  for (int v = lo; v < hi; ++v) cnt += (v != blank && col2sel[v] != 0);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int per = ((V + nw - 1) / nw + 63) / 64 * 64;
+  const int lo = min(V, wid * per), hi = min(V, lo + per);
+  int cnt = 0;  // marked ids of this wavefront's range (wave-uniform)
+  for (int v0 = lo; v0 < hi; v0 += 64) {
+    const int v = v0 + lane;
+    cnt += __popcll(__ballot(v < hi && v != blank && col2sel[v] != 0));
+  }
   long long tot;
-  const long long ex = block_exclusive_scan(cnt, &tot, sm);
-  int idx = 1 + (int)ex;
-  for (int v = lo; v < hi; ++v) {
-    if (v == blank) {
-      col2sel[v] = 0;
-    } else if (col2sel[v] != 0) {
-      col2sel[v] = idx;
-      U[idx] = v;
-      ++idx;
-    } else {
-      col2sel[v] = -1;
+  // lane 0 carries the wavefront's count: its exclusive prefix is the number
+  // of marked ids in the ranges of the lower wavefronts
+  const long long ex = block_exclusive_scan(lane == 0 ? cnt : 0, &tot, sm);
+  int idx = 1 + (int)__shfl(ex, 0, 64);
+  for (int v0 = lo; v0 < hi; v0 += 64) {
+    const int v = v0 + lane;
+    const bool in = v < hi;
+    const bool sel = in && v != blank && col2sel[v] != 0;
+    const unsigned long long bal = __ballot(sel);
+    const int pos = idx + __popcll(bal & ((1ull << lane) - 1ull));
+    if (in) {
+      if (v == blank) {
+        col2sel[v] = 0;
+      } else if (sel) {
+        col2sel[v] = pos;
+        U[pos] = v;
+      } else {
+        col2sel[v] = -1;
+      }
     }
+    idx += __popcll(bal);
   }
   if (threadIdx.x == 0) {
     U[0] = blank;
