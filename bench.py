@@ -39,6 +39,27 @@ GEMM_KERNELS = ("fwd_gemm_lse", "bwd_recompute_dz", "dx_gemm", "dw_gemm")
 # value (alpha, beta: 2 x 8 B) and reads one fp32 emission (2 x 4 B).
 DP_KERNEL = "ctc_alpha_beta"
 DP_BYTES_PER_STATE = 24
+# Memory-bound passes beside the GEMMs, with their algorithmic bytes per step:
+#   ctc_alpha_beta  24 B per (frame, extended-label state), as above;
+#   lambda          the M x ceil(V / 2048) FP64 (max, sum) span partials read
+#                   (16 B each), lambda written in FP64 and fp32 (12 B/frame);
+#   scores          Zsel read and S written in place (K x M fp32 each), lambda
+#                   read (8 B/frame);
+#   occupancy       alpha and beta read (16 B/state), S read (4 B/state), the
+#                   occupancy written (4 B/state), g written (8 B/frame).
+LSE_SPAN = 2048
+
+
+def pass_bytes(bt, K):
+    L = np.diff(bt.tgt_off).astype(np.int64)
+    states = int(np.sum(bt.frame_counts.astype(np.int64) * (2 * L + 1)))
+    nspan = (bt.V + LSE_SPAN - 1) // LSE_SPAN
+    return {
+        DP_KERNEL: DP_BYTES_PER_STATE * states,
+        "lambda": bt.M * (16 * nspan + 12),
+        "scores": bt.M * (8 * K + 8),
+        "occupancy": 24 * states + 8 * bt.M,
+    }
 
 
 def parse():
@@ -181,6 +202,14 @@ def main():
                 "traffic": None}
     kernels = {k: {"ms_per_step": v[0] / args.steps, "launches_per_step": v[1] / args.steps}
                for k, v in prof.items() if v[1]}
+    # achieved HBM rate of the DP and normalizer passes (event time per step)
+    hbm_passes = {}
+    for k, nbytes in pass_bytes(bt, info["K"]).items():
+        if k in prof and prof[k][1]:
+            sec = prof[k][0] / 1e3 / args.steps
+            hbm_passes[k] = {"bytes_per_step": nbytes, "ms_per_step": 1e3 * sec,
+                             "achieved_GBps": nbytes / sec / 1e9,
+                             "frac": nbytes / sec / HBM_PEAK}
     out = {
         "metric": "frames/s fused head+CTC fwd+bwd (V=180k,M=16k,D=512); % MFMA peak",
         "value": frames_per_s,
@@ -202,6 +231,7 @@ def main():
         "workspace_GiB": info["workspace_bytes"] / 2**30,
         "roofline": dict(kernel=dom, **roof),
         "kernels": kernels,
+        "hbm_passes": hbm_passes,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(bt, args.cpu_sample_utts)
