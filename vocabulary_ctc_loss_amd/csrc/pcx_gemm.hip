@@ -640,6 +640,96 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 // recompute epilogue lets every lane handle its own selected columns instead
 // of sharing each selected column among all 64 lanes.
 constexpr int SEL_DENSE = 8;
+constexpr int SEL_PRE_BIG = 6;
+
+// Selected columns of one wavefront's tile block for the cooperative pass
+// (at most SEL_DENSE of them), in (fragment column, lane) order, with the S
+// and Gamma values of the wavefront's rows (WM / 64 per lane).  They do not
+// depend on the product, so they are loaded before it and their latency
+// hides behind the matrix work.  n > SEL_DENSE: the dense pass runs instead.
+template <class C>
+struct SelPre {
+  static constexpr int RPL = C::WM / 64;
+  int n;
+  int sel[SEL_DENSE], col[SEL_DENSE];
+  float s[SEL_DENSE][RPL], g[SEL_DENSE][RPL];
+};
+
+// s_sel[c]: selected index of tile column c (or -1); columns at or past c1
+// are never selected.
+template <class C>
+__device__ __forceinline__ void sel_prefetch(SelPre<C>& p, const int* s_sel, int n0, int c1,
+                                             int m0, int M, const float* __restrict__ S,
+                                             const float* __restrict__ Gam) {
+  static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
+  unsigned long long mk[C::FN];
+  int cs[C::FN];
+  int total = 0;
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    const int col = acc_col<C>(fj);
+    cs[fj] = s_sel[col];
+    mk[fj] = __ballot(lane < 32 && n0 + col < c1 && cs[fj] >= 0);
+    total += __popcll(mk[fj]);
+  }
+  p.n = total;
+  if (total > SEL_DENSE) return;
+#pragma unroll
+  for (int k = 0; k < SEL_DENSE; ++k) {
+    int sel = 0, col = 0;
+    bool found = false;
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      if (!found && mk[fj] != 0ull) {
+        const int src = __ffsll((long long)mk[fj]) - 1;
+        mk[fj] &= mk[fj] - 1;
+        sel = __builtin_amdgcn_readlane(cs[fj], src);
+        col = wn * C::WN + fj * 32 + src;
+        found = true;
+      }
+    }
+    p.sel[k] = sel;
+    p.col[k] = col;
+#pragma unroll
+    for (int t = 0; t < SelPre<C>::RPL; ++t) {
+      const int row = wm * C::WM + SelPre<C>::RPL * lane + t;
+      const bool ok = found && m0 + row < M;
+      p.s[k][t] = ok ? S[(long long)sel * M + m0 + row] : 0.f;
+      p.g[k][t] = ok ? Gam[(long long)sel * M + m0 + row] : 0.f;
+    }
+  }
+}
+
+// dZ of the prefetched selected columns, grad (g_m exp(S) - Gamma) formed in
+// FP64 and rounded once; each column's sum over the wavefront's rows (a
+// fixed-order wave sum) goes to s_db_w[column].
+template <class C, typename T>
+__device__ __forceinline__ void sel_finish(const SelPre<C>& p, const double* s_g, int m0, int M,
+                                           int n0, int c0, double grad, T* __restrict__ dZ,
+                                           int ldz, float* s_db_w) {
+  const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / C::WGN;
+#pragma unroll
+  for (int k = 0; k < SEL_DENSE; ++k) {
+    if (k < p.n) {
+      float sum = 0.f;
+#pragma unroll
+      for (int t = 0; t < SelPre<C>::RPL; ++t) {
+        const int row = wm * C::WM + SelPre<C>::RPL * lane + t;
+        if (m0 + row < M) {
+          // S <= 0 (a log-probability)
+          const float dz =
+              (float)(grad * (s_g[row] * exp_nonpos((double)p.s[k][t]) - (double)p.g[k][t]));
+          dZ[(long long)(m0 + row) * ldz + (n0 + p.col[k] - c0)] = Elem<T>::from_f32(dz);
+          sum += dz;
+        }
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+      if (lane == 0) s_db_w[p.col[k]] = sum;
+    }
+  }
+}
 
 // Recompute one BM x BN tile of chunk logits and form the logit gradient
 //   v not selected:  dZ = (grad g_m) * exp(z - fp32(lambda_m)), evaluated in
@@ -686,6 +776,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
     s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
   }
+  lds_barrier();
+  SelPre<C> pre;
+  sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam);
   f32x16 acc[C::FM][C::FN];
   gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
@@ -730,10 +823,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   // With few of them in this wavefront (the large-vocabulary case) each is
   // done by all 64 lanes in the pass further down; with many, every lane
   // does its own here.
-  int nsel = 0;
-#pragma unroll
-  for (int fj = 0; fj < C::FN; ++fj) nsel += __popcll(__ballot(lane < 32 && crole[fj] == 2));
-  const bool dense = nsel > SEL_DENSE;
+  const bool dense = pre.n > SEL_DENSE;
   if (dense) {
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
@@ -762,37 +852,9 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     cs[fj] += __shfl_xor(cs[fj], 32, 64);
     if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
   }
-  // Few selected classes: each selected column of this wavefront by all 64
-  // lanes (WM / 64 of the wavefront's rows each); the column sum is a
-  // fixed-order wave sum.
-  constexpr int RPL = C::WM / 64;
-#pragma unroll
-  for (int fj = 0; fj < C::FN; ++fj) {
-    unsigned long long todo = dense ? 0ull : __ballot(lane < 32 && crole[fj] == 2);
-    while (todo) {
-      const int src = __ffsll((long long)todo) - 1;
-      todo &= todo - 1;
-      const int sel = __shfl(csel[fj], src, 64);
-      const int col = (w % C::WGN) * C::WN + fj * 32 + src;
-      const float* Sp = S + (long long)sel * M + m0;
-      const float* Gp = Gam + (long long)sel * M + m0;
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < RPL; ++t) {
-        const int row = wm * C::WM + RPL * lane + t;
-        if (m0 + row < M) {
-          // S <= 0 (a log-probability)
-          const float dz =
-              (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
-          dZ[(long long)(m0 + row) * ldz + (n0 + col - c0)] = Elem<T>::from_f32(dz);
-          sum += dz;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      if (lane == 0) s_db[wm][col] = sum;
-    }
-  }
+  // Few selected classes: each prefetched column of this wavefront by all 64
+  // lanes (WM / 64 of the wavefront's rows each).
+  if (!dense) sel_finish<C, T>(pre, s_g, m0, M, n0, c0, grad, dZ, ldz, s_db[wm]);
   lds_barrier();
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
@@ -1008,6 +1070,24 @@ __device__ __forceinline__ void big_stage(const bf16_t* __restrict__ G, long lon
 // Barrier of the big core: this wave's LDS reads are complete and at most N
 // of its global memory operations are in flight, then all waves meet.  (A
 // release fence would also wait for every outstanding global->LDS load.)
+// Two fp32 values rounded to nearest-even bf16 by the hardware conversion,
+// packed low (lo) / high (hi).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b16x2 __attribute__((ext_vector_type(2)));
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b16x2));
+}
+
+// Value of lane l ^ 1 (DPP quad permutation 1,0,3,2) and of lane l ^ 2
+// (2,3,0,1).
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t lane_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+}
+
 template <int N>
 __device__ __forceinline__ void big_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -1275,10 +1355,18 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const float* __restrict__ lamu) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
-  // one LDS object (see k_fwd_lse_big)
+  static_assert(C::WM == 64, "selected-class pass: one row per lane");
+  // one LDS object (see k_fwd_lse_big): the operand stages, then the row and
+  // column data, then per wavefront the S and Gamma values (64 rows each) of
+  // up to SEL_PRE_BIG selected columns.  After the product the stage buffers
+  // hold the selected-class values on their way to the accumulators (from
+  // offset 0) and the column sums (from O_DB).
   constexpr int O_G = C::LDS_BYTES, O_SEL = O_G + BM * 8, O_BIAS = O_SEL + BN * 4;
-  constexpr int O_LAM = O_BIAS + BN * 4, O_RS = O_LAM + BM * 4, O_DB = O_RS + BM * 4;
-  __shared__ __attribute__((aligned(16))) char smem[O_DB + C::WGM * BN * 4];
+  constexpr int O_LAM = O_BIAS + BN * 4, O_RS = O_LAM + BM * 4, O_PRE = O_RS + BM * 4;
+  constexpr int O_DB = C::LDS_BYTES / 2;
+  static_assert(C::WAVES * SEL_DENSE * (C::WM + 1) * 4 <= O_DB &&
+                    O_DB + C::WGM * BN * 4 <= C::LDS_BYTES, "post-product LDS use");
+  __shared__ __attribute__((aligned(16))) char smem[O_PRE + C::WAVES * SEL_PRE_BIG * 512];
   double* s_g = reinterpret_cast<double*>(smem + O_G);
   int* s_sel = reinterpret_cast<int*>(smem + O_SEL);
   float* s_bias = reinterpret_cast<float*>(smem + O_BIAS);
@@ -1303,9 +1391,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
     s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
   }
+  lds_barrier();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  // Selected columns of this wavefront, in (fragment column, lane) order; with
+  // at most SEL_PRE_BIG of them their S and Gamma values are loaded straight
+  // into LDS now, behind the product (they do not depend on it).
+  int pn, pcol[SEL_PRE_BIG];
+  {
+    unsigned long long mk[C::FN];
+    int cs_[C::FN];
+    pn = 0;
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      const int col = acc_col<C>(fj);
+      cs_[fj] = s_sel[col];
+      mk[fj] = __ballot(lane < 32 && n0 + col < c1 && cs_[fj] >= 0);
+      pn += __popcll(mk[fj]);
+    }
+    const int grow = min(m0 + wm * C::WM + lane, M - 1);
+#pragma unroll
+    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+      int sel = 0, col = 0;
+      bool found = false;
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj) {
+        if (!found && mk[fj] != 0ull) {
+          const int src = __ffsll((long long)mk[fj]) - 1;
+          mk[fj] &= mk[fj] - 1;
+          sel = __builtin_amdgcn_readlane(cs_[fj], src);
+          col = (w % C::WGN) * C::WN + fj * 32 + src;
+          found = true;
+        }
+      }
+      pcol[k] = col;
+      if (found && pn <= SEL_PRE_BIG) {
+        char* dst = smem + O_PRE + (w * SEL_PRE_BIG + k) * 512;
+        __builtin_amdgcn_global_load_lds((const void*)(S + (long long)sel * M + grow),
+                                         PCX_LDS_PTR(dst), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds((const void*)(Gam + (long long)sel * M + grow),
+                                         PCX_LDS_PTR(dst + 256), 4, 0, 0);
+      }
+    }
+  }
   f32x16 acc[C::FM][C::FN];
   gemm_big1<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   const bool rows_full = m0 + BM <= M;
   // Column roles: 0 = unselected class (formula below), 1 = padding up to
   // the next multiple of 64 (zero), 2 = selected class or past the padding
@@ -1321,7 +1450,33 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     crole[fj] = v < c1 ? (csel[fj] < 0 ? 0 : 2) : (v < c_pad ? 1 : 2);
     cs[fj] = 0.f;
   }
-  // Unselected classes: every lane its own accumulators, four rows at a time.
+  // Few selected classes (at most SEL_PRE_BIG in this wavefront): each
+  // column by all 64 lanes (one of the wavefront's rows each), in FP64 and
+  // rounded once, into LDS (one region per wavefront) with the column's sum
+  // over the wavefront's rows (a fixed-order wave sum) ...
+  const bool dense = pn > SEL_PRE_BIG;
+  float* tmp = reinterpret_cast<float*>(smem) + w * (SEL_DENSE * (C::WM + 1));
+  if (!dense && pn > 0) {
+    const int row = wm * C::WM + lane;
+#pragma unroll
+    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+      if (k < pn) {
+        const float* pv = reinterpret_cast<const float*>(smem + O_PRE +
+                                                         (w * SEL_PRE_BIG + k) * 512);
+        float sum = 0.f, dz = 0.f;
+        if (m0 + row < M) {
+          // S <= 0 (a log-probability)
+          dz = (float)(grad * (s_g[row] * exp_nonpos((double)pv[lane]) - (double)pv[64 + lane]));
+          sum = dz;
+        }
+        tmp[k * C::WM + lane] = dz;
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
+        if (lane == 0) tmp[SEL_DENSE * C::WM + k] = sum;
+      }
+    }
+  }
+  // Unselected classes, in place of the accumulators (padding columns 0).
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi) {
 #pragma unroll
@@ -1331,31 +1486,97 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(s_lam2 + row0);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = row0 + e;
-        const bool in = rows_full || m0 + row < M;
+        const bool in = rows_full || m0 + row0 + e < M;
 #pragma unroll
         for (int fj = 0; fj < C::FN; ++fj) {
           float dz =
               rs4[e] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
           if (crole[fj] == 1) dz = 0.f;
-          if (in && crole[fj] != 2) {
-            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = f32_to_bf16(dz);
-            cs[fj] += dz;
-          }
+          acc[fi][fj][4 * q + e] = dz;
+          if (in && crole[fj] != 2) cs[fj] += dz;
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (!dense) {
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj) {
+      cs[fj] += __shfl_xor(cs[fj], 32, 64);
+      if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
+    }
+  }
+  // ... and into the accumulators of the lanes that own the selected columns;
+  // their column sums overwrite the ones just written (later writes of this
+  // wavefront to the same LDS word take effect after earlier ones).
+  if (!dense && pn > 0) {
+    const int h = lane >> 5;
+#pragma unroll
+    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+      if (k < pn) {
+        const int cw = pcol[k] - (w % C::WGN) * C::WN;
+        const bool own = (lane & 31) == (cw & 31);
+#pragma unroll
+        for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v4 =
+                *reinterpret_cast<const f32x4*>(tmp + k * C::WM + fi * 32 + 8 * q + 4 * h);
+#pragma unroll
+            for (int fj = 0; fj < C::FN; ++fj) {
+              const bool take = own && fj == (cw >> 5);
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                acc[fi][fj][4 * q + e] = take ? v4[e] : acc[fi][fj][4 * q + e];
+            }
+          }
+        if (lane == 0) s_db[wm][pcol[k]] = tmp[SEL_DENSE * C::WM + k];
+      }
+    }
+  }
+  // Stores of four consecutive columns (8 bytes) per lane: a lane holds four
+  // rows of one column, so lanes l, l ^ 1 and then l, l ^ 2 trade values until
+  // lane l holds row (l & 3) of the group for columns (l & ~3) .. (l & ~3) + 3.
+  // With many selected classes (dense pass below) their columns are written
+  // here with the unselected formula and overwritten by that pass, from the
+  // same wavefront.
+  {
+    const int odd = lane & 1, b1 = (lane >> 1) & 1;
+#pragma unroll
+    for (int fi = 0; fi < C::FM; ++fi) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = acc_row<C>(fi, 4 * q) + (lane & 3);
+        const bool rin = rows_full || m0 + row < M;
+#pragma unroll
+        for (int fj = 0; fj < C::FN; ++fj) {
+          const float v[4] = {acc[fi][fj][4 * q], acc[fi][fj][4 * q + 1], acc[fi][fj][4 * q + 2],
+                              acc[fi][fj][4 * q + 3]};
+          const float r01 = __uint_as_float(lane_xor1(__float_as_uint(odd ? v[0] : v[1])));
+          const float r23 = __uint_as_float(lane_xor1(__float_as_uint(odd ? v[2] : v[3])));
+          // even lanes: rows 0 / 2 of columns (l, l + 1); odd: rows 1 / 3 of (l - 1, l)
+          const uint32_t p0 = odd ? pack_bf16x2(r01, v[1]) : pack_bf16x2(v[0], r01);
+          const uint32_t p1 = odd ? pack_bf16x2(r23, v[3]) : pack_bf16x2(v[2], r23);
+          const uint32_t r = lane_xor2(b1 ? p0 : p1);
+          const uint2 out = b1 ? make_uint2(r, p1) : make_uint2(p0, r);
+          const int col = acc_col<C>(fj) & ~3;
+          if (rin && n0 + col < c_pad)
+            *reinterpret_cast<uint2*>(dZ + (long long)(m0 + row) * ldz + (n0 + col - c0)) = out;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
   // Selected classes: dZ needs no recomputed logit, only S, Gamma and g.
   // With few of them in this wavefront (the large-vocabulary case) each is
   // done by all 64 lanes in the pass further down; with many, every lane
   // does its own here.
-  int nsel = 0;
-#pragma unroll
-  for (int fj = 0; fj < C::FN; ++fj)
-    nsel += __popcll(__ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0));
-  const bool dense = nsel > SEL_DENSE;
+  // The dense pass's stores must land after this wavefront's packed stores
+  // to the same addresses: wait until those are acknowledged.
+  if (dense) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+    __builtin_amdgcn_sched_barrier(0);
+  }
   if (dense) {
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
@@ -1379,42 +1600,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       }
     }
   }
+  if (dense) {
 #pragma unroll
-  for (int fj = 0; fj < C::FN; ++fj) {
-    cs[fj] += __shfl_xor(cs[fj], 32, 64);
-    if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
-  }
-  // Few selected classes: each selected column of this wavefront by all 64
-  // lanes (WM / 64 of the wavefront's rows each); the column sum is a
-  // fixed-order wave sum.
-  static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
-  constexpr int RPL = C::WM / 64;
-#pragma unroll
-  for (int fj = 0; fj < C::FN; ++fj) {
-    unsigned long long todo =
-        dense ? 0ull : __ballot(lane < 32 && crole[fj] == 2 && csel[fj] >= 0);
-    while (todo) {
-      const int src = __ffsll((long long)todo) - 1;
-      todo &= todo - 1;
-      const int sel = __shfl(csel[fj], src, 64);
-      const int col = (w % C::WGN) * C::WN + fj * 32 + src;
-      const float* Sp = S + (long long)sel * M + m0;
-      const float* Gp = Gam + (long long)sel * M + m0;
-      float sum = 0.f;
-#pragma unroll
-      for (int t = 0; t < RPL; ++t) {
-        const int row = wm * C::WM + RPL * lane + t;
-        if (m0 + row < M) {
-          // S <= 0 (a log-probability)
-          const float dz =
-              (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
-          dZ[(long long)(m0 + row) * ldz + (n0 + col - c0)] = f32_to_bf16(dz);
-          sum += dz;
-        }
-      }
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-      if (lane == 0) s_db[wm][col] = sum;
+    for (int fj = 0; fj < C::FN; ++fj) {
+      cs[fj] += __shfl_xor(cs[fj], 32, 64);
+      if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
     }
   }
   lds_barrier();
