@@ -217,6 +217,11 @@ pcx_status pcx_get_other(pcx_ctx* ctx, double* out, int64_t capacity);
  * Off by default; enabling adds two event records per launch.
  */
 pcx_status pcx_profile_enable(pcx_ctx* ctx, int32_t on);
+/* Restrict the timing to the kernel families whose bit is set in `mask`
+ * (bit i: family i; all families by default).  Each timed launch adds two
+ * event records to the stream, so timing one family perturbs a run far less
+ * than timing all of them. */
+pcx_status pcx_profile_mask(pcx_ctx* ctx, uint32_t mask);
 pcx_status pcx_profile_reset(pcx_ctx* ctx);
 int32_t pcx_profile_count(void);
 pcx_status pcx_profile_read(pcx_ctx* ctx, int32_t i, const char** name,

@@ -105,6 +105,8 @@ def test_profile_api_without_device(lib):
         assert lib.pcx_profile_read(h, 1, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(n)) == 0
         assert name.value == b"fwd_gemm_lse" and n.value == 0
         assert lib.pcx_profile_read(h, 999, None, None, None) == 1
+        assert lib.pcx_profile_mask(h, 1 << 1) == 0
+        assert lib.pcx_profile_mask(None, 0) == 1
     finally:
         lib.pcx_destroy(h)
 

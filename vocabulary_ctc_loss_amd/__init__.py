@@ -162,6 +162,16 @@ class Context:
     def profile_enable(self, on: bool = True):
         check(self._lib.pcx_profile_enable(self._h, 1 if on else 0))
 
+    def profile_mask(self, names=None):
+        """Time only the kernel families named (all of them for None)."""
+        mask = 0xFFFFFFFF
+        if names is not None:
+            mask = 0
+            all_names = list(self.profile_read())
+            for n in names:
+                mask |= 1 << all_names.index(n)
+        check(self._lib.pcx_profile_mask(self._h, mask))
+
     def profile_reset(self):
         check(self._lib.pcx_profile_reset(self._h))
 

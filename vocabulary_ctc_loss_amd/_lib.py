@@ -48,6 +48,7 @@ SIGNATURES = {
     "pcx_get_occupancy": (_I32, [_P, _P, _I64]),
     "pcx_get_other": (_I32, [_P, _P, _I64]),
     "pcx_profile_enable": (_I32, [_P, _I32]),
+    "pcx_profile_mask": (_I32, [_P, ctypes.c_uint32]),
     "pcx_profile_reset": (_I32, [_P]),
     "pcx_profile_count": (_I32, []),
     "pcx_profile_read": (_I32, [_P, _I32, ctypes.POINTER(ctypes.c_char_p),

@@ -81,6 +81,7 @@ struct pcx_ctx {
   int nspan = 0;
   // profiling
   bool prof = false;
+  uint32_t prof_mask = 0xFFFFFFFFu;  // bit i: kernel family i is timed
   std::vector<Pending> pending;
   std::vector<hipEvent_t> pool;
   double prof_ms[K_COUNT] = {0};
@@ -152,7 +153,7 @@ struct Timed {
   hipStream_t st;
   hipEvent_t a = nullptr;
   Timed(pcx_ctx* c_, int kid_, hipStream_t st_) : c(c_), kid(kid_), st(st_) {
-    if (c->prof) {
+    if (c->prof && ((c->prof_mask >> kid) & 1u)) {
       a = take_event(c);
       if (a) (void)hipEventRecord(a, st);
     }
@@ -549,6 +550,12 @@ pcx_status pcx_set_formulation(pcx_ctx* ctx, int32_t form) {
 pcx_status pcx_profile_enable(pcx_ctx* ctx, int32_t on) {
   if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
   ctx->prof = on != 0;
+  return PCX_OK;
+}
+
+pcx_status pcx_profile_mask(pcx_ctx* ctx, uint32_t mask) {
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  ctx->prof_mask = mask;
   return PCX_OK;
 }
 
