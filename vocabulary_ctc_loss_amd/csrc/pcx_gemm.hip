@@ -1635,28 +1635,50 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
   const int m0 = mt * C::BM, n0 = nt * C::BN;
   f32x16 acc[C::FM][C::FN];
   gemm_big1<C>(dZ, ldz, m0, M, Wt, ldz, n0, D, Kp, acc, smem);
-  // Read-modify-write of the fp32 accumulator, one block of 16 rows at a
-  // time with all of the block's loads issued before its stores (in program
-  // order: the compiler cannot tell the addresses apart).
+  // Read-modify-write of the fp32 accumulator with 16-byte accesses: a lane
+  // holds four rows of one column, so lanes l, l ^ 1 and then l, l ^ 2 trade
+  // values until lane l holds row (l & 3) of each four-row group for the
+  // columns (l & ~3) .. (l & ~3) + 3; eight lanes then cover 128 contiguous
+  // bytes of a row.  One fragment row block at a time, its loads issued
+  // before its stores.
+  const int lane = threadIdx.x & 63, odd = lane & 1, b1 = (lane >> 1) & 1;
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi) {
-    float old[C::FN][16];
+    f32x4 val[C::FN][4], old[C::FN][4];
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const f32x16& a = acc[fi][fj];
+        const float r0 = __uint_as_float(lane_xor1(__float_as_uint(odd ? a[4 * q] : a[4 * q + 1])));
+        const float r2 =
+            __uint_as_float(lane_xor1(__float_as_uint(odd ? a[4 * q + 2] : a[4 * q + 3])));
+        // row (odd) and row (2 + odd) of columns (l & ~1), (l & ~1) + 1
+        const float p0 = odd ? r0 : a[4 * q], p1 = odd ? a[4 * q + 1] : r0;
+        const float c0 = odd ? r2 : a[4 * q + 2], c1 = odd ? a[4 * q + 3] : r2;
+        const float t0 = __uint_as_float(lane_xor2(__float_as_uint(b1 ? p0 : c0)));
+        const float t1 = __uint_as_float(lane_xor2(__float_as_uint(b1 ? p1 : c1)));
+        val[fj][q] = b1 ? f32x4{t0, t1, c0, c1} : f32x4{p0, p1, t0, t1};
+      }
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
-      const int col = n0 + acc_col<C>(fj);
+      const int col = n0 + (acc_col<C>(fj) & ~3);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = m0 + acc_row<C>(fi, rr);
-        old[fj][rr] = (!first && row < M && col < D) ? dXacc[(long long)row * D + col] : 0.f;
+      for (int q = 0; q < 4; ++q) {
+        const int row = m0 + acc_row<C>(fi, 4 * q) + (lane & 3);
+        old[fj][q] = (!first && row < M && col < D)
+                         ? *reinterpret_cast<const f32x4*>(dXacc + (long long)row * D + col)
+                         : f32x4{0.f, 0.f, 0.f, 0.f};
       }
     }
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
-      const int col = n0 + acc_col<C>(fj);
+      const int col = n0 + (acc_col<C>(fj) & ~3);
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int row = m0 + acc_row<C>(fi, rr);
-        if (row < M && col < D) dXacc[(long long)row * D + col] = old[fj][rr] + acc[fi][fj][rr];
+      for (int q = 0; q < 4; ++q) {
+        const int row = m0 + acc_row<C>(fi, 4 * q) + (lane & 3);
+        if (row < M && col < D)
+          *reinterpret_cast<f32x4*>(dXacc + (long long)row * D + col) = old[fj][q] + val[fj][q];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
