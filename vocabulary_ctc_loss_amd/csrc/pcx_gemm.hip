@@ -1476,7 +1476,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       }
     }
   }
-  // Unselected classes, in place of the accumulators (padding columns 0).
+  // Unselected classes, in place of the accumulators.  Padding columns get
+  // the bias -inf, so their value is exp2(-inf) = 0.  The column sums take
+  // every column; those of selected columns are replaced further down.
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj)
+    if (crole[fj] == 1) cbv[fj] = -INFINITY;
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi) {
 #pragma unroll
@@ -1489,11 +1494,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         const bool in = rows_full || m0 + row0 + e < M;
 #pragma unroll
         for (int fj = 0; fj < C::FN; ++fj) {
-          float dz =
-              rs4[e] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
-          if (crole[fj] == 1) dz = 0.f;
+          const float dz = rs4[e] * __builtin_amdgcn_exp2f(
+                                        fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
           acc[fi][fj][4 * q + e] = dz;
-          if (in && crole[fj] != 2) cs[fj] += dz;
+          cs[fj] += in ? dz : 0.f;
         }
       }
     }
@@ -1516,19 +1520,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         const int cw = pcol[k] - (w % C::WGN) * C::WN;
         const bool own = (lane & 31) == (cw & 31);
 #pragma unroll
-        for (int fi = 0; fi < C::FM; ++fi)
+        for (int fj = 0; fj < C::FN; ++fj) {
+          if (fj != (cw >> 5)) continue;  // the same for the whole wavefront
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const f32x4 v4 =
-                *reinterpret_cast<const f32x4*>(tmp + k * C::WM + fi * 32 + 8 * q + 4 * h);
+          for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
-            for (int fj = 0; fj < C::FN; ++fj) {
-              const bool take = own && fj == (cw >> 5);
+            for (int q = 0; q < 4; ++q) {
+              const f32x4 v4 =
+                  *reinterpret_cast<const f32x4*>(tmp + k * C::WM + fi * 32 + 8 * q + 4 * h);
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                acc[fi][fj][4 * q + e] = take ? v4[e] : acc[fi][fj][4 * q + e];
+                acc[fi][fj][4 * q + e] = own ? v4[e] : acc[fi][fj][4 * q + e];
             }
-          }
+        }
         if (lane == 0) s_db[wm][pcol[k]] = tmp[SEL_DENSE * C::WM + k];
       }
     }
@@ -1573,6 +1577,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   // The dense pass's stores must land after this wavefront's packed stores
   // to the same addresses: wait until those are acknowledged.
   if (dense) {
+#pragma unroll
+    for (int fj = 0; fj < C::FN; ++fj)
+      if (crole[fj] == 2) cs[fj] = 0.f;
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
     __builtin_amdgcn_sched_barrier(0);
