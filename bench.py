@@ -43,19 +43,15 @@ DP_KERNEL = "ctc_alpha_beta"
 DP_BYTES_PER_STATE = 24
 # Memory-bound passes beside the GEMMs, with their algorithmic bytes per step:
 #   ctc_alpha_beta  24 B per (frame, extended-label state), as above;
-#   lambda          the M x ceil(V / 2048) FP64 (max, sum) span partials read
+#   lambda          the M x (vocabulary spans) FP64 (max, sum) partials read
 #                   (16 B each), lambda written in FP64 and fp32 (12 B/frame);
 #   scores          Zsel read and S written in place (K x M fp32 each), lambda
 #                   read (8 B/frame);
 #   occupancy       alpha and beta read (16 B/state), S read (4 B/state), the
 #                   occupancy written (4 B/state), g written (8 B/frame).
-LSE_SPAN = 2048
-
-
-def pass_bytes(bt, K):
+def pass_bytes(bt, K, nspan):
     L = np.diff(bt.tgt_off).astype(np.int64)
     states = int(np.sum(bt.frame_counts.astype(np.int64) * (2 * L + 1)))
-    nspan = (bt.V + LSE_SPAN - 1) // LSE_SPAN
     return {
         DP_KERNEL: DP_BYTES_PER_STATE * states,
         "lambda": bt.M * (16 * nspan + 12),
@@ -217,7 +213,7 @@ def main():
                for k, v in breakdown.items() if v[1]}
     # achieved HBM rate of the DP and normalizer passes (same step)
     hbm_passes = {}
-    for k, nbytes in pass_bytes(bt, info["K"]).items():
+    for k, nbytes in pass_bytes(bt, info["K"], info["lse_spans"]).items():
         if k in breakdown and breakdown[k][1]:
             sec = breakdown[k][0] / 1e3
             hbm_passes[k] = {"bytes_per_step": nbytes, "ms_per_step": 1e3 * sec,

@@ -82,6 +82,7 @@ typedef struct {
   int32_t n_nonfinite;     /* alignable utterances whose loss was not finite */
   int32_t max_target_len;  /* longest target in the batch                   */
   uint64_t workspace_bytes;/* device bytes the context holds after the call */
+  int32_t lse_spans;       /* vocabulary spans of the forward normalizer fold */
 } pcx_fwd_info;
 
 /* Create / destroy a context.  The context owns its device workspace, which
@@ -103,7 +104,7 @@ void pcx_destroy(pcx_ctx* ctx);
  *   dtype         PCX_F32 or PCX_BF16 (the element type of X, W and b), or
  *                 PCX_F32_BF16W (X fp32, W and b bf16; the projections run in
  *                 fp32 on W widened chunk by chunk, C rows at a time in the
- *                 backward pass and whole 2048-row spans in the forward).
+ *                 backward pass and whole normalizer spans in the forward).
  *   M, D, V, N    frames, head width, vocabulary size, utterances (N >= 0,
  *                 M >= 0, D >= 1, V >= 1).
  *   tgt_off       device int32, N + 1 monotone offsets into tgt, tgt_off[0]

@@ -59,7 +59,7 @@ SIGNATURES = {
 class FwdInfo(ctypes.Structure):
     _fields_ = [("K", ctypes.c_int32), ("n_unalignable", ctypes.c_int32),
                 ("n_nonfinite", ctypes.c_int32), ("max_target_len", ctypes.c_int32),
-                ("workspace_bytes", ctypes.c_uint64)]
+                ("workspace_bytes", ctypes.c_uint64), ("lse_spans", ctypes.c_int32)]
 
 
 class PcxError(RuntimeError):

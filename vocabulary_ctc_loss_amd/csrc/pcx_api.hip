@@ -293,7 +293,9 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ctx->max_T = hm.max_T;
   ctx->dp_total = hm.dp_total;
 
-  const int nspan = (iV + LSE_SPAN - 1) / LSE_SPAN;
+  const int big = (M > 0 && dtype != PCX_F32_BF16W) ? use_big_fwd(dtype, iD, X, W) : 0;
+  const int span = lse_span(dtype, big, iM, iV);
+  const int nspan = (iV + span - 1) / span;
   ctx->nspan = nspan;
   // Grouped form: the projection's log-sum-exp covers the unselected classes
   // only, giving the other column o; lambda then comes from [Z[:, U], o].
@@ -310,11 +312,11 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
 
   if (M > 0 && dtype == PCX_F32_BF16W) {
-    // fp32 projection of a bf16 head: whole 2048-class spans of W (about C
-    // rows) widened to fp32 at a time.
+    // fp32 projection of a bf16 head: whole spans of W (about C rows)
+    // widened to fp32 at a time.
     const int eff_chunk = chunk < iV ? chunk : iV;
-    const int fspans = eff_chunk / LSE_SPAN > 1 ? eff_chunk / LSE_SPAN : 1;
-    const int Cf = fspans * LSE_SPAN;
+    const int fspans = eff_chunk / span > 1 ? eff_chunk / span : 1;
+    const int Cf = fspans * span;
     ENSURE(w32, (size_t)Cf * D * sizeof(float));
     if (b) ENSURE(b32, (size_t)Cf * sizeof(float));
     for (int c0 = 0; c0 < iV; c0 += Cf) {
@@ -326,14 +328,13 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
       LAUNCH(K_FWD_LSE, launch_fwd_lse(st, PCX_F32, X, ctx->w32.p, b ? ctx->b32.p : nullptr, iM,
                                        iD, c1 - c0, (const int*)ctx->col2sel.p + c0,
                                        (float*)ctx->S.p, (double2*)ctx->part.p,
-                                       (c1 - c0 + LSE_SPAN - 1) / LSE_SPAN, 0, c0 / LSE_SPAN,
-                                       nspan, grouped));
+                                       (c1 - c0 + span - 1) / span, 0, c0 / span, nspan,
+                                       grouped, span));
     }
   } else if (M > 0) {
-    const int big = use_big_fwd(dtype, iD, X, W);
     LAUNCH(K_FWD_LSE, launch_fwd_lse(st, dtype, X, W, b, iM, iD, iV, (const int*)ctx->col2sel.p,
                                      (float*)ctx->S.p, (double2*)ctx->part.p, nspan, big, 0,
-                                     nspan, grouped));
+                                     nspan, grouped, span));
   }
   if (M > 0) {
     LAUNCH(K_LAMBDA, launch_lambda(st, (const double2*)ctx->part.p, iM, nspan,
@@ -381,6 +382,7 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
     info->n_nonfinite = fm.n_nonfinite;
     info->max_target_len = hm.max_L;
     info->workspace_bytes = total_bytes(ctx);
+    info->lse_spans = nspan;
   }
   return PCX_OK;
 }

@@ -122,8 +122,9 @@ struct Meta {
 // Utterance status codes.
 enum : int { UTT_OK = 0, UTT_UNALIGNABLE = 1, UTT_NONFINITE = 2 };
 
-// Columns folded into one normalizer partial by the forward kernel.
-constexpr int LSE_SPAN = 2048;
+// Largest vocabulary span folded into one normalizer partial by the forward
+// kernel (one work-group walks one span of one frame tile).
+constexpr int LSE_SPAN_MAX = 2048;
 // Frames per work-group of the occupancy kernel.
 constexpr int OCC_FRAMES = 32;
 
@@ -149,7 +150,12 @@ int use_big_core(int dtype, int D, int chunk, const void* X, const void* W);
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W,
                           const void* b, int M, int D, int V, const int* col2sel,
                           float* Zsel, double2* part, int nspan, int big, int span0,
-                          int part_ld, int masked);
+                          int part_ld, int masked, int span);
+// Span width of the forward for a head: the largest multiple of the kernel's
+// tile rows, at most LSE_SPAN_MAX, that still gives about 2048 work-groups or
+// more (small vocabularies get narrow spans, so the launch fills the chip).
+// A function of the dtype, the core, M and V only.
+int lse_span(int dtype, int big, int M, int V);
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan,
                          double* lam, float* lamf);
 // Grouped form: lambda from the K gathered logits and the other column.

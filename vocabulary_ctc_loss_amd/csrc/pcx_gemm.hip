@@ -455,7 +455,7 @@ template <> struct Pick<bf16_t> {
 // The forward tile is computed transposed: BM vocabulary rows (operand A =
 // W) by BN frames (operand B = X), so each lane holds FM x 16 vocabulary
 // values of each of its FN frames and the per-frame log-sum-exp of a tile
-// needs no cross-lane step.  One work-group: BN frames x one LSE_SPAN-wide
+// needs no cross-lane step.  One work-group: BN frames x one span-wide
 // vocabulary span, walked in BM-row tiles, the next tile's first k stage
 // loaded before the current tile's epilogue.  Per tile and frame each lane
 // folds the max and the FP64 sum of exp(z - max) over its values into a
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
     const typename C::type* __restrict__ bias, int M, int D, int V,
     const int* __restrict__ col2sel, float* __restrict__ Zsel, double2* __restrict__ part,
-    int nspan, int ftiles, int vec_ok, int span0, int part_ld) {
+    int nspan, int ftiles, int vec_ok, int span0, int part_ld, int span) {
   using T = typename C::type;
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ __attribute__((aligned(16))) int s_sel[2][C::BM];
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   int ft, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
   const int f0 = ft * C::BN;
-  const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
+  const int c_begin = sp * span, c_end = min(V, c_begin + span);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   float run_m[C::FN];
   double run_s[C::FN];
@@ -1220,7 +1220,7 @@ __device__ __forceinline__ void gemm_big1(const bf16_t* __restrict__ A, long lon
 // rows (operand A = W) by 256 frames (operand B = X), so every lane holds 64
 // vocabulary values of each of its FN frames and the per-frame log-sum-exp
 // of a tile needs no cross-lane step.  One work-group: 256 frames x one
-// LSE_SPAN-wide vocabulary span in 256-row tiles.  Per tile and frame, each
+// span-wide vocabulary span in 256-row tiles.  Per tile and frame, each
 // lane folds max and FP64 sum of exp(z - max) over its 64 values into its
 // running partial; at the end of the span the partials of the two lane
 // halves and of the WGM wave rows are folded in a fixed order.  Selected
@@ -1230,7 +1230,7 @@ template <class C, bool MASKED>
 __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
     int M, int D, int V, const int* __restrict__ col2sel, float* __restrict__ Zsel,
-    double2* __restrict__ part, int nspan, int ftiles) {
+    double2* __restrict__ part, int nspan, int ftiles, int span) {
   // One LDS object for everything: with a second one, the compiler makes
   // every fragment read wait for all outstanding global->LDS loads.
   constexpr int O_SEL = C::LDS_BYTES, O_BIAS = O_SEL + 2 * C::BM * 4;
@@ -1246,7 +1246,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
   int ft, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
   const int f0 = ft * C::BN;
-  const int c_begin = sp * LSE_SPAN, c_end = min(V, c_begin + LSE_SPAN);
+  const int c_begin = sp * span, c_end = min(V, c_begin + span);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   float run_m[C::FN];
   double run_s[C::FN];
@@ -1714,7 +1714,7 @@ int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 template <typename T>
 hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                      int V, const int* col2sel, float* Zsel, double2* part, int nspan, int span0,
-                     int part_ld, int masked) {
+                     int part_ld, int masked, int span) {
   using C = typename Pick<T>::fwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
@@ -1723,24 +1723,24 @@ hipError_t fwd_lse_t(hipStream_t st, const void* X, const void* W, const void* b
   if (masked)
     k_fwd_lse<C, true><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D,
                                                     V, col2sel, Zsel, part, nspan, ftiles, vec,
-                                                    span0, part_ld);
+                                                    span0, part_ld, span);
   else
     k_fwd_lse<C, false><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M,
                                                      D, V, col2sel, Zsel, part, nspan, ftiles,
-                                                     vec, span0, part_ld);
+                                                     vec, span0, part_ld, span);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                           int M, int D, int V, const int* col2sel, float* Zsel, double2* part,
-                          int nspan, int big, int span0, int part_ld, int masked) {
+                          int nspan, int big, int span0, int part_ld, int masked, int span) {
   if (dtype == 0)
     return fwd_lse_t<float>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, span0, part_ld,
-                            masked);
+                            masked, span);
   if (span0 != 0 || part_ld != nspan) return hipErrorInvalidValue;  // bf16: whole vocabulary
   if (!big)
     return fwd_lse_t<bf16_t>(st, X, W, b, M, D, V, col2sel, Zsel, part, nspan, 0, nspan,
-                             masked);
+                             masked, span);
   using C = CfgBigFwd;
   const int ftiles = ceil_div(M, C::BN);
   const int grid = ftiles * nspan;
@@ -1748,12 +1748,32 @@ hipError_t launch_fwd_lse(hipStream_t st, int dtype, const void* X, const void* 
   if (masked)
     k_fwd_lse_big<C, true><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
                                                         (const bf16_t*)b, M, D, V, col2sel, Zsel,
-                                                        part, nspan, ftiles);
+                                                        part, nspan, ftiles, span);
   else
     k_fwd_lse_big<C, false><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
                                                          (const bf16_t*)b, M, D, V, col2sel,
-                                                         Zsel, part, nspan, ftiles);
+                                                         Zsel, part, nspan, ftiles, span);
   return hipGetLastError();
+}
+
+int lse_span(int dtype, int big, int M, int V) {
+  int bm, bn;
+  if (dtype == 0 || dtype == 2) {
+    bm = Pick<float>::fwd::BM;
+    bn = Pick<float>::fwd::BN;
+  } else if (big) {
+    bm = CfgBigFwd::BM;
+    bn = CfgBigFwd::BN;
+  } else {
+    bm = Pick<bf16_t>::fwd::BM;
+    bn = Pick<bf16_t>::fwd::BN;
+  }
+  const long long ftiles = (M + bn - 1) / bn;
+  long long span = (long long)V * ftiles / 2048;  // about 2048 work-groups or more
+  span = span / bm * bm;
+  if (span < bm) span = bm;
+  if (span > LSE_SPAN_MAX) span = LSE_SPAN_MAX;
+  return (int)span;
 }
 
 hipError_t launch_lambda(hipStream_t st, const double2* part, int M, int nspan, double* lam,
