@@ -101,6 +101,11 @@ void pcx_destroy(pcx_ctx* ctx);
  *                 after those of utterances 0..n-1 (Sec. 3.1).
  *   W             device, V x D row-major (nn.Linear weight layout).
  *   b             device, V entries, or NULL for a zero bias.
+ *                 X, W and b must be finite (PrunedCTC README constraints).
+ *                 An utterance whose rows of X are not finite comes out
+ *                 nonfinite: it is excluded (zero loss, zero dX rows,
+ *                 counted), but dW and db, which mix all rows, are then
+ *                 undefined.
  *   dtype         PCX_F32 or PCX_BF16 (the element type of X, W and b), or
  *                 PCX_F32_BF16W (X fp32, W and b bf16; the projections run in
  *                 fp32 on W widened chunk by chunk, C rows at a time in the

@@ -178,6 +178,32 @@ def test_parity_with_oracle(name):
             assert np.all(got["dX"][row_off[n]:row_off[n + 1]] == 0.0)
 
 
+@pytest.mark.parametrize("name", ["tiles", "bf16_big_grads"])
+def test_nonfinite_input_utterance_is_excluded(name):
+    """One utterance's encoder states are NaN (a precondition violation): its
+    loss comes out nonfinite, so it is excluded like the pages' nonfinite
+    utterances (zero loss, zero dX rows, counted), and every other
+    utterance's loss and dX rows are unchanged.  dW and db mix all rows
+    (0 * NaN) and are not checked."""
+    import dataclasses
+    bt = case(name)
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    X = bt.X.copy()
+    X[row_off[2]:row_off[3]] = np.nan
+    bt = dataclasses.replace(bt, X=X)
+    got = run_pcx(bt, want_dW=False, want_db=False, getters="light")
+    ref = run_oracle(bt, want_dW=False, want_db=False)
+    tol = tolerance(bt)
+    assert ref["status"][2] == 2 and got["status"].tolist() == ref["status"].tolist()
+    assert got["info"]["n_nonfinite"] == 1
+    assert got["utt_loss"][2] == 0.0
+    assert abs(got["loss"] - ref["loss"]) <= tol * abs(ref["loss"])
+    assert np.all(got["dX"][row_off[2]:row_off[3]] == 0.0)
+    keep = np.ones(bt.M, bool)
+    keep[row_off[2]:row_off[3]] = False
+    assert rel_fro(got["dX"][keep], ref["dX"][keep]) <= tol
+
+
 def test_grad_scaling_and_skipped_outputs():
     bt = case("tiles")
     ref = run_oracle(bt, grad=-0.37)

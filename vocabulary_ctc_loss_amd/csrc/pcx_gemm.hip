@@ -809,8 +809,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
         const bool in = rows_full || m0 + row < M;
 #pragma unroll
         for (int fj = 0; fj < C::FN; ++fj) {
-          const float dz =
-              rs4[e] * __builtin_amdgcn_exp2f(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
+          // the exponent is <= 0 for every class; the clamp also turns the
+          // NaN logit of an excluded row (non-finite input) into rs = 0 times 1
+          const float dz = rs4[e] * __builtin_amdgcn_exp2f(
+                                        fminf(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]), 0.f));
           if (in && crole[fj] == 0) {
             dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
             cs[fj] += dz;
@@ -1494,8 +1496,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         const bool in = rows_full || m0 + row0 + e < M;
 #pragma unroll
         for (int fj = 0; fj < C::FN; ++fj) {
+          // the exponent is <= 0 for every class; the clamp also turns the
+          // NaN logit of an excluded row (non-finite input) into rs = 0 times 1
           const float dz = rs4[e] * __builtin_amdgcn_exp2f(
-                                        fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]));
+                                        fminf(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]), 0.f));
           acc[fi][fj][4 * q + e] = dz;
           cs[fj] += in ? dz : 0.f;
         }
