@@ -1069,9 +1069,6 @@ __device__ __forceinline__ void big_stage(const bf16_t* __restrict__ G, long lon
   }
 }
 
-// Barrier of the big core: this wave's LDS reads are complete and at most N
-// of its global memory operations are in flight, then all waves meet.  (A
-// release fence would also wait for every outstanding global->LDS load.)
 // Two fp32 values rounded to nearest-even bf16 by the hardware conversion,
 // packed low (lo) / high (hi).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
@@ -1090,6 +1087,9 @@ __device__ __forceinline__ uint32_t lane_xor2(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
 }
 
+// Barrier of the big core: this wave's LDS reads are complete and at most N
+// of its global memory operations are in flight, then all waves meet.  (A
+// release fence would also wait for every outstanding global->LDS load.)
 template <int N>
 __device__ __forceinline__ void big_barrier() {
   static_assert(N >= 0 && N < 64, "vmcnt");
