@@ -328,7 +328,8 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     const double* __restrict__ beta, float* __restrict__ Gam, double* __restrict__ g,
     int Lcap) {
   extern __shared__ double sh[];
-  __shared__ double s_bl[OCC_THREADS], s_tot[OCC_THREADS];
+  constexpr int NW = OCC_THREADS / 64;
+  __shared__ double s_bl[NW], s_tot[NW];
   const int n = blockIdx.x;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int t0 = blockIdx.y * OCC_FRAMES;
@@ -341,26 +342,24 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   double* s_q = sh;                                       // Sn doubles
   int* s_y = reinterpret_cast<int*>(sh + (2 * Lcap + 1));  // L ints
-  int* s_next = s_y + Lcap;                                // L ints
-  int* s_lead = s_next + Lcap;                             // L ints
+  int* s_ord = s_y + Lcap;                                 // L ints
+  int* s_seg = s_ord + Lcap;                               // L ints
   for (int i = threadIdx.x; i < L; i += blockDim.x) s_y[i] = tgt_rel[y0 + i];
   lds_barrier();
+  // Label positions sorted by (class, position): the occurrences of a class
+  // form one segment, in position order.  The first occurrence of a class
+  // (its lead) holds start << 16 | length of the segment; the others -1.
   for (int i = threadIdx.x; i < L; i += blockDim.x) {
     const int c = s_y[i];
-    int lead = 1;
-    for (int j = 0; j < i; ++j)
-      if (s_y[j] == c) {
-        lead = 0;
-        break;
-      }
-    int nx = -1;
-    for (int j = i + 1; j < L; ++j)
-      if (s_y[j] == c) {
-        nx = j;
-        break;
-      }
-    s_lead[i] = lead;
-    s_next[i] = nx;
+    int less = 0, before = 0, same = 0;
+    for (int j = 0; j < L; ++j) {
+      const int cj = s_y[j];
+      less += cj < c;
+      same += cj == c;
+      before += (cj == c) & (j < i);
+    }
+    s_ord[less + before] = i;
+    s_seg[i] = before == 0 ? (less << 16) | same : -1;
   }
   lds_barrier();
   const double logP = utt_logp[n];
@@ -378,26 +377,37 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
       tot += q;
       if (!(s & 1)) bl += q;
     }
-    s_bl[threadIdx.x] = bl;
-    s_tot[threadIdx.x] = tot;
-    lds_barrier();
-    for (int stride = OCC_THREADS / 2; stride > 0; stride >>= 1) {
-      if ((int)threadIdx.x < stride) {
-        s_bl[threadIdx.x] += s_bl[threadIdx.x + stride];
-        s_tot[threadIdx.x] += s_tot[threadIdx.x + stride];
-      }
-      lds_barrier();
+    // fixed-order sums: a butterfly within each wavefront, then the
+    // wavefront sums in order
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      bl += __shfl_xor(bl, o, 64);
+      tot += __shfl_xor(tot, o, 64);
     }
+    if ((threadIdx.x & 63) == 0) {
+      s_bl[threadIdx.x >> 6] = bl;
+      s_tot[threadIdx.x >> 6] = tot;
+    }
+    lds_barrier();
     for (int i = threadIdx.x; i < L; i += blockDim.x) {
-      if (s_lead[i]) {
-        double gm = 0.0;
-        for (int k = i; k >= 0; k = s_next[k]) gm += s_q[2 * k + 1];
+      const int seg = s_seg[i];
+      if (seg >= 0) {
+        const int* ord = s_ord + (seg >> 16);
+        const int len = seg & 0xFFFF;
+        double gm = 0.0;  // occurrences in position order
+        for (int j = 0; j < len; ++j) gm += s_q[2 * ord[j] + 1];
         Gam[(long long)s_y[i] * M + row] = (float)gm;
       }
     }
     if (threadIdx.x == 0) {
-      Gam[row] = (float)s_bl[0];  // blank is U[0]
-      g[row] = s_tot[0];
+      double b0 = s_bl[0], t0s = s_tot[0];
+#pragma unroll
+      for (int q = 1; q < NW; ++q) {
+        b0 += s_bl[q];
+        t0s += s_tot[q];
+      }
+      Gam[row] = (float)b0;  // blank is U[0]
+      g[row] = t0s;
     }
     lds_barrier();
   }

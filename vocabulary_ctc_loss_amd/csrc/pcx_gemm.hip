@@ -640,6 +640,9 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 // recompute epilogue lets every lane handle its own selected columns instead
 // of sharing each selected column among all 64 lanes.
 constexpr int SEL_DENSE = 8;
+// On the 256 x 256 core the per-wavefront limit of that cooperative pass,
+// whose S and Gamma values are loaded into a 24 KiB LDS region beside the
+// operand stages (the registers are taken by the accumulators).
 constexpr int SEL_PRE_BIG = 6;
 
 // Selected columns of one wavefront's tile block for the cooperative pass
@@ -651,7 +654,7 @@ template <class C>
 struct SelPre {
   static constexpr int RPL = C::WM / 64;
   int n;
-  int sel[SEL_DENSE], col[SEL_DENSE];
+  int col[SEL_DENSE];
   float s[SEL_DENSE][RPL], g[SEL_DENSE][RPL];
 };
 
@@ -689,7 +692,6 @@ __device__ __forceinline__ void sel_prefetch(SelPre<C>& p, const int* s_sel, int
         found = true;
       }
     }
-    p.sel[k] = sel;
     p.col[k] = col;
 #pragma unroll
     for (int t = 0; t < SelPre<C>::RPL; ++t) {
@@ -782,7 +784,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   f32x16 acc[C::FM][C::FN];
   gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
-  static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
   const bool rows_full = m0 + BM <= M;
   // Unselected classes on the accumulators, four rows at a time; selected
   // classes (role 2) and columns past the chunk (role 3) are skipped here.
@@ -1366,7 +1367,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   constexpr int O_G = C::LDS_BYTES, O_SEL = O_G + BM * 8, O_BIAS = O_SEL + BN * 4;
   constexpr int O_LAM = O_BIAS + BN * 4, O_RS = O_LAM + BM * 4, O_PRE = O_RS + BM * 4;
   constexpr int O_DB = C::LDS_BYTES / 2;
-  static_assert(C::WAVES * SEL_DENSE * (C::WM + 1) * 4 <= O_DB &&
+  static_assert(C::WAVES * SEL_PRE_BIG * (C::WM + 1) * 4 <= O_DB &&
                     O_DB + C::WGM * BN * 4 <= C::LDS_BYTES, "post-product LDS use");
   __shared__ __attribute__((aligned(16))) char smem[O_PRE + C::WAVES * SEL_PRE_BIG * 512];
   double* s_g = reinterpret_cast<double*>(smem + O_G);
@@ -1457,7 +1458,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   // rounded once, into LDS (one region per wavefront) with the column's sum
   // over the wavefront's rows (a fixed-order wave sum) ...
   const bool dense = pn > SEL_PRE_BIG;
-  float* tmp = reinterpret_cast<float*>(smem) + w * (SEL_DENSE * (C::WM + 1));
+  float* tmp = reinterpret_cast<float*>(smem) + w * (SEL_PRE_BIG * (C::WM + 1));
   if (!dense && pn > 0) {
     const int row = wm * C::WM + lane;
 #pragma unroll
@@ -1474,7 +1475,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         tmp[k * C::WM + lane] = dz;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-        if (lane == 0) tmp[SEL_DENSE * C::WM + k] = sum;
+        if (lane == 0) tmp[SEL_PRE_BIG * C::WM + k] = sum;
       }
     }
   }
@@ -1537,7 +1538,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
                 acc[fi][fj][4 * q + e] = own ? v4[e] : acc[fi][fj][4 * q + e];
             }
         }
-        if (lane == 0) s_db[wm][pcol[k]] = tmp[SEL_DENSE * C::WM + k];
+        if (lane == 0) s_db[wm][pcol[k]] = tmp[SEL_PRE_BIG * C::WM + k];
       }
     }
   }
