@@ -8,7 +8,9 @@ The oracle cannot redo a whole V = 180k or LLM-head batch in seconds, so:
   utterance itself);
 * dW and db, which mix all utterances, are checked by properties that hold
   at any size: every alignable frame's logit-gradient row sums to zero, so
-  sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding.
+  sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding;
+* the grouped formulation is held to the same sampled bar and compared with
+  the direct one on the whole batch.
 """
 import numpy as np
 import pytest
@@ -56,3 +58,30 @@ def test_full_size_sampled(name):
         colsum = np.abs(dW.sum(0))
         scale = np.abs(dW).sum(0)
         assert np.all(colsum <= 1e-5 * scale)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["v180k", "llm152k"])
+def test_full_size_grouped_matches_oracle_and_direct(name):
+    """The grouped ("other" column) formulation at full size: per-utterance
+    losses and sampled dX rows against the oracle, and everything against the
+    direct formulation on the same inputs (equal up to rounding)."""
+    bt = workloads.make(name, seed=0)
+    print("workload", name, "grouped", flush=True)
+    d = run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters="light")
+    g = run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters="light", grouped=True)
+    tol = tolerance(bt)
+    assert g["status"].tolist() == d["status"].tolist()
+    assert abs(g["loss"] - d["loss"]) <= 1e-6 * abs(d["loss"])
+    for k in ("dX", "dW", "db"):
+        if d[k] is not None:
+            assert rel_fro(g[k], d[k]) <= (1e-6 if bt.dtype == "f32" else 1e-2), k
+    idx = _sample(bt)
+    sb = workloads.sample_utterances(bt, idx)
+    ref = oracle.pcx(sb.X, sb.W, sb.b, sb.frame_counts, sb.tgt_off, sb.tgt, sb.blank,
+                     want_dW=False, want_db=False)
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    for j, n in enumerate(idx):
+        assert abs(g["utt_loss"][n] - ref["utt_loss"][j]) <= tol * abs(ref["utt_loss"][j])
+    rows = np.concatenate([np.arange(row_off[n], row_off[n + 1]) for n in idx])
+    assert rel_fro(g["dX"][rows], ref["dX"]) <= tol
