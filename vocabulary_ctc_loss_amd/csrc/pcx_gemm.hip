@@ -1345,9 +1345,10 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
 }
 
 // Backward recompute on the big core (frames x vocabulary, as k_recompute):
-// the same per-element formulas; in addition the chunk block's columns
-// between the chunk end and the next multiple of 64 are written as zeros,
-// because the dX product on the big core reduces over whole 64-column steps.
+// the same per-element formulas, stored four columns (8 bytes) per lane; in
+// addition the chunk block's columns between the chunk end and the next
+// multiple of 64 are written as zeros, because the dX product on the big
+// core reduces over whole 64-column steps.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
@@ -1440,8 +1441,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   gemm_big1<C>(X, D, m0, M, W, D, n0, c1, D, acc, smem);
   const bool rows_full = m0 + BM <= M;
   // Column roles: 0 = unselected class (formula below), 1 = padding up to
-  // the next multiple of 64 (zero), 2 = selected class or past the padding
-  // (left to the pass after this one / not written).
+  // the next multiple of 64 (zero), 2 = selected class (its value from S and
+  // Gamma, patched into the accumulators or stored by the dense pass) or past
+  // the padding (not stored).
   int csel[C::FN], crole[C::FN];
   float cbv[C::FN], cs[C::FN];
 #pragma unroll
