@@ -426,16 +426,18 @@ __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double
 
 // Tile configurations of the four head products, chosen by sweeps of tile /
 // wave shapes on the V = 180k (fp32) and LLM (bf16) heads.  fp32: 128 x 128
-// work-group tiles with 16-k stages; the dX product prefers eight 64 x 32
-// wavefronts.
+// work-group tiles with 16-k stages; the forward (whose epilogue ends every
+// short K = D product) gains from 32-k stages, the dX product from eight
+// 64 x 32 wavefronts.
 using CfgF32 = Cfg<float, 128, 128, 64, 64, 64, 2>;
+using CfgF32Fwd = Cfg<float, 128, 128, 64, 64, 128, 2>;
 using CfgF32Dx = Cfg<float, 128, 128, 64, 32, 128, 2>;
 using CfgB16 = Cfg<bf16_t, 128, 128, 64, 64, 128, 2>;
 using CfgB16W8 = Cfg<bf16_t, 128, 128, 32, 64, 128, 2>;
 using CfgB16Wide = Cfg<bf16_t, 128, 256, 64, 128, 64, 2>;
 template <typename T> struct Pick;
 template <> struct Pick<float> {
-  using fwd = CfgF32;
+  using fwd = CfgF32Fwd;
   using rec = CfgF32;
   using dx = CfgF32Dx;
   using dw = CfgF32;
