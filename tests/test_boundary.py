@@ -124,3 +124,16 @@ def test_formulation_switch_without_device(lib):
         assert lib.pcx_get_other(h, buf, 8) == 5       # no forward yet
     finally:
         lib.pcx_destroy(h)
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    """Without the built HIP library every entry point raises: there is no
+    CPU or oracle fallback anywhere in the product."""
+    from vocabulary_ctc_loss_amd import _lib
+    import vocabulary_ctc_loss_amd as pcx
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libpcx.so"))
+    with pytest.raises(ImportError, match="not built"):
+        _lib.load()
+    with pytest.raises(ImportError, match="not built"):
+        pcx.Context()
