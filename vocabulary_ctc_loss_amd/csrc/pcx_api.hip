@@ -45,13 +45,12 @@ struct DevBuf {
 // Kernel families timed by the optional event profiler.
 enum Kid {
   K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
-  K_RECOMPUTE, K_DX, K_DW, K_DW_REDUCE, K_DB_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_ROWSCALE,
-  K_COUNT
+  K_RECOMPUTE, K_DX, K_DW, K_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_ROWSCALE, K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
     "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
     "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
-    "dw_reduce", "db_reduce", "cast", "blank_offset_grad", "widen_head", "grouped_rowscale"};
+    "grad_reduce", "cast", "blank_offset_grad", "widen_head", "grouped_rowscale"};
 
 struct Pending {
   int kid;
@@ -523,15 +522,13 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     if (dX)
       LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, C, Wk, M, D, w0, w0 + Cc, dxacc, ch == 0,
                              ctx->wt.p, big));
-    if (dW) {
+    if (dW)
       LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, C, ctx->X, M, D, w0, w0 + Cc,
                              (float*)ctx->dwpart.p, splitk));
-      LAUNCH(K_DW_REDUCE, launch_dw_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc, D,
-                                           dW, c0));
-    }
-    if (db)
-      LAUNCH(K_DB_REDUCE, launch_db_reduce(st, wdt, (const float*)ctx->dbpart.p, mtiles, Cc, C,
-                                           db, c0));
+    if (dW || db)
+      LAUNCH(K_REDUCE, launch_grad_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc, D,
+                                          dW, c0, (const float*)ctx->dbpart.p, mtiles, Cc, C,
+                                          db, c0));
   }
   if (dX && cdt != PCX_F32)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));

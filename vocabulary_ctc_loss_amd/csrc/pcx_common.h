@@ -183,10 +183,13 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
                      int M, int D, int c0, int c1, float* dXacc, int first, void* wt, int big);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
-hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk,
-                            int rows, int D, void* dW, long long row_base);
-hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int mtiles,
-                            int cols, int ld, void* db, long long col_base);
+// dW rows [row_base, row_base + rows) from the split partials and db
+// columns [col_base, col_base + cols) from the per-row-tile partials
+// (leading dimension ld), in one launch; either output may be NULL.
+hipError_t launch_grad_reduce(hipStream_t st, int dtype, const float* part, int splitk,
+                              int rows, int D, void* dW, long long row_base,
+                              const float* dbpart, int mtiles, int cols, int ld, void* db,
+                              long long col_base);
 hipError_t launch_cast_out(hipStream_t st, int dtype, const float* src, void* dst,
                            long long n);
 // dst[i] = fp32(src[i]) for n bf16 values.

@@ -938,44 +938,48 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dw(
     }
 }
 
+// The two head-gradient reductions of one chunk in one launch of 256-thread
+// blocks: the first nb_db blocks reduce the bias partials, 16 columns each
+// (db[col] = sum over row tiles of dbpart[tile][col]: sixteen fixed groups of
+// consecutive tiles, the group sums added in group order); the other blocks
+// reduce the dW split partials (dW[row_base + r][d] = sum over k, in order,
+// of part[k][r][d]).  The db part is latency-bound and the dW part
+// HBM-bound, so they share the launch.
+constexpr int DB_GROUPS = 16;
+constexpr int DB_COLS = 256 / DB_GROUPS;
 template <typename T>
-__global__ void k_dw_reduce(const float* __restrict__ part, int splitk, int rows, int D,
-                            T* __restrict__ dW, long long row_base) {
+__global__ __launch_bounds__(256) void k_grad_reduce(
+    const float* __restrict__ part, int splitk, int rows, int D, T* __restrict__ dW,
+    long long row_base, const float* __restrict__ dbpart, int mtiles, int cols, int ld,
+    T* __restrict__ db, long long col_base, int nb_db) {
+  if ((int)blockIdx.x < nb_db) {
+    __shared__ float gs[DB_GROUPS][DB_COLS];
+    const int lc = threadIdx.x % DB_COLS, q = threadIdx.x / DB_COLS;
+    const int c = blockIdx.x * DB_COLS + lc;
+    const int per = (mtiles + DB_GROUPS - 1) / DB_GROUPS;
+    const int k1 = min(mtiles, (q + 1) * per);
+    float s = 0.f;
+    if (c < cols) {
+#pragma unroll 8
+      for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
+    }
+    gs[q][lc] = s;
+    lds_barrier();
+    if (q == 0 && c < cols) {
+      float t = gs[0][lc];
+#pragma unroll
+      for (int g = 1; g < DB_GROUPS; ++g) t += gs[g][lc];
+      db[col_base + c] = Elem<T>::from_f32(t);
+    }
+    return;
+  }
   const long long n = (long long)rows * D;
-  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
-       i += (long long)gridDim.x * blockDim.x) {
+  const long long stride = (long long)(gridDim.x - nb_db) * blockDim.x;
+  for (long long i = (blockIdx.x - nb_db) * (long long)blockDim.x + threadIdx.x; i < n;
+       i += stride) {
     float s = 0.f;
     for (int k = 0; k < splitk; ++k) s += part[(long long)k * n + i];
     dW[row_base * D + i] = Elem<T>::from_f32(s);
-  }
-}
-
-// db[col] = sum over row tiles of dbpart[tile][col]: sixteen fixed groups of
-// consecutive tiles per column (one wavefront each, 64 columns per block),
-// the group sums then added in group order.
-constexpr int DB_GROUPS = 16;
-template <typename T>
-__global__ __launch_bounds__(64 * DB_GROUPS) void k_db_reduce(const float* __restrict__ dbpart,
-                                                              int mtiles, int cols, int ld,
-                                                              T* __restrict__ db,
-                                                              long long col_base) {
-  __shared__ float part[DB_GROUPS][64];
-  const int lc = threadIdx.x & 63, q = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + lc;
-  const int per = (mtiles + DB_GROUPS - 1) / DB_GROUPS;
-  const int k1 = min(mtiles, (q + 1) * per);
-  float s = 0.f;
-  if (c < cols) {
-#pragma unroll 8
-    for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
-  }
-  part[q][lc] = s;
-  lds_barrier();
-  if (q == 0 && c < cols) {
-    float t = part[0][lc];
-#pragma unroll
-    for (int g = 1; g < DB_GROUPS; ++g) t += part[g][lc];
-    db[col_base + c] = Elem<T>::from_f32(t);
   }
 }
 
@@ -1933,28 +1937,22 @@ int dw_tiles(int dtype, int C, int D) {
   return ceil_div(C, Pick<bf16_t>::dw::BM) * ceil_div(D, Pick<bf16_t>::dw::BN);
 }
 
-hipError_t launch_dw_reduce(hipStream_t st, int dtype, const float* part, int splitk, int rows,
-                            int D, void* dW, long long row_base) {
-  const long long n = (long long)rows * D;
-  if (n == 0) return hipSuccess;
+hipError_t launch_grad_reduce(hipStream_t st, int dtype, const float* part, int splitk,
+                              int rows, int D, void* dW, long long row_base,
+                              const float* dbpart, int mtiles, int cols, int ld, void* db,
+                              long long col_base) {
+  const long long n = dW ? (long long)rows * D : 0;
+  const int nb_dw = n ? grid_cap(n, 256) : 0;
+  const int nb_db = (db && cols > 0) ? ceil_div(cols, DB_COLS) : 0;
+  if (nb_dw + nb_db == 0) return hipSuccess;
   if (dtype == 0)
-    k_dw_reduce<float><<<grid_cap(n, 256), 256, 0, st>>>(part, splitk, rows, D, (float*)dW,
-                                                          row_base);
+    k_grad_reduce<float><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
+                                                       (float*)dW, row_base, dbpart, mtiles,
+                                                       cols, ld, (float*)db, col_base, nb_db);
   else
-    k_dw_reduce<bf16_t><<<grid_cap(n, 256), 256, 0, st>>>(part, splitk, rows, D, (bf16_t*)dW,
-                                                           row_base);
-  return hipGetLastError();
-}
-
-hipError_t launch_db_reduce(hipStream_t st, int dtype, const float* dbpart, int mtiles, int cols,
-                            int ld, void* db, long long col_base) {
-  if (cols == 0) return hipSuccess;
-  if (dtype == 0)
-    k_db_reduce<float><<<ceil_div(cols, 64), 64 * DB_GROUPS, 0, st>>>(dbpart, mtiles, cols, ld,
-                                                                      (float*)db, col_base);
-  else
-    k_db_reduce<bf16_t><<<ceil_div(cols, 64), 64 * DB_GROUPS, 0, st>>>(dbpart, mtiles, cols, ld,
-                                                                       (bf16_t*)db, col_base);
+    k_grad_reduce<bf16_t><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
+                                                        (bf16_t*)dW, row_base, dbpart, mtiles,
+                                                        cols, ld, (bf16_t*)db, col_base, nb_db);
   return hipGetLastError();
 }
 
