@@ -642,9 +642,10 @@ __global__ void k_scores(float* __restrict__ S, const double* __restrict__ lam, 
 // recompute epilogue lets every lane handle its own selected columns instead
 // of sharing each selected column among all 64 lanes.
 constexpr int SEL_DENSE = 8;
-// On the 256 x 256 core the per-wavefront limit of that cooperative pass,
-// whose S and Gamma values are loaded into a 24 KiB LDS region beside the
-// operand stages (the registers are taken by the accumulators).
+// On the 256 x 256 core with eight wavefronts the per-wavefront limit of
+// that cooperative pass, whose S and Gamma values are loaded into a 24 KiB LDS
+// region beside the operand stages (the registers are taken by the
+// accumulators); with sixteen wavefronts (half the columns each) half of it.
 constexpr int SEL_PRE_BIG = 6;
 
 // Selected columns of one wavefront's tile block for the cooperative pass
@@ -1049,11 +1050,12 @@ struct CfgBig {
   static_assert(TILEB % (1024 * WAVES) == 0 && WM % 32 == 0 && WN % 32 == 0, "big tile");
   static_assert((BK == 32 || BK == 64) && NBUF >= 2 && LDS_BYTES <= 128 * 1024, "big stages");
 };
-// Eight 64 x 128 wavefronts (4 x 2): measured ahead of 2 x 4 on the LLM head.
-// The dX product, whose epilogue is light, runs sixteen 64 x 64 wavefronts
-// (4 x 4, four per SIMD; measured 3% faster there).
+// The forward runs eight 64 x 128 wavefronts (4 x 2; ahead of 2 x 4 on the
+// LLM head; its FP64 epilogue does not fit the registers of more).  The
+// recompute and dX products run sixteen 64 x 64 wavefronts (4 x 4, four per
+// SIMD; measured about 2% and 3% faster).
 using CfgBigFwd = CfgBig<4, 2, 64, 2>;
-using CfgBigRec = CfgBig<4, 2, 64, 2>;
+using CfgBigRec = CfgBig<4, 4, 64, 2>;
 using CfgBigDx = CfgBig<4, 4, 64, 2>;
 
 #define PCX_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
@@ -1367,18 +1369,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const float* __restrict__ lamu) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
+  // selected columns prefetched per wavefront: a fixed 24 KiB LDS region
+  constexpr int SELP = SEL_PRE_BIG * 8 / C::WAVES;
+  static_assert(SELP >= 1, "prefetch region");
   static_assert(C::WM == 64, "selected-class pass: one row per lane");
   // one LDS object (see k_fwd_lse_big): the operand stages, then the row and
   // column data, then per wavefront the S and Gamma values (64 rows each) of
-  // up to SEL_PRE_BIG selected columns.  After the product the stage buffers
+  // up to SELP selected columns.  After the product the stage buffers
   // hold the selected-class values on their way to the accumulators (from
   // offset 0) and the column sums (from O_DB).
   constexpr int O_G = C::LDS_BYTES, O_SEL = O_G + BM * 8, O_BIAS = O_SEL + BN * 4;
   constexpr int O_LAM = O_BIAS + BN * 4, O_RS = O_LAM + BM * 4, O_PRE = O_RS + BM * 4;
   constexpr int O_DB = C::LDS_BYTES / 2;
-  static_assert(C::WAVES * SEL_PRE_BIG * (C::WM + 1) * 4 <= O_DB &&
+  static_assert(C::WAVES * SELP * (C::WM + 1) * 4 <= O_DB &&
                     O_DB + C::WGM * BN * 4 <= C::LDS_BYTES, "post-product LDS use");
-  __shared__ __attribute__((aligned(16))) char smem[O_PRE + C::WAVES * SEL_PRE_BIG * 512];
+  __shared__ __attribute__((aligned(16))) char smem[O_PRE + C::WAVES * SELP * 512];
   double* s_g = reinterpret_cast<double*>(smem + O_G);
   int* s_sel = reinterpret_cast<int*>(smem + O_SEL);
   float* s_bias = reinterpret_cast<float*>(smem + O_BIAS);
@@ -1406,9 +1411,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   // Selected columns of this wavefront, in (fragment column, lane) order; with
-  // at most SEL_PRE_BIG of them their S and Gamma values are loaded straight
+  // at most SELP of them their S and Gamma values are loaded straight
   // into LDS now, behind the product (they do not depend on it).
-  int pn, pcol[SEL_PRE_BIG];
+  int pn, pcol[SELP];
   {
     unsigned long long mk[C::FN];
     int cs_[C::FN];
@@ -1422,7 +1427,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     }
     const int grow = min(m0 + wm * C::WM + lane, M - 1);
 #pragma unroll
-    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+    for (int k = 0; k < SELP; ++k) {
       int sel = 0, col = 0;
       bool found = false;
 #pragma unroll
@@ -1436,8 +1441,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         }
       }
       pcol[k] = col;
-      if (found && pn <= SEL_PRE_BIG) {
-        char* dst = smem + O_PRE + (w * SEL_PRE_BIG + k) * 512;
+      if (found && pn <= SELP) {
+        char* dst = smem + O_PRE + (w * SELP + k) * 512;
         __builtin_amdgcn_global_load_lds((const void*)(S + (long long)sel * M + grow),
                                          PCX_LDS_PTR(dst), 4, 0, 0);
         __builtin_amdgcn_global_load_lds((const void*)(Gam + (long long)sel * M + grow),
@@ -1463,19 +1468,19 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     crole[fj] = v < c1 ? (csel[fj] < 0 ? 0 : 2) : (v < c_pad ? 1 : 2);
     cs[fj] = 0.f;
   }
-  // Few selected classes (at most SEL_PRE_BIG in this wavefront): each
+  // Few selected classes (at most SELP in this wavefront): each
   // column by all 64 lanes (one of the wavefront's rows each), in FP64 and
   // rounded once, into LDS (one region per wavefront) with the column's sum
   // over the wavefront's rows (a fixed-order wave sum) ...
-  const bool dense = pn > SEL_PRE_BIG;
-  float* tmp = reinterpret_cast<float*>(smem) + w * (SEL_PRE_BIG * (C::WM + 1));
+  const bool dense = pn > SELP;
+  float* tmp = reinterpret_cast<float*>(smem) + w * (SELP * (C::WM + 1));
   if (!dense && pn > 0) {
     const int row = wm * C::WM + lane;
 #pragma unroll
-    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+    for (int k = 0; k < SELP; ++k) {
       if (k < pn) {
         const float* pv = reinterpret_cast<const float*>(smem + O_PRE +
-                                                         (w * SEL_PRE_BIG + k) * 512);
+                                                         (w * SELP + k) * 512);
         float sum = 0.f, dz = 0.f;
         if (m0 + row < M) {
           // S <= 0 (a log-probability)
@@ -1485,7 +1490,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         tmp[k * C::WM + lane] = dz;
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o, 64);
-        if (lane == 0) tmp[SEL_PRE_BIG * C::WM + k] = sum;
+        if (lane == 0) tmp[SELP * C::WM + k] = sum;
       }
     }
   }
@@ -1530,7 +1535,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   if (!dense && pn > 0) {
     const int h = lane >> 5;
 #pragma unroll
-    for (int k = 0; k < SEL_PRE_BIG; ++k) {
+    for (int k = 0; k < SELP; ++k) {
       if (k < pn) {
         const int cw = pcol[k] - (w % C::WGN) * C::WN;
         const bool own = (lane & 31) == (cw & 31);
@@ -1548,7 +1553,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
                 acc[fi][fj][4 * q + e] = own ? v4[e] : acc[fi][fj][4 * q + e];
             }
         }
-        if (lane == 0) s_db[wm][pcol[k]] = tmp[SEL_PRE_BIG * C::WM + k];
+        if (lane == 0) s_db[wm][pcol[k]] = tmp[SELP * C::WM + k];
       }
     }
   }
