@@ -77,6 +77,14 @@ def case(name):
         L = [600, 300]
         return workloads.make_random(11, N=2, T_lo=0, T_hi=0, V=500, D=32, chunk=256,
                                      frame_counts=T, target_lengths=L)
+    if name == "max_target":   # the longest target accepted: 4095 states, 4 per thread
+        T = [4200, 300]
+        L = [2047, 50]
+        return workloads.make_random(22, N=2, T_lo=0, T_hi=0, V=60, D=32, chunk=64,
+                                     frame_counts=T, target_lengths=L)
+    if name == "many_utts":    # several hundred short utterances: wide DP and occupancy grids
+        return workloads.make_random(23, N=400, T_lo=5, T_hi=30, V=300, D=32, chunk=128,
+                                     len_div=3.0)
     if name == "one_utt":
         return workloads.make_random(12, N=1, T_lo=200, T_hi=200, V=1000, D=64, chunk=512)
     if name == "bf16_llm":
@@ -129,7 +137,7 @@ def case(name):
 
 CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
          "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
-         "long_targets", "one_utt", "bf16_llm", "bf16_head", "bf16_big_ragged",
+         "long_targets", "max_target", "many_utts", "one_utt", "bf16_llm", "bf16_head", "bf16_big_ragged",
          "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120",
          "f32_bf16w_head", "f32_bf16w_llm"]
 
