@@ -53,6 +53,19 @@ MUTANTS = [
     ("db_overwrites", "if (db) db[v] += g;", "if (db) db[v] = g;"),
     ("loss_counts_unalignable_as_inf", "if (L + r > T) {\n    status = 1;",
      "if (L + r > T) {\n    status = 1; loss = INFINITY;"),
+    ("alpha_stay_dropped", "double a = prev[s];", "double a = -INFINITY;"),
+    ("beta_drops_emission", "cur[s] = b + lp[ext[s]];", "cur[s] = b;"),
+    ("alpha_emission_of_previous_frame", "cur[s] = a + lp[ext[s]];",
+     "cur[s] = a + lp[ext[s] - V];"),
+    ("normalizer_skips_last_class", "for (int v = 0; v < V; ++v) s += exp(z[v] - mx);",
+     "for (int v = 0; v + 1 < V; ++v) s += exp(z[v] - mx);"),
+    ("loss_from_first_state", "double logP = last[S - 1];", "double logP = last[0];"),
+    ("gamma_overwrites_repeats", "gam_row[ext[s]] += exp(lg);", "gam_row[ext[s]] = exp(lg);"),
+    ("relabel_search_includes_blank", "int lo = 1, hi = K - 1;", "int lo = 0, hi = K - 1;"),
+    ("alignability_strict", "flags[n] = (L + r <= frame_counts[n]) ? 1 : 0;",
+     "flags[n] = (L + r < frame_counts[n]) ? 1 : 0;"),
+    ("gradient_log_probability", "grad * (exp(lp[v]) - gam_row[v])",
+     "grad * (lp[v] - gam_row[v])"),
 ]
 
 
