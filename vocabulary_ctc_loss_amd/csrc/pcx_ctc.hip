@@ -318,8 +318,15 @@ __global__ __launch_bounds__(1024) void k_alpha_beta(
 // utterance: q(t, s) = exp(alpha + beta - emission - log P) per state,
 // gamma of a class = sum of q over its states (fixed order), g_m = sum_s q.
 // Rows of excluded utterances get g = 0 (Gamma was zero-filled).
+//
+// The frames are taken F at a time (F = 1, 2, 4 or 8, as many as the LDS
+// holds for the longest utterance), so that the loads of F frames are in
+// flight together and one pair of barriers serves F frames.  Work is split
+// frame-fastest: thread k always handles frame k mod F of a round, and a
+// class's Gamma stores for the F frames are contiguous.
 constexpr int OCC_THREADS = 256;
 
+template <int F>
 __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
@@ -327,9 +334,10 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     const long long* __restrict__ dp_off, const double* __restrict__ alpha,
     const double* __restrict__ beta, float* __restrict__ Gam, double* __restrict__ g,
     int Lcap) {
+  static_assert(OCC_THREADS % F == 0 && 64 % F == 0, "frames per round");
   extern __shared__ double sh[];
   constexpr int NW = OCC_THREADS / 64;
-  __shared__ double s_bl[NW], s_tot[NW];
+  __shared__ double s_bl[NW][F], s_tot[NW][F];
   const int n = blockIdx.x;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int t0 = blockIdx.y * OCC_FRAMES;
@@ -340,10 +348,10 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     return;
   }
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
-  double* s_q = sh;                                       // Sn doubles
-  int* s_y = reinterpret_cast<int*>(sh + (2 * Lcap + 1));  // L ints
-  int* s_ord = s_y + Lcap;                                 // L ints
-  int* s_seg = s_ord + Lcap;                               // L ints
+  double* s_q = sh;                                            // [Sn][F] doubles
+  int* s_y = reinterpret_cast<int*>(sh + F * (2 * Lcap + 1));  // L ints
+  int* s_ord = s_y + Lcap;                                     // L ints
+  int* s_seg = s_ord + Lcap;                                   // L ints
   for (int i = threadIdx.x; i < L; i += blockDim.x) s_y[i] = tgt_rel[y0 + i];
   lds_barrier();
   // Label positions sorted by (class, position): the occurrences of a class
@@ -365,49 +373,58 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   const double logP = utt_logp[n];
   const double* A = alpha + dp_off[n];
   const double* B = beta + dp_off[n];
-  for (int t = t0; t < t1; ++t) {
-    const int row = row0 + t;
+  const int f = threadIdx.x % F;  // this thread's frame within a round
+  for (int tb = t0; tb < t1; tb += F) {
+    const int t = tb + f;
+    const bool live = t < t1;
+    // q of (state, frame) pairs, state-major / frame-fastest
     double bl = 0.0, tot = 0.0;
-    for (int s = threadIdx.x; s < Sn; s += blockDim.x) {
-      const int cls = (s & 1) ? s_y[s >> 1] : 0;
-      const double e = (double)S[(long long)cls * M + row];
-      const long long o = (long long)t * Sn + s;
-      const double q = exp(A[o] + B[o] - e - logP);
-      s_q[s] = q;
+#pragma unroll 4
+    for (int s = threadIdx.x / F; s < Sn; s += OCC_THREADS / F) {
+      double q = 0.0;
+      if (live) {
+        const int cls = (s & 1) ? s_y[s >> 1] : 0;
+        const double e = (double)S[(long long)cls * M + row0 + t];
+        const long long o = (long long)t * Sn + s;
+        q = exp(A[o] + B[o] - e - logP);
+      }
+      s_q[s * F + f] = q;
       tot += q;
       if (!(s & 1)) bl += q;
     }
-    // fixed-order sums: a butterfly within each wavefront, then the
-    // wavefront sums in order
+    // fixed-order sums per frame: a butterfly over the lanes of one frame
+    // within each wavefront, then the wavefront sums in order
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
+    for (int o = 32; o >= F; o >>= 1) {
       bl += __shfl_xor(bl, o, 64);
       tot += __shfl_xor(tot, o, 64);
     }
-    if ((threadIdx.x & 63) == 0) {
-      s_bl[threadIdx.x >> 6] = bl;
-      s_tot[threadIdx.x >> 6] = tot;
+    if ((threadIdx.x & 63) < F) {
+      s_bl[threadIdx.x >> 6][f] = bl;
+      s_tot[threadIdx.x >> 6][f] = tot;
     }
     lds_barrier();
-    for (int i = threadIdx.x; i < L; i += blockDim.x) {
+    for (int k = threadIdx.x; k < L * F; k += OCC_THREADS) {
+      const int i = k / F, tk = tb + k % F;
       const int seg = s_seg[i];
-      if (seg >= 0) {
+      if (seg >= 0 && tk < t1) {
         const int* ord = s_ord + (seg >> 16);
         const int len = seg & 0xFFFF;
         double gm = 0.0;  // occurrences in position order
-        for (int j = 0; j < len; ++j) gm += s_q[2 * ord[j] + 1];
-        Gam[(long long)s_y[i] * M + row] = (float)gm;
+        for (int j = 0; j < len; ++j) gm += s_q[(2 * ord[j] + 1) * F + k % F];
+        Gam[(long long)s_y[i] * M + row0 + tk] = (float)gm;
       }
     }
-    if (threadIdx.x == 0) {
-      double b0 = s_bl[0], t0s = s_tot[0];
+    if (threadIdx.x < F && tb + (int)threadIdx.x < t1) {
+      const int fr = threadIdx.x;
+      double b0 = s_bl[0][fr], t0s = s_tot[0][fr];
 #pragma unroll
       for (int q = 1; q < NW; ++q) {
-        b0 += s_bl[q];
-        t0s += s_tot[q];
+        b0 += s_bl[q][fr];
+        t0s += s_tot[q][fr];
       }
-      Gam[row] = (float)b0;  // blank is U[0]
-      g[row] = t0s;
+      Gam[row0 + tb + fr] = (float)b0;  // blank is U[0]
+      g[row0 + tb + fr] = t0s;
     }
     lds_barrier();
   }
@@ -516,10 +533,25 @@ hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int ma
                             float* Gam, double* g) {
   if (N == 0 || max_T <= 0) return hipSuccess;
   const int Lcap = max_L > 0 ? max_L : 1;
-  const size_t shm = (2 * (size_t)Lcap + 1) * sizeof(double) + 3 * (size_t)Lcap * sizeof(int);
+  // frames per round: the most whose q block leaves room for four
+  // work-groups per CU (one frame whatever the length)
+  auto shm_of = [&](int F) {
+    return (size_t)F * (2 * (size_t)Lcap + 1) * sizeof(double) + 3 * (size_t)Lcap * sizeof(int);
+  };
+  int F = 8;
+  while (F > 1 && shm_of(F) > 40 * 1024) F >>= 1;
+  const size_t shm = shm_of(F);
   dim3 grid(N, (max_T + OCC_FRAMES - 1) / OCC_FRAMES);
-  k_occupancy<<<grid, OCC_THREADS, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status,
-                                              utt_logp, dp_off, alpha, beta, Gam, g, Lcap);
+#define PCX_OCC(FR)                                                                          \
+  k_occupancy<FR><<<grid, OCC_THREADS, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status, \
+                                                  utt_logp, dp_off, alpha, beta, Gam, g, Lcap)
+  switch (F) {
+    case 8: PCX_OCC(8); break;
+    case 4: PCX_OCC(4); break;
+    case 2: PCX_OCC(2); break;
+    default: PCX_OCC(1); break;
+  }
+#undef PCX_OCC
   return hipGetLastError();
 }
 
