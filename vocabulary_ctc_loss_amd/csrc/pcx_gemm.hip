@@ -763,6 +763,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   __shared__ float s_rs[BM];
   __shared__ double s_g[BM];
   __shared__ float s_db[C::WGM][BN];
+  __shared__ int s_list[BN], s_pos[BN], s_cnt[BN / 64];
   int mt, nt;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
@@ -788,6 +789,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   const bool rows_full = m0 + BM <= M;
+  // Many selected columns in some wavefront: the whole work-group takes the
+  // dense pass below.  (Also a barrier: every wavefront is done with the
+  // operand stages, which that pass reuses.)
+  const bool dense = __syncthreads_or(pre.n > SEL_DENSE) != 0;
   // Unselected classes on the accumulators, four rows at a time; selected
   // classes (role 2) and columns past the chunk (role 3) are skipped here.
   int csel[C::FN], crole[C::FN];
@@ -826,29 +831,67 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     }
   }
   // Selected classes: dZ needs no recomputed logit, only S, Gamma and g.
-  // With few of them in this wavefront (the large-vocabulary case) each is
-  // done by all 64 lanes in the pass further down; with many, every lane
-  // does its own here.
-  const bool dense = pre.n > SEL_DENSE;
+  // With few of them in each wavefront (the large-vocabulary case) each is
+  // done by all 64 lanes of its wavefront in the pass further down.  With
+  // many, the work-group forms them in batches in the free operand stages:
+  // one thread per tile row reads a selected column's S and Gamma (class-
+  // major, so these reads are contiguous), and each lane then takes its own
+  // elements from there.
   if (dense) {
+    // the selected tile columns in ascending order, and each one's place
+    bool is_sel = false;
+    int before = 0;
+    if (threadIdx.x < BN) {
+      is_sel = s_sel[threadIdx.x] >= 0;  // -1 past the chunk end
+      const unsigned long long bal = __ballot(is_sel);
+      before = __popcll(bal & ((1ull << lane) - 1ull));
+      if (lane == 0) s_cnt[w] = __popcll(bal);
+    }
+    lds_barrier();
+    int n_sel = 0, base = 0;
 #pragma unroll
-    for (int fj = 0; fj < C::FN; ++fj) {
-      if (crole[fj] != 2) continue;
-      const float* Sp = S + (long long)csel[fj] * M + m0;
-      const float* Gp = Gam + (long long)csel[fj] * M + m0;
-#pragma unroll
-      for (int fi = 0; fi < C::FM; ++fi)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(fi, r);
-          if (rows_full || m0 + row < M) {
-            // S <= 0 (a log-probability)
-            const float dz =
-                (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
-            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
-            cs[fj] += dz;
-          }
+    for (int q = 0; q < BN / 64; ++q) {
+      base += q < w ? s_cnt[q] : 0;
+      n_sel += s_cnt[q];
+    }
+    if (threadIdx.x < BN) {
+      s_pos[threadIdx.x] = is_sel ? base + before : -1;
+      if (is_sel) s_list[base + before] = threadIdx.x;
+    }
+    lds_barrier();
+    float* tmp = reinterpret_cast<float*>(smem);
+    constexpr int PADR = BM + 1;  // column stride: conflict-free both ways
+    constexpr int CAP = C::STAGE_BYTES / (PADR * (int)sizeof(float));
+    for (int k0 = 0; k0 < n_sel; k0 += CAP) {
+      const int kn = min(CAP, n_sel - k0);
+      for (int idx = threadIdx.x; idx < kn * BM; idx += C::THREADS) {
+        const int kk = idx / BM, row = idx - kk * BM;
+        float dz = 0.f;
+        if (rows_full || m0 + row < M) {
+          const long long o = (long long)s_sel[s_list[k0 + kk]] * M + m0 + row;
+          // S <= 0 (a log-probability)
+          dz = (float)(grad * (s_g[row] * exp_nonpos((double)S[o]) - (double)Gam[o]));
         }
+        tmp[kk * PADR + row] = dz;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj) {
+        const int slot = s_pos[acc_col<C>(fj)] - k0;
+        if (crole[fj] != 2 || slot < 0 || slot >= kn) continue;
+#pragma unroll 1
+        for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = acc_row<C>(fi, r);
+            if (rows_full || m0 + row < M) {
+              const float dz = tmp[slot * PADR + row];
+              dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
+              cs[fj] += dz;
+            }
+          }
+      }
+      lds_barrier();
     }
   }
   // column sum: the two lane halves hold the same column, then the waves
