@@ -476,6 +476,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   __shared__ __attribute__((aligned(16))) float s_bias[2][C::BM];
   __shared__ float f_m[C::WGM][C::BN];
   __shared__ double f_s[C::WGM][C::BN];
+  __shared__ int s_any[2][C::WAVES];  // per wavefront: a selected row among its loads
 
   int ft, sp;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), ftiles, nspan, ft, sp);
@@ -495,10 +496,17 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
   for (int v0 = c_begin; v0 < c_end; v0 += C::BM, par ^= 1) {
     // this tile's row data: visible after the GEMM's barriers; the buffer
     // written here was last read two tiles ago
+    bool any_sel = false;
     for (int r = threadIdx.x; r < C::BM; r += C::THREADS) {
       const int v = v0 + r;
-      s_sel[par][r] = v < c_end ? col2sel[v] : -2;  // -2: past the span
+      const int sl = v < c_end ? col2sel[v] : -2;  // -2: past the span
+      s_sel[par][r] = sl;
       s_bias[par][r] = (bias != nullptr && v < c_end) ? Elem<T>::to_f32(bias[v]) : 0.f;
+      any_sel |= sl >= 0;
+    }
+    {
+      const unsigned long long b = __ballot(any_sel);
+      if (lane == 0) s_any[par][w] = b != 0ull;
     }
     f32x16 acc[C::FM][C::FN];
     gemm_tile_run<C, true, true>(pf, W, D, v0, c_end, X, D, f0, M, 0, D, vec_ok, vec_ok, acc,
@@ -506,9 +514,32 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
     if (v0 + C::BM < c_end)
       gemm_prefetch<C, true, true>(pf, W, D, v0 + C::BM, c_end, X, D, f0, M, 0, D, vec_ok,
                                    vec_ok);
+    // selected vocabulary rows of this tile into Zsel (most tiles of a large
+    // vocabulary have none, and skip this as a whole)
+    bool tile_sel = false;
+#pragma unroll
+    for (int q = 0; q < C::WAVES; ++q) tile_sel |= s_any[par][q] != 0;
+    if (tile_sel) {
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj) {
+        const int frame = f0 + acc_col<C>(fj);
+#pragma unroll
+        for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r0 = acc_row<C>(fi, 4 * q);
+            const int4 sel4 = *reinterpret_cast<const int4*>(&s_sel[par][r0]);
+            const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_bias[par][r0]);
+            const int sl[4] = {sel4.x, sel4.y, sel4.z, sel4.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (sl[e] >= 0 && frame < M)
+                Zsel[(long long)sl[e] * M + frame] = acc[fi][fj][4 * q + e] + b4[e];
+          }
+      }
+    }
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
-      const int frame = f0 + acc_col<C>(fj);
       float mx = -INFINITY;
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi)
@@ -525,7 +556,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
             // only the unselected ones
             acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
-            if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
         }
       double sum = 0.0;
