@@ -1025,7 +1025,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_grad_reduce(
     const float* __restrict__ part, int splitk, int rows, int D, T* __restrict__ dW,
     long long row_base, const float* __restrict__ dbpart, int mtiles, int cols, int ld,
-    T* __restrict__ db, long long col_base, int nb_db) {
+    T* __restrict__ db, long long col_base, int nb_db, int vec4) {
   if ((int)blockIdx.x < nb_db) {
     __shared__ float gs[DB_GROUPS][DB_COLS];
     const int lc = threadIdx.x % DB_COLS, q = threadIdx.x / DB_COLS;
@@ -1049,8 +1049,26 @@ __global__ __launch_bounds__(256) void k_grad_reduce(
   }
   const long long n = (long long)rows * D;
   const long long stride = (long long)(gridDim.x - nb_db) * blockDim.x;
-  for (long long i = (blockIdx.x - nb_db) * (long long)blockDim.x + threadIdx.x; i < n;
-       i += stride) {
+  const long long i0 = (blockIdx.x - nb_db) * (long long)blockDim.x + threadIdx.x;
+  if (vec4) {
+    // four consecutive elements per thread (16-byte partial loads); the
+    // same split order per element
+    for (long long i = i0; i < n / 4; i += stride) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < splitk; ++k)
+        s += *reinterpret_cast<const f32x4*>(part + (long long)k * n + 4 * i);
+      T o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
+      T* dst = dW + row_base * D + 4 * i;
+      if (sizeof(T) == 4)
+        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(o);
+      else
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(o);
+    }
+    return;
+  }
+  for (long long i = i0; i < n; i += stride) {
     float s = 0.f;
     for (int k = 0; k < splitk; ++k) s += part[(long long)k * n + i];
     dW[row_base * D + i] = Elem<T>::from_f32(s);
@@ -2016,17 +2034,25 @@ hipError_t launch_grad_reduce(hipStream_t st, int dtype, const float* part, int 
                               const float* dbpart, int mtiles, int cols, int ld, void* db,
                               long long col_base) {
   const long long n = dW ? (long long)rows * D : 0;
-  const int nb_dw = n ? grid_cap(n, 256) : 0;
+  // 16-byte partial loads when the rows' output starts on a four-element
+  // boundary (the partials themselves are 16-byte aligned when n is a
+  // multiple of four)
+  const size_t esz = dtype == 0 ? 4 : 2;
+  const int vec4 = n % 4 == 0 &&
+                   ((uintptr_t)dW + (uintptr_t)(row_base * D) * esz) % (4 * esz) == 0;
+  const int nb_dw = n ? grid_cap(vec4 ? n / 4 : n, 256) : 0;
   const int nb_db = (db && cols > 0) ? ceil_div(cols, DB_COLS) : 0;
   if (nb_dw + nb_db == 0) return hipSuccess;
   if (dtype == 0)
     k_grad_reduce<float><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
                                                        (float*)dW, row_base, dbpart, mtiles,
-                                                       cols, ld, (float*)db, col_base, nb_db);
+                                                       cols, ld, (float*)db, col_base, nb_db,
+                                                       vec4);
   else
     k_grad_reduce<bf16_t><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
                                                         (bf16_t*)dW, row_base, dbpart, mtiles,
-                                                        cols, ld, (bf16_t*)db, col_base, nb_db);
+                                                        cols, ld, (bf16_t*)db, col_base, nb_db,
+                                                        vec4);
   return hipGetLastError();
 }
 
