@@ -797,7 +797,11 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   int mt, nt;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
-  // Row and column data of the tile (visible after gemm_tile's barriers).
+  // The product's first k stage is requested before the tile's row and
+  // column data, so the two loads' latencies overlap.
+  Prefetch<C, true, true> pf;
+  gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok);
+  // Row and column data of the tile.
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
     s_sel[c] = v < c1 ? col2sel[v] : -1;
@@ -816,7 +820,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   SelPre<C> pre;
   sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam);
   f32x16 acc[C::FM][C::FN];
-  gemm_tile<C, true, true>(X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
+  gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   const bool rows_full = m0 + BM <= M;
   // Many selected columns in some wavefront: the whole work-group takes the
