@@ -1098,6 +1098,45 @@ __global__ void k_transpose(const T* __restrict__ src, int rows, int rows_pad, i
   }
 }
 
+// The same for 2-byte elements with 16-byte accesses on both sides (D and
+// ldd multiples of 8, 16-byte aligned src and dst): eight consecutive
+// elements of a source row are loaded and scattered into the LDS tile by
+// column; eight consecutive elements of a destination row are gathered from
+// it and stored.
+template <typename T>
+__global__ __launch_bounds__(256) void k_transpose16(const T* __restrict__ src, int rows,
+                                                     int rows_pad, int D, T* __restrict__ dst,
+                                                     int ldd) {
+  static_assert(sizeof(T) == 2, "2-byte elements");
+  __shared__ T t[64][66];  // t[d][c]
+  const int r0 = blockIdx.y * 64, d0 = blockIdx.x * 64;
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int r = i >> 3, v = i & 7;
+    const int rr = r0 + r, dd = d0 + v * 8;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (rr < rows && dd < D) x = *reinterpret_cast<const uint4*>(src + (long long)rr * D + dd);
+    const T* e = reinterpret_cast<const T*>(&x);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) t[v * 8 + j][r] = e[j];
+  }
+  lds_barrier();
+  for (int i = threadIdx.x; i < 512; i += 256) {
+    const int d = i >> 3, v = i & 7;
+    const int dd = d0 + d, rr = r0 + v * 8;
+    if (dd >= D) continue;
+    T* out = dst + (long long)dd * ldd + rr;
+    if (rr + 8 <= rows_pad) {
+      uint4 x;
+      T* e = reinterpret_cast<T*>(&x);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = t[d][v * 8 + j];
+      *reinterpret_cast<uint4*>(out) = x;
+    } else {
+      for (int j = 0; j < 8 && rr + j < rows_pad; ++j) out[j] = t[d][v * 8 + j];
+    }
+  }
+}
+
 __global__ void k_cast_bf16(const float* __restrict__ src, bf16_t* __restrict__ dst, long long n) {
   for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
        i += (long long)gridDim.x * blockDim.x)
@@ -1971,7 +2010,10 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
     const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
     const int Kp = big ? (Cc + 63) & ~63 : Cc;
     dim3 tg(ceil_div(D, 64), ceil_div(Kp, 64));
-    k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+    if (D % 8 == 0 && ldz % 8 == 0 && aligned16(Wc) && aligned16(wt))
+      k_transpose16<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+    else
+      k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
     if (big) {
       using C = CfgBigDx;
       const int grid = ceil_div(M, C::BM) * ceil_div(D, C::BN);
