@@ -94,6 +94,11 @@ def case(name):
     if name == "bf16_head":
         return workloads.make_random(14, N=3, T_lo=30, T_hi=90, V=900, D=136, chunk=256,
                                      dtype="bf16")
+    # bf16 with D and the chunk width not multiples of 8: scalar staging and
+    # the element-wise weight-chunk transpose
+    if name == "bf16_odd_D":
+        return workloads.make_random(24, N=3, T_lo=10, T_hi=50, V=77, D=13, chunk=30,
+                                     dtype="bf16")
     # bf16 heads with D and the chunk width multiples of 64 run on the 256 x 256
     # core: one ragged frame tile and one ragged vocabulary tile, the chunk
     # narrower than a tile
@@ -137,8 +142,8 @@ def case(name):
 
 CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
          "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
-         "long_targets", "max_target", "many_utts", "one_utt", "bf16_llm", "bf16_head", "bf16_big_ragged",
-         "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120",
+         "long_targets", "max_target", "many_utts", "one_utt", "bf16_llm", "bf16_head",
+         "bf16_odd_D", "bf16_big_ragged", "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120",
          "f32_bf16w_head", "f32_bf16w_llm"]
 
 
