@@ -133,7 +133,7 @@ def main():
         copy_probe()
         return
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: pcx has no multi-GPU path "
               "(asked for --gpus %d)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import torch

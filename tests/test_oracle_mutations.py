@@ -15,6 +15,8 @@ or the first label and end on the last label or the final blank.
 """
 import os
 
+import numpy as np
+
 import pytest
 
 import oracle
@@ -93,11 +95,14 @@ def _failures(lib_path):
     oracle._default = oracle.Oracle(lib_path)
     failed = []
     try:
-        for name, fn, kw in _calls():
-            try:
-                fn(**kw)
-            except Exception as e:  # an assertion, or the oracle rejecting its input
-                failed.append("%s%s: %s" % (name, kw or "", type(e).__name__))
+        # a planted mistake can zero a gradient or make a value infinite; the
+        # pins then fail on the comparison, and numpy's warnings are noise
+        with np.errstate(all="ignore"):
+            for name, fn, kw in _calls():
+                try:
+                    fn(**kw)
+                except Exception as e:  # an assertion, or the oracle rejecting its input
+                    failed.append("%s%s: %s" % (name, kw or "", type(e).__name__))
     finally:
         oracle._default = saved
     return failed
