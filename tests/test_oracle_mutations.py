@@ -16,7 +16,6 @@ or the first label and end on the last label or the final blank.
 import os
 
 import numpy as np
-
 import pytest
 
 import oracle
