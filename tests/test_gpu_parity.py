@@ -133,6 +133,14 @@ def case(name):
     if name == "f32_bf16w_head":
         return workloads.make_random(20, N=4, T_lo=40, T_hi=110, V=5000, D=64, chunk=1024,
                                      dtype="f32_bf16w")
+    # dX alone on the 256 x 256 core with at least two frame tiles: frames in
+    # two parts, chunks in pairs (the last pair ragged: 7 x 128 + 4)
+    if name == "bf16_big_parts":
+        return workloads.make_random(25, N=6, T_lo=100, T_hi=140, V=900, D=64, chunk=128,
+                                     dtype="bf16")
+    if name == "f32_bf16w_parts":
+        return workloads.make_random(26, N=5, T_lo=60, T_hi=110, V=1500, D=64, chunk=256,
+                                     dtype="f32_bf16w")
     if name == "f32_bf16w_llm":
         return workloads.make_random(21, N=3, T_lo=50, T_hi=100, V=3000, D=128, blank=2999,
                                      chunk=4096, dtype="f32_bf16w", llm_head=True,
@@ -215,6 +223,25 @@ def test_nonfinite_input_utterance_is_excluded(name):
     keep = np.ones(bt.M, bool)
     keep[row_off[2]:row_off[3]] = False
     assert rel_fro(got["dX"][keep], ref["dX"][keep]) <= tol
+
+
+@pytest.mark.parametrize("name,grouped", [("tiles", False), ("tiles", True),
+                                          ("bf16_big_parts", False), ("f32_bf16w_parts", False)])
+def test_dx_only_frame_parts(name, grouped):
+    """With dX alone requested the backward takes the frames in two parts and
+    the chunks in pairs (a half-height block of two chunks in the same
+    M x C elements): dX matches the oracle, and the all-gradients call (one
+    part, single chunks) up to the summation grouping."""
+    bt = case(name)
+    assert bt.M >= 2 * (256 if name.startswith("bf16_big") else 128) and bt.V > 2 * bt.chunk
+    print("case", name, "grouped", grouped, "M", bt.M, "V", bt.V, "C", bt.chunk, flush=True)
+    got = run_pcx(bt, want_dW=False, want_db=False, getters="light", grouped=grouped)
+    full = run_pcx(bt, getters="light", grouped=grouped)
+    ref = run_oracle(bt, want_dW=False, want_db=False)
+    tol = tolerance(bt)
+    assert got["loss"] == full["loss"]
+    assert rel_fro(got["dX"], ref["dX"]) <= tol
+    assert rel_fro(got["dX"], full["dX"]) <= (1e-2 if bt.dtype == "bf16" else 1e-6)
 
 
 def test_grad_scaling_and_skipped_outputs():

@@ -469,22 +469,33 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   }
 
   const int big = use_big_core(cdt, D, C, ctx->X, ctx->W);
-  const int mtiles = (M + rec_tile_rows(cdt, big) - 1) / rec_tile_rows(cdt, big);
-  ENSURE(dZ, (size_t)M * C * esz);
-  ENSURE(dbpart, (size_t)mtiles * C * sizeof(float));
+  const int rtile = rec_tile_rows(cdt, big);
+  const int nchunks = (V + C - 1) / C;
+  // dX only: the frames are taken in two parts and the chunks in pairs.  A
+  // part's dZ block is (part rows) x 2C, the same M x C elements, and each dX
+  // product reduces over 2C columns, so the fp32 dX accumulator is read and
+  // written once per pair of chunks instead of once per chunk.  (dW and db
+  // need every frame of a chunk in one block.)
+  const int G = (dX && !dW && !db && nchunks >= 2 && M >= 2 * rtile) ? 2 : 1;
+  const int CG = G * C;  // columns per group
+  // rows of the first part: whole row tiles, so the second starts on a tile
+  const int Mh = G == 1 ? M : ((M + 1) / 2 + rtile - 1) / rtile * rtile;
+  const int mtiles = (Mh + rtile - 1) / rtile;  // row tiles of the larger part
+  ENSURE(dZ, (size_t)Mh * CG * esz);
+  ENSURE(dbpart, (size_t)mtiles * CG * sizeof(float));
   float* dxacc = nullptr;
   if (dX) {
     if (cdt == PCX_F32) {
       dxacc = (float*)dX;
     } else {
       ENSURE(dXacc, (size_t)M * D * sizeof(float));
-      ENSURE(wt, (size_t)D * C * esz);
+      ENSURE(wt, (size_t)D * CG * esz);
       dxacc = (float*)ctx->dXacc.p;
     }
   }
   if (widen) {
-    ENSURE(w32, (size_t)C * D * sizeof(float));
-    if (ctx->b) ENSURE(b32, (size_t)C * sizeof(float));
+    ENSURE(w32, (size_t)CG * D * sizeof(float));
+    if (ctx->b) ENSURE(b32, (size_t)CG * sizeof(float));
   }
   // Split of the frame reduction of dW: enough work-groups to fill the chip,
   // at least 1024 frames per split; fixed for a given shape.
@@ -495,10 +506,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (splitk < 1) splitk = 1;
   if (dW) ENSURE(dwpart, (size_t)splitk * C * D * sizeof(float));
 
-  const int nchunks = (V + C - 1) / C;
-  for (int ch = 0; ch < nchunks; ++ch) {
-    const int c0 = ch * C, c1 = (c0 + C < V) ? c0 + C : V, Cc = c1 - c0;
-    // The products see the chunk's head rows as rows [w0, w0 + Cc) of Wk
+  const int ngroups = (V + CG - 1) / CG;
+  for (int gi = 0; gi < ngroups; ++gi) {
+    const int c0 = gi * CG, c1 = (c0 + CG < V) ? c0 + CG : V, Cc = c1 - c0;
+    // The products see the group's head rows as rows [w0, w0 + Cc) of Wk
     // (the head itself, or its fp32 copy for a bf16-stored head).
     const void* Wk = ctx->W;
     const void* bk = ctx->b;
@@ -514,21 +525,30 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       sel += c0;
       w0 = 0;
     }
-    LAUNCH(K_RECOMPUTE,
-           launch_recompute(st, cdt, ctx->X, Wk, bk, M, D, w0, w0 + Cc, sel,
-                            (const float*)ctx->lamf.p, (const double*)ctx->g.p, S,
-                            (const float*)ctx->Gam.p, grad_loss, ctx->dZ.p, C,
-                            (float*)ctx->dbpart.p, big, gu, ou));
-    if (dX)
-      LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, C, Wk, M, D, w0, w0 + Cc, dxacc, ch == 0,
-                             ctx->wt.p, big));
-    if (dW)
-      LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, C, ctx->X, M, D, w0, w0 + Cc,
-                             (float*)ctx->dwpart.p, splitk));
-    if (dW || db)
-      LAUNCH(K_REDUCE, launch_grad_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc, D,
-                                          dW, c0, (const float*)ctx->dbpart.p, mtiles, Cc, C,
-                                          db, c0));
+    for (int part = 0; part < G; ++part) {
+      // frames [r0, r0 + Mp); S and Gamma keep their leading dimension M
+      const int r0 = part == 0 ? 0 : Mh;
+      const int Mp = (part == 0 ? Mh : M) - r0;
+      if (Mp <= 0) continue;
+      LAUNCH(K_RECOMPUTE,
+             launch_recompute(st, cdt, (const char*)ctx->X + (size_t)r0 * D * esz, Wk, bk, Mp,
+                              D, w0, w0 + Cc, sel, (const float*)ctx->lamf.p + r0,
+                              (const double*)ctx->g.p + r0, S + r0,
+                              (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, CG,
+                              (float*)ctx->dbpart.p, big, gu ? gu + r0 : nullptr,
+                              ou ? ou + r0 : nullptr, M));
+      if (dX)
+        LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, CG, Wk, Mp, D, w0, w0 + Cc,
+                               dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
+      // (G == 1 below: one part of all M frames)
+      if (dW)
+        LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, CG, ctx->X, M, D, w0, w0 + Cc,
+                               (float*)ctx->dwpart.p, splitk));
+      if (dW || db)
+        LAUNCH(K_REDUCE, launch_grad_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc,
+                                            D, dW, c0, (const float*)ctx->dbpart.p, mtiles, Cc,
+                                            CG, db, c0));
+    }
   }
   if (dX && cdt != PCX_F32)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));

@@ -173,14 +173,17 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const int* col2sel, const float* lamf, const double* g,
                             const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart, int big,
-                            const double* gu = nullptr, const float* ou = nullptr);
-// wt: D x ldz scratch for the transposed weight chunk (bf16 only).
+                            const double* gu = nullptr, const float* ou = nullptr,
+                            long long ldS = 0);  // S / Gamma leading dimension (0: M)
+// wt: D x ldz scratch for the transposed weight chunk (bf16 only); with
+// stage_wt == 0 it already holds these columns (an earlier call staged them).
 // Rows of the recompute tile (one bias-gradient partial per row tile) and
 // the number of output tiles of one dW product.
 int rec_tile_rows(int dtype, int big);
 int dw_tiles(int dtype, int C, int D);
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
-                     int M, int D, int c0, int c1, float* dXacc, int first, void* wt, int big);
+                     int M, int D, int c0, int c1, float* dXacc, int first, void* wt, int big,
+                     int stage_wt = 1);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
 // dW rows [row_base, row_base + rows) from the split partials and db

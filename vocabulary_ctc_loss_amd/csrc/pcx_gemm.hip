@@ -692,11 +692,11 @@ struct SelPre {
 };
 
 // s_sel[c]: selected index of tile column c (or -1); columns at or past c1
-// are never selected.
+// are never selected.  S and Gamma are class-major with leading dimension ldS.
 template <class C>
 __device__ __forceinline__ void sel_prefetch(SelPre<C>& p, const int* s_sel, int n0, int c1,
                                              int m0, int M, const float* __restrict__ S,
-                                             const float* __restrict__ Gam) {
+                                             const float* __restrict__ Gam, long long ldS) {
   static_assert(C::WM % 64 == 0, "selected-class pass: whole rows per lane");
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN, wn = w % C::WGN;
   unsigned long long mk[C::FN];
@@ -730,8 +730,8 @@ __device__ __forceinline__ void sel_prefetch(SelPre<C>& p, const int* s_sel, int
     for (int t = 0; t < SelPre<C>::RPL; ++t) {
       const int row = wm * C::WM + SelPre<C>::RPL * lane + t;
       const bool ok = found && m0 + row < M;
-      p.s[k][t] = ok ? S[(long long)sel * M + m0 + row] : 0.f;
-      p.g[k][t] = ok ? Gam[(long long)sel * M + m0 + row] : 0.f;
+      p.s[k][t] = ok ? S[sel * ldS + m0 + row] : 0.f;
+      p.g[k][t] = ok ? Gam[sel * ldS + m0 + row] : 0.f;
     }
   }
 }
@@ -782,7 +782,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const int* __restrict__ col2sel, const float* __restrict__ lamf,
     const double* __restrict__ g, const float* __restrict__ S, const float* __restrict__ Gam,
     double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
-    int mtiles, int vec_ok, const double* __restrict__ gu, const float* __restrict__ lamu) {
+    int mtiles, int vec_ok, const double* __restrict__ gu, const float* __restrict__ lamu,
+    long long ldS) {
   using T = typename C::type;
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
@@ -818,7 +819,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   }
   lds_barrier();
   SelPre<C> pre;
-  sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam);
+  sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam, ldS);
   f32x16 acc[C::FM][C::FN];
   gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
@@ -902,7 +903,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
         const int kk = idx / BM, row = idx - kk * BM;
         float dz = 0.f;
         if (rows_full || m0 + row < M) {
-          const long long o = (long long)s_sel[s_list[k0 + kk]] * M + m0 + row;
+          const long long o = s_sel[s_list[k0 + kk]] * ldS + m0 + row;
           // S <= 0 (a log-probability)
           dz = (float)(grad * (s_g[row] * exp_nonpos((double)S[o]) - (double)Gam[o]));
         }
@@ -1500,7 +1501,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const float* __restrict__ lamf, const double* __restrict__ g, const float* __restrict__ S,
     const float* __restrict__ Gam, double grad, bf16_t* __restrict__ dZ, int ldz,
     float* __restrict__ dbpart, int mtiles, const double* __restrict__ gu,
-    const float* __restrict__ lamu) {
+    const float* __restrict__ lamu, long long ldS) {
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
   // selected columns prefetched per wavefront: a fixed 24 KiB LDS region
@@ -1577,9 +1578,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       pcol[k] = col;
       if (found && pn <= SELP) {
         char* dst = smem + O_PRE + (w * SELP + k) * 512;
-        __builtin_amdgcn_global_load_lds((const void*)(S + (long long)sel * M + grow),
+        __builtin_amdgcn_global_load_lds((const void*)(S + sel * ldS + grow),
                                          PCX_LDS_PTR(dst), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds((const void*)(Gam + (long long)sel * M + grow),
+        __builtin_amdgcn_global_load_lds((const void*)(Gam + sel * ldS + grow),
                                          PCX_LDS_PTR(dst + 256), 4, 0, 0);
       }
     }
@@ -1742,8 +1743,8 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
       if (crole[fj] != 2 || csel[fj] < 0) continue;
-      const float* Sp = S + (long long)csel[fj] * M + m0;
-      const float* Gp = Gam + (long long)csel[fj] * M + m0;
+      const float* Sp = S + csel[fj] * ldS + m0;
+      const float* Gp = Gam + csel[fj] * ldS + m0;
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi) {
 #pragma unroll
@@ -1956,7 +1957,7 @@ template <typename T>
 hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                        int c0, int c1, const int* col2sel, const float* lamf, const double* g,
                        const float* S, const float* Gam, double grad, void* dZ, int ldz,
-                       float* dbpart, const double* gu, const float* lamu) {
+                       float* dbpart, const double* gu, const float* lamu, long long ldS) {
   using C = typename Pick<T>::rec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
@@ -1964,7 +1965,7 @@ hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void*
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
   k_recompute<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, c0, c1,
                                                col2sel, lamf, g, S, Gam, grad, (T*)dZ, ldz,
-                                               dbpart, mtiles, vec, gu, lamu);
+                                               dbpart, mtiles, vec, gu, lamu, ldS);
   return hipGetLastError();
 }
 
@@ -1972,13 +1973,14 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             int M, int D, int c0, int c1, const int* col2sel, const float* lamf,
                             const double* g, const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart, int big, const double* gu,
-                            const float* lamu) {
+                            const float* lamu, long long ldS) {
+  if (ldS <= 0) ldS = M;
   if (dtype == 0)
     return recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ, ldz,
-                              dbpart, gu, lamu);
+                              dbpart, gu, lamu, ldS);
   if (!big)
     return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
-                               ldz, dbpart, gu, lamu);
+                               ldz, dbpart, gu, lamu, ldS);
   using C = CfgBigRec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
@@ -1986,12 +1988,13 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
   k_recompute_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)X, (const bf16_t*)W,
                                                    (const bf16_t*)b, M, D, c0, c1, col2sel, lamf,
                                                    g, S, Gam, grad, (bf16_t*)dZ, ldz, dbpart,
-                                                   mtiles, gu, lamu);
+                                                   mtiles, gu, lamu, ldS);
   return hipGetLastError();
 }
 
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W, int M,
-                     int D, int c0, int c1, float* dXacc, int first, void* wt, int big) {
+                     int D, int c0, int c1, float* dXacc, int first, void* wt, int big,
+                     int stage_wt) {
   const int Cc = c1 - c0;
   if (dtype == 0) {
     using C = Pick<float>::dx;
@@ -2009,11 +2012,14 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
     // are zero.
     const bf16_t* Wc = (const bf16_t*)W + (long long)c0 * D;
     const int Kp = big ? (Cc + 63) & ~63 : Cc;
+    // (stage_wt == 0: staged by an earlier call on the same columns)
     dim3 tg(ceil_div(D, 64), ceil_div(Kp, 64));
-    if (D % 8 == 0 && ldz % 8 == 0 && aligned16(Wc) && aligned16(wt))
-      k_transpose16<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
-    else
-      k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+    if (stage_wt) {
+      if (D % 8 == 0 && ldz % 8 == 0 && aligned16(Wc) && aligned16(wt))
+        k_transpose16<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+      else
+        k_transpose<bf16_t><<<tg, 256, 0, st>>>(Wc, Cc, Kp, D, (bf16_t*)wt, ldz);
+    }
     if (big) {
       using C = CfgBigDx;
       const int grid = ceil_div(M, C::BM) * ceil_div(D, C::BN);
