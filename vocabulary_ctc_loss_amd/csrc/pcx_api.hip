@@ -471,16 +471,18 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   const int big = use_big_core(cdt, D, C, ctx->X, ctx->W);
   const int rtile = rec_tile_rows(cdt, big);
   const int nchunks = (V + C - 1) / C;
-  // dX only: the frames are taken in two parts and the chunks in pairs.  A
-  // part's dZ block is (part rows) x 2C, the same M x C elements, and each dX
-  // product reduces over 2C columns, so the fp32 dX accumulator is read and
-  // written once per pair of chunks instead of once per chunk.  (dW and db
-  // need every frame of a chunk in one block.)
-  const int G = (dX && !dW && !db && nchunks >= 2 && M >= 2 * rtile) ? 2 : 1;
+  // dX only: the frames are taken in G parts and the chunks in groups of G.
+  // A part's dZ block is (part rows) x G C, the same M x C elements, and each
+  // dX product reduces over G C columns, so the fp32 dX accumulator is read
+  // and written once per group of chunks instead of once per chunk.  (dW
+  // and db need every frame of a chunk in one block.)
+  int G = 1;
+  if (dX && !dW && !db)
+    while (G < DX_PARTS && nchunks >= 2 * G && M >= 2 * G * rtile) G *= 2;
   const int CG = G * C;  // columns per group
-  // rows of the first part: whole row tiles, so the second starts on a tile
-  const int Mh = G == 1 ? M : ((M + 1) / 2 + rtile - 1) / rtile * rtile;
-  const int mtiles = (Mh + rtile - 1) / rtile;  // row tiles of the larger part
+  // rows per part: whole row tiles, so that every part starts on a tile
+  const int Mh = G == 1 ? M : ((M + G - 1) / G + rtile - 1) / rtile * rtile;
+  const int mtiles = (Mh + rtile - 1) / rtile;  // row tiles of the largest part
   ENSURE(dZ, (size_t)Mh * CG * esz);
   ENSURE(dbpart, (size_t)mtiles * CG * sizeof(float));
   float* dxacc = nullptr;
@@ -527,8 +529,8 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     }
     for (int part = 0; part < G; ++part) {
       // frames [r0, r0 + Mp); S and Gamma keep their leading dimension M
-      const int r0 = part == 0 ? 0 : Mh;
-      const int Mp = (part == 0 ? Mh : M) - r0;
+      const int r0 = part * Mh;
+      const int Mp = (r0 + Mh < M ? r0 + Mh : M) - r0;
       if (Mp <= 0) continue;
       LAUNCH(K_RECOMPUTE,
              launch_recompute(st, cdt, (const char*)ctx->X + (size_t)r0 * D * esz, Wk, bk, Mp,
