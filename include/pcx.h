@@ -122,7 +122,9 @@ void pcx_destroy(pcx_ctx* ctx);
  *   blank         blank class id in [0, V).
  *   chunk         vocabulary chunk width C >= 1 used by the backward pass for
  *                 its one M x C gradient block (App. B.1); results do not
- *                 depend on it beyond rounding.
+ *                 depend on it beyond rounding.  (A backward that wants dX
+ *                 alone fills the block as half the frames by 2C columns,
+ *                 the half rounded up to whole row tiles.)
  *   stream        hipStream_t (void*), NULL for the default stream.
  *   loss          host out, may be NULL: sum of the finite per-utterance
  *                 losses (unalignable / nonfinite ones contribute 0; the
