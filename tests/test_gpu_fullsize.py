@@ -10,7 +10,10 @@ The oracle cannot redo a whole V = 180k or LLM-head batch in seconds, so:
   at any size: every alignable frame's logit-gradient row sums to zero, so
   sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding;
 * the grouped formulation is held to the same sampled bar and compared with
-  the direct one on the whole batch.
+  the direct one on the whole batch;
+* the two small-vocabulary workloads (V = 500 and 5000), where the oracle
+  runs the whole batch in seconds, are compared output by output: every
+  utterance's loss, and all of dX, dW and db.
 """
 import numpy as np
 import pytest
@@ -85,3 +88,24 @@ def test_full_size_grouped_matches_oracle_and_direct(name):
         assert abs(g["utt_loss"][n] - ref["utt_loss"][j]) <= tol * abs(ref["utt_loss"][j])
     rows = np.concatenate([np.arange(row_off[n], row_off[n + 1]) for n in idx])
     assert rel_fro(g["dX"][rows], ref["dX"]) <= tol
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["v500", "v5k"])
+def test_full_size_whole_batch(name):
+    """Full size, no sampling: the oracle on the whole batch, every output
+    held to the element-wise bar."""
+    bt = workloads.make(name, seed=0)
+    print("workload", name, "M", bt.M, "V", bt.V, "D", bt.D, "N", bt.N, flush=True)
+    got = run_pcx(bt, want_dW=True, want_db=True, getters="light")
+    print("oracle on the whole batch", flush=True)
+    ref = oracle.pcx(bt.X, bt.W, bt.b, bt.frame_counts, bt.tgt_off, bt.tgt, bt.blank,
+                     want_lambda=False)
+    tol = tolerance(bt)
+    assert got["status"].tolist() == ref["status"].tolist()
+    assert abs(got["loss"] - ref["loss"]) <= tol * abs(ref["loss"])
+    assert rel_fro(got["utt_loss"], ref["utt_loss"]) <= tol
+    for k in ("dX", "dW", "db"):
+        e = rel_fro(got[k], ref[k])
+        print(k, "relative Frobenius error %.3g" % e, flush=True)
+        assert e <= tol, (k, e)
