@@ -542,7 +542,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       if (dX)
         LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, CG, Wk, Mp, D, w0, w0 + Cc,
                                dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
-      // (G == 1 below: one part of all M frames)
+      // dW and db are only wanted with G == 1: this part is all M frames
       if (dW)
         LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, CG, ctx->X, M, D, w0, w0 + Cc,
                                (float*)ctx->dwpart.p, splitk));
