@@ -113,3 +113,30 @@ def test_full_size_whole_batch(name):
         e = rel_fro(got[k], ref[k])
         print(k, "relative Frobenius error %.3g" % e, flush=True)
         assert e <= tol, (k, e)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["v180k", "llm152k"])
+def test_full_size_workspace(name):
+    """On the two large-vocabulary heads (V much larger than the chunk C) the
+    device workspace a context holds after a forward and a backward (read at
+    the following forward; it only grows) has no block of the batch's M x V
+    size: it stays under a quarter of one fp32 M x V logits matrix, and at
+    the V = 180k, M = 16k point within the 1.29 GiB of head and loss memory
+    the pages report for their own implementation ([P] Sec. 5.1, Fig. 4)."""
+    from vocabulary_ctc_loss_amd import Context
+    bt = workloads.make(name, seed=0)
+    c = Context()
+    try:
+        run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters=False, ctx=c)
+        got = run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters=False, ctx=c)
+    finally:
+        c.close()
+    ws = got["info"]["workspace_bytes"]
+    dense = bt.M * bt.V * 4
+    print(name, "workspace %.3f GiB, fp32 M x V %.3f GiB" % (ws / 2**30, dense / 2**30),
+          flush=True)
+    assert ws < dense / 4
+    if name == "v180k":
+        assert ws <= 1.29 * 2**30
+

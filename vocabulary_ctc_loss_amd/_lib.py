@@ -79,6 +79,12 @@ def load() -> ctypes.CDLL:
             raise ImportError(
                 "libpcx.so is not built (expected at %s); run "
                 "`python -m vocabulary_ctc_loss_amd.build` or __graft_entry__.build()" % LIB_PATH)
+        # torch first: it carries its own HIP runtime (same soname as the
+        # system one), and the library must bind to the runtime that owns
+        # the tensors' device memory and streams.  Loaded before torch it
+        # bound to the system runtime, and its first allocation on the
+        # device then failed ("no ROCm-capable device").
+        import torch  # noqa: F401
         lib = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)
