@@ -42,5 +42,29 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+C_EXAMPLE_SRC = os.path.join(ROOT, "tests", "c_abi", "pcx_c_run.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi", "pcx_c_run")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """Compile the plain-C program that drives the C ABI in the tests (gcc,
+    C11; HIP runtime API for device memory; libpcx.so found next to it by a
+    relative runpath)."""
+    rocm = os.path.dirname(os.path.dirname(HIPCC))
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-Wextra", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(rocm, "include"), "-I", os.path.join(ROOT, "include"),
+           C_EXAMPLE_SRC, "-L", HERE, "-lpcx", "-L", os.path.join(rocm, "lib"), "-lamdhip64",
+           "-Wl,-rpath,$ORIGIN/../../vocabulary_ctc_loss_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib"), "-o", C_EXAMPLE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        sys.stderr.write(r.stdout + r.stderr + "\n")
+        raise RuntimeError("gcc failed building the C ABI test program")
+    return C_EXAMPLE
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_example(verbose=True))
