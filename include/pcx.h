@@ -158,7 +158,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W,
  *   dW         device, V x D in the dtype of W, or NULL to skip.
  *   db         device, V in the dtype of b (that of W), or NULL to skip.
  * Outputs are overwritten, not accumulated.  Rows of excluded utterances get
- * exact zeros.  May be called more than once per forward.  No host sync.
+ * exact zeros.  May be called more than once per forward.  No host sync; once
+ * a first call on ctx has sized its workspace for these shapes, a call makes
+ * no allocation either (kernel launches on `stream` only), so it can be
+ * captured in a HIP graph and replayed.
  */
 pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
                         void* db, void* stream);
