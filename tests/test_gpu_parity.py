@@ -379,6 +379,33 @@ def test_device_side_validation_errors():
     c.close()
 
 
+def test_target_limit_and_offset_errors():
+    """A target one label over PCX_MAX_TARGET_LEN (2047) is refused with
+    PCX_ERR_LIMIT (the longest accepted one is the max_target parity case);
+    target offsets that do not start at 0, or decrease, with PCX_ERR_TARGET.
+    The context stays usable."""
+    import torch
+    from vocabulary_ctc_loss_amd import Context, PcxError
+    from pcx_harness import to_device
+    bt = workloads.make_random(27, N=1, T_lo=0, T_hi=0, V=60, D=8, chunk=64,
+                               frame_counts=[2100], target_lengths=[2048])
+    X, W, b, off, tgt, fc = to_device(bt)
+    c = Context()
+    with pytest.raises(PcxError) as e:
+        c.forward(X, W, b, off, tgt, fc, bt.blank, bt.chunk)
+    assert e.value.status == 7
+    bt = case("readme")
+    X, W, b, off, tgt, fc = to_device(bt)
+    for bad_off in ([1, 3, 5], [0, 4, 3]):   # the valid offsets are [0, 3, 5]
+        bad = torch.tensor(bad_off, dtype=torch.int32, device=X.device)
+        with pytest.raises(PcxError) as e:
+            c.forward(X, W, b, bad, tgt, fc, 0, 4)
+        assert e.value.status == 3, bad_off
+    loss, _ = c.forward(X, W, b, off, tgt, fc, 0, 4)
+    assert np.isfinite(loss)
+    c.close()
+
+
 def test_autograd_function():
     import torch
     from vocabulary_ctc_loss_amd import pruned_ctc_loss
