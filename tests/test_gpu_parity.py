@@ -138,6 +138,13 @@ def case(name):
     if name == "bf16_big_parts":
         return workloads.make_random(25, N=6, T_lo=100, T_hi=140, V=900, D=64, chunk=128,
                                      dtype="bf16")
+    # V a whole number of chunks (the last chunk full width; chunk pairs
+    # exact for a dX-only backward)
+    if name == "exact_chunks":
+        return workloads.make_random(28, N=5, T_lo=60, T_hi=110, V=1024, D=64, chunk=256)
+    if name == "bf16_big_exact":
+        return workloads.make_random(29, N=6, T_lo=100, T_hi=140, V=1024, D=64, chunk=256,
+                                     dtype="bf16")
     if name == "f32_bf16w_parts":
         return workloads.make_random(26, N=5, T_lo=60, T_hi=110, V=1500, D=64, chunk=256,
                                      dtype="f32_bf16w")
@@ -149,10 +156,10 @@ def case(name):
 
 
 CASES = ["readme", "tiles", "spans", "blank_last", "blank_mid", "odd_D", "v_lt_c",
-         "all_classes", "unalignable_mix", "single_alignment", "empty_targets",
-         "long_targets", "max_target", "many_utts", "one_utt", "bf16_llm", "bf16_head",
-         "bf16_odd_D", "bf16_big_ragged", "bf16_big_grads", "bf16_big_dense", "bf16_big_spans", "bf16_big_d5120",
-         "f32_bf16w_head", "f32_bf16w_llm"]
+         "all_classes", "unalignable_mix", "single_alignment", "empty_targets", "long_targets",
+         "max_target", "many_utts", "one_utt", "bf16_llm", "bf16_head", "bf16_odd_D",
+         "exact_chunks", "bf16_big_exact", "bf16_big_ragged", "bf16_big_grads", "bf16_big_dense",
+         "bf16_big_spans", "bf16_big_d5120", "f32_bf16w_head", "f32_bf16w_llm"]
 
 
 @pytest.mark.parametrize("name", CASES)
@@ -226,7 +233,8 @@ def test_nonfinite_input_utterance_is_excluded(name):
 
 
 @pytest.mark.parametrize("name,grouped", [("tiles", False), ("tiles", True),
-                                          ("bf16_big_parts", False), ("f32_bf16w_parts", False)])
+                                          ("bf16_big_parts", False), ("f32_bf16w_parts", False),
+                                          ("exact_chunks", False), ("bf16_big_exact", False)])
 def test_dx_only_frame_parts(name, grouped):
     """With dX alone requested the backward takes the frames in two parts and
     the chunks in pairs (a half-height block of two chunks in the same
