@@ -3,8 +3,10 @@
 Each case draws its own sizes: vocabulary size (tens to thousands), head
 width (multiples of 64, which the bf16 256 x 256 core takes, or not), chunk
 width (a multiple of 64 or ragged), blank position, utterance count and
-lengths, dtype (fp32, bf16, fp32 states with a bf16-stored head) and the
-formulation (direct or grouped).  The bar is the one of test_gpu_parity.py.
+lengths, dtype (fp32, bf16, fp32 states with a bf16-stored head), the
+formulation (direct or grouped) and, for every fourth seed, a backward that
+wants dX alone (frames in parts, chunks in groups where the batch allows).
+The bar is the one of test_gpu_parity.py.
 The draws are fixed by the case seed, so a failure names a reproducible
 shape.
 """
@@ -40,11 +42,13 @@ def draw(seed):
 @pytest.mark.parametrize("seed", SEEDS)
 def test_random_shape_parity(seed):
     bt, grouped = draw(seed)
+    full = seed % 4 != 3  # else dX alone
     print("seed", seed, bt.dtype, "grouped" if grouped else "direct", "N", bt.N, "M", bt.M,
-          "D", bt.D, "V", bt.V, "C", bt.chunk, "blank", bt.blank, flush=True)
-    got = run_pcx(bt, grouped=grouped)
+          "D", bt.D, "V", bt.V, "C", bt.chunk, "blank", bt.blank,
+          "all gradients" if full else "dX only", flush=True)
+    got = run_pcx(bt, grouped=grouped, want_dW=full, want_db=full)
     U, rel, flags = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
-    ref = run_oracle(bt, cols=U, want_gamma=True)
+    ref = run_oracle(bt, cols=U, want_gamma=True, want_dW=full, want_db=full)
     tol = tolerance(bt)
     assert got["U"].tolist() == U.tolist()
     assert got["rel"].tolist() == rel.tolist()
