@@ -225,7 +225,9 @@ pcx_status pcx_get_other(pcx_ctx* ctx, double* out, int64_t capacity);
  * pcx_profile_read waits for the recorded events and returns, for kernel
  * family i in [0, pcx_profile_count()), its name, the summed event-measured
  * duration in milliseconds and the number of launches since the last reset.
- * Off by default; enabling adds two event records per launch.
+ * Off by default; enabling adds two event records per launch.  When more
+ * than 4096 pairs are pending, pcx_forward folds them into the totals at its
+ * first synchronisation, so they stay bounded when nothing reads them.
  */
 pcx_status pcx_profile_enable(pcx_ctx* ctx, int32_t on);
 /* Restrict the timing to the kernel families whose bit is set in `mask`

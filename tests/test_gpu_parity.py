@@ -414,6 +414,42 @@ def test_target_limit_and_offset_errors():
     c.close()
 
 
+def test_profile_counts_and_mask():
+    """Per-family event timing: launch counts per step follow the chunking
+    (V = 700 in chunks of 200: four recompute, dX, dW and reduction launches
+    per backward, one forward product), they accumulate over steps that read
+    nothing, and a mask times only the families it names."""
+    import torch
+    from vocabulary_ctc_loss_amd import Context
+    from pcx_harness import to_device
+    bt = case("tiles")
+    X, W, b, off, tgt, fc = to_device(bt)
+    dX, dW, db = torch.empty_like(X), torch.empty_like(W), torch.empty_like(b)
+    c = Context()
+    c.profile_enable(True)
+    c.profile_reset()
+    steps = 5
+    for _ in range(steps):
+        c.forward(X, W, b, off, tgt, fc, bt.blank, bt.chunk)
+        c.backward(1.0, dX, dW, db)
+    prof = c.profile_read()
+    for fam, per_step in (("fwd_gemm_lse", 1), ("ctc_alpha_beta", 1), ("bwd_recompute_dz", 4),
+                          ("dx_gemm", 4), ("dw_gemm", 4), ("grad_reduce", 4)):
+        ms, n = prof[fam]
+        assert n == steps * per_step, (fam, n)
+        assert ms > 0.0, fam
+    c.profile_mask(["dx_gemm"])
+    c.profile_reset()
+    for _ in range(2):
+        c.forward(X, W, b, off, tgt, fc, bt.blank, bt.chunk)
+        c.backward(1.0, dX, dW, db)
+    prof = c.profile_read()
+    assert prof["dx_gemm"][1] == 8
+    assert all(n == 0 for fam, (_, n) in prof.items() if fam != "dx_gemm")
+    c.profile_enable(False)
+    c.close()
+
+
 def test_autograd_function():
     import torch
     from vocabulary_ctc_loss_amd import pruned_ctc_loss

@@ -131,6 +131,9 @@ hipEvent_t take_event(pcx_ctx* c) {
   return e;
 }
 
+// Pending timing pairs past which a forward folds them into the totals.
+constexpr size_t kMaxPendingTimed = 4096;
+
 // Collect finished event pairs into the per-kernel totals.
 void prof_drain(pcx_ctx* c) {
   for (Pending& p : c->pending) {
@@ -276,6 +279,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                                    (int*)ctx->U.p, (int*)ctx->tgt_rel.p, dmeta));
   PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
   PCX_HIP(hipStreamSynchronize(st));
+  // everything recorded so far on this stream has finished: past a few
+  // thousand pending timing events (nobody is reading them), fold them into
+  // the totals here, so that they stay bounded
+  if (ctx->pending.size() > kMaxPendingTimed) prof_drain(ctx);
   const Meta hm = *ctx->host_meta;
   if (hm.err & ERRBIT_LENGTHS)
     return fail(PCX_ERR_LENGTHS, "frame counts must be positive and sum to M=%d", iM);
