@@ -64,3 +64,46 @@ def test_two_contexts_on_two_streams():
     finally:
         for c, _, _, _ in jobs:
             c.close()
+
+
+def test_one_context_across_streams_with_growth():
+    """One context, a small batch on one side stream (its backward left in
+    flight), then a larger one on another stream: the workspace grows while
+    the first stream may still be working, and both results equal their
+    default-stream references bit for bit."""
+    import torch
+    from vocabulary_ctc_loss_amd import Context
+    small = workloads.make_random(30, N=2, T_lo=20, T_hi=40, V=300, D=64, chunk=64,
+                                  dtype="bf16")
+    large = _batches()[0][0]  # fp32 with all gradients: most buffers grow
+    jobs = [(small, False), (large, True)]
+    devs = [to_device(bt) for bt, _ in jobs]
+    torch.cuda.synchronize()
+    ref = []
+    for (bt, grads), dev in zip(jobs, devs):
+        c = Context()
+        loss, outs = _run(c, bt, dev, grads, None)
+        c.backward(0.6, *outs)
+        torch.cuda.synchronize()
+        ref.append((loss, [None if t is None else t.clone() for t in outs]))
+        c.close()
+    c = Context()
+    try:
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for s in streams:
+            s.wait_stream(torch.cuda.current_stream())
+        got = []
+        for (bt, grads), dev, s in zip(jobs, devs, streams):
+            with torch.cuda.stream(s):
+                loss, outs = _run(c, bt, dev, grads, s)
+                c.backward(0.6, *outs, stream=s)
+                got.append((loss, outs))
+        torch.cuda.synchronize()
+        for (loss, outs), (rloss, routs) in zip(got, ref):
+            assert loss == rloss
+            for k, (a, b) in enumerate(zip(outs, routs)):
+                if b is not None:
+                    assert torch.equal(a, b), k
+    finally:
+        c.close()
+

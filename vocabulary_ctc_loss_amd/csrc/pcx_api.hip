@@ -104,7 +104,10 @@ pcx_status ensure(pcx_ctx* c, DevBuf& b, size_t bytes, hipStream_t st) {
   if (bytes == 0) bytes = 16;
   if (b.cap >= bytes) return PCX_OK;
   if (b.p) {
-    PCX_HIP(hipStreamSynchronize(st));
+    // the old buffer may still be read by work of an earlier call, possibly
+    // on another stream: wait for the whole device before freeing it (growth
+    // is rare; a sized workspace never gets here)
+    PCX_HIP(hipDeviceSynchronize());
     PCX_HIP(hipFree(b.p));
     b.p = nullptr;
     b.cap = 0;
@@ -117,6 +120,7 @@ pcx_status ensure(pcx_ctx* c, DevBuf& b, size_t bytes, hipStream_t st) {
   }
   b.cap = bytes;
   (void)c;
+  (void)st;
   return PCX_OK;
 }
 
