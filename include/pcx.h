@@ -87,7 +87,10 @@ typedef struct {
 
 /* Create / destroy a context.  The context owns its device workspace, which
  * grows on demand (hipMalloc) and is released by pcx_destroy.  A context may
- * be used by one thread at a time. */
+ * be used by one thread at a time.  Its calls run in call order even when
+ * they name different streams: a call on another stream than the previous
+ * call's makes its stream wait for the previous one (except while that
+ * stream is being captured into a graph, whose capture the caller orders). */
 pcx_status pcx_create(pcx_ctx** out_ctx);
 void pcx_destroy(pcx_ctx* ctx);
 

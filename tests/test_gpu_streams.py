@@ -107,3 +107,45 @@ def test_one_context_across_streams_with_growth():
     finally:
         c.close()
 
+
+def test_one_context_across_streams_same_shapes():
+    """One context, the same shapes twice (so the workspace does not grow)
+    with different inputs, on two streams: the second call's forward must
+    not overwrite the scores, normalizer and recursions the first call's
+    backward, still in flight on the other stream, reads.  Calls on one
+    context follow each other across streams; both results equal their
+    default-stream references bit for bit."""
+    import torch
+    from vocabulary_ctc_loss_amd import Context
+    bt = _batches()[0][0]
+    dev1 = to_device(bt)
+    X2 = dev1[0] * 0.5
+    dev2 = (X2,) + tuple(dev1[1:])
+    torch.cuda.synchronize()
+    ref = []
+    for dev in (dev1, dev2):
+        c = Context()
+        loss, outs = _run(c, bt, dev, True, None)
+        c.backward(0.6, *outs)
+        torch.cuda.synchronize()
+        ref.append((loss, [t.clone() for t in outs]))
+        c.close()
+    c = Context()
+    try:
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+        got = []
+        for dev, st in zip((dev1, dev2), streams):
+            with torch.cuda.stream(st):
+                loss, outs = _run(c, bt, dev, True, st)
+                c.backward(0.6, *outs, stream=st)
+                got.append((loss, outs))
+        torch.cuda.synchronize()
+        for (loss, outs), (rloss, routs) in zip(got, ref):
+            assert loss == rloss
+            for k, (a, b) in enumerate(zip(outs, routs)):
+                assert torch.equal(a, b), k
+    finally:
+        c.close()
+

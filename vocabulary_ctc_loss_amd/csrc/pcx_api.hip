@@ -68,7 +68,9 @@ struct pcx_ctx {
   // forward state kept for backward / getters
   bool fwd_ok = false;
   bool bwd_done = false;
-  hipStream_t stream = nullptr;
+  hipStream_t stream = nullptr;  // stream of the latest call
+  bool stream_set = false;
+  hipEvent_t handoff = nullptr;  // orders a call after the previous one's stream
   const void* X = nullptr;
   const void* W = nullptr;
   const void* b = nullptr;
@@ -86,6 +88,30 @@ struct pcx_ctx {
   double prof_ms[K_COUNT] = {0};
   long long prof_n[K_COUNT] = {0};
 };
+
+namespace {
+
+// Calls on one context run in call order even when they come on different
+// streams: a call on another stream than the previous call's first makes its
+// stream wait for everything issued so far on that one.  (Not while the new
+// stream is being captured into a graph: a capture may not wait on work
+// recorded outside it, and whoever captures orders the capture stream.)
+pcx_status follow_last_call(pcx_ctx* c, hipStream_t st) {
+  if (c->stream_set && c->stream != st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    PCX_HIP(hipStreamIsCapturing(st, &cs));
+    if (cs == hipStreamCaptureStatusNone) {
+      if (!c->handoff) PCX_HIP(hipEventCreateWithFlags(&c->handoff, hipEventDisableTiming));
+      PCX_HIP(hipEventRecord(c->handoff, c->stream));
+      PCX_HIP(hipStreamWaitEvent(st, c->handoff, 0));
+    }
+  }
+  c->stream = st;
+  c->stream_set = true;
+  return PCX_OK;
+}
+
+}  // namespace
 
 namespace {
 
@@ -226,6 +252,7 @@ void pcx_destroy(pcx_ctx* c) {
     (void)hipEventDestroy(p.b);
   }
   for (hipEvent_t e : c->pool) (void)hipEventDestroy(e);
+  if (c->handoff) (void)hipEventDestroy(c->handoff);
   if (c->host_meta) (void)hipHostFree(c->host_meta);
   delete c;
 }
@@ -254,6 +281,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   if (L_tot > 0 && !tgt) return fail(PCX_ERR_ARG, "tgt is NULL");
   if (M > 0 && (!X || !W)) return fail(PCX_ERR_ARG, "X / W is NULL");
   hipStream_t st = (hipStream_t)stream;
+  {
+    const pcx_status s_ = follow_last_call(ctx, st);
+    if (s_ != PCX_OK) return s_;
+  }
   const int iM = (int)M, iD = (int)D, iV = (int)V;
   if (!ctx->host_meta) {
     hipError_t e = hipHostMalloc((void**)&ctx->host_meta, sizeof(Meta), hipHostMallocDefault);
@@ -371,7 +402,6 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   PCX_HIP(hipStreamSynchronize(st));
   const Meta fm = *ctx->host_meta;
 
-  ctx->stream = st;
   ctx->X = X;
   ctx->W = W;
   ctx->b = b;
@@ -419,6 +449,10 @@ pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta, 
   if (!d_eta) return fail(PCX_ERR_ARG, "d_eta is NULL");
   if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "pcx_blank_offset_grad needs a successful pcx_forward");
   hipStream_t st = (hipStream_t)stream;
+  {
+    const pcx_status s_ = follow_last_call(ctx, st);
+    if (s_ != PCX_OK) return s_;
+  }
   if (ctx->M == 0) {
     *d_eta = 0.0;
     return PCX_OK;
@@ -442,6 +476,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
   if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "pcx_backward needs a successful pcx_forward");
   hipStream_t st = (hipStream_t)stream;
+  {
+    const pcx_status s_ = follow_last_call(ctx, st);
+    if (s_ != PCX_OK) return s_;
+  }
   const int M = ctx->M, D = ctx->D, V = ctx->V, dt = ctx->dtype;
   const int C = ctx->chunk;
   // compute dtype of the products, and dtype of the head-shaped outputs
