@@ -450,6 +450,55 @@ def test_profile_counts_and_mask():
     c.close()
 
 
+def test_autograd_steps_reuse_pooled_contexts():
+    """The autograd function leases a context per graph and gets it back
+    when the graph is freed, so a training loop reuses sized workspaces.
+    Steps alternate two batches of different shapes; one step holds two live
+    graphs at once (a summed loss); one backward runs twice (retain_graph).
+    Every gradient matches the oracle, and the pool stays small."""
+    import gc
+    import torch
+    import vocabulary_ctc_loss_amd as pcx
+    from pcx_harness import to_device
+    batches = [case("blank_mid"), case("tiles")]
+    devs = [to_device(bt) for bt in batches]
+    refs = [run_oracle(bt, grad=1.0) for bt in batches]
+
+    def loss_of(i):
+        bt, (X, W, b, off, tgt, fc) = batches[i], devs[i]
+        X, W, b = (t.detach().clone().requires_grad_(True) for t in (X, W, b))
+        return pcx.pruned_ctc_loss(X, W, b, (off, tgt), fc, blank_id=bt.blank,
+                                   chunk_size=bt.chunk), (X, W, b)
+
+    def check(i, leaves, scale=1.0):
+        for t, k in zip(leaves, ("dX", "dW", "db")):
+            assert rel_fro(t.grad.double().cpu().numpy(), scale * refs[i][k]) <= 1e-5, (i, k)
+
+    used = set()
+    for step in range(4):
+        i = step % 2
+        loss, leaves = loss_of(i)
+        used.add(id(loss.grad_fn.lease.ctx))
+        loss.backward()
+        check(i, leaves)
+        del loss
+        gc.collect()
+    assert len(used) == 1  # one graph at a time: one context, reused
+    la, va = loss_of(0)
+    lb, vb = loss_of(1)
+    (la + lb).backward()
+    check(0, va)
+    check(1, vb)
+    loss, leaves = loss_of(1)
+    loss.backward(retain_graph=True)
+    loss.backward()
+    check(1, leaves, scale=2.0)
+    del la, lb, loss
+    gc.collect()
+    idle = pcx._POOL.get(torch.device("cuda:0").index, [])
+    assert 1 <= len(idle) <= pcx._POOL_KEEP
+
+
 def test_autograd_function():
     import torch
     from vocabulary_ctc_loss_amd import pruned_ctc_loss

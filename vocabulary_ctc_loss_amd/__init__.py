@@ -187,15 +187,43 @@ class Context:
         return out
 
 
+# Idle contexts per device, kept for the autograd function: a context goes
+# back here when the autograd graph that used it is freed (nothing can call
+# its backward any more), so later steps reuse a workspace that is already
+# sized instead of allocating and freeing it every step.
+_POOL = {}
+_POOL_KEEP = 4
+
+
+class _Lease:
+    """A context held by one autograd graph, returned to the pool when the
+    graph (and with it this object) is freed."""
+
+    def __init__(self, device):
+        self.device = device
+        idle = _POOL.setdefault(device, [])
+        self.ctx = idle.pop() if idle else Context()
+
+    def __del__(self):
+        try:
+            idle = _POOL.setdefault(self.device, [])
+            if len(idle) < _POOL_KEEP:
+                idle.append(self.ctx)
+            else:
+                self.ctx.close()
+        except Exception:
+            pass
+
+
 def _make_function():
     torch = _torch()
 
     class PcxLossFunction(torch.autograd.Function):
         @staticmethod
         def forward(fctx, X, W, b, tgt_off, tgt, frame_counts, blank, chunk):
-            c = Context()
-            loss, _ = c.forward(X, W, b, tgt_off, tgt, frame_counts, blank, chunk)
-            fctx.pcx = c
+            lease = _Lease(X.device.index)
+            loss, _ = lease.ctx.forward(X, W, b, tgt_off, tgt, frame_counts, blank, chunk)
+            fctx.lease = lease
             fctx.shapes = (X, W, b)
             return torch.tensor(loss, dtype=torch.float32, device=X.device)
 
@@ -206,7 +234,7 @@ def _make_function():
             dX = torch.empty_like(X) if need[0] else None
             dW = torch.empty_like(W) if need[1] else None
             db = torch.empty_like(b) if (b is not None and need[2]) else None
-            fctx.pcx.backward(float(grad.item()), dX, dW, db)
+            fctx.lease.ctx.backward(float(grad.item()), dX, dW, db)
             return dX, dW, db, None, None, None, None, None
 
     return PcxLossFunction
