@@ -1792,8 +1792,11 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
                                                           float* __restrict__ dXacc, int first) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int ntiles = (D + C::BN - 1) / C::BN;
-  const int lin = xcd_tile(blockIdx.x, gridDim.x);
-  const int nt = lin % ntiles, mt = lin / ntiles;
+  // tiles in groups of 4 row tiles: the 32 work-groups an XCD runs at once
+  // cover 4 x 8 tiles, 12 operand panels (2 x 16, 18 panels, with column
+  // tiles fastest; 4.5% slower on the LLM head)
+  int nt, mt;
+  grouped_tile<4>(xcd_tile(blockIdx.x, gridDim.x), (M + C::BM - 1) / C::BM, ntiles, mt, nt);
   const int m0 = mt * C::BM, n0 = nt * C::BN;
   f32x16 acc[C::FM][C::FN];
   gemm_big1<C>(dZ, ldz, m0, M, Wt, ldz, n0, D, Kp, acc, smem);
