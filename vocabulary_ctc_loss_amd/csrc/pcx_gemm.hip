@@ -1525,8 +1525,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   float* s_lam2 = reinterpret_cast<float*>(smem + O_LAM);
   float* s_rs = reinterpret_cast<float*>(smem + O_RS);
   float (*s_db)[BN] = reinterpret_cast<float (*)[BN]>(smem + O_DB);
+  // groups of 4 row tiles (measured 1.2% ahead of 8 and 2 on the LLM head)
   int mt, nt;
-  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
+  grouped_tile<4>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
   const int c_pad = c0 + ((c1 - c0 + 63) & ~63);
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
