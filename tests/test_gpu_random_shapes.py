@@ -19,7 +19,7 @@ from pcx_harness import rel_fro, run_oracle, run_pcx, tolerance
 
 pytestmark = pytest.mark.gpu
 
-SEEDS = list(range(100, 164))
+SEEDS = list(range(100, 356))
 
 
 def draw(seed):
