@@ -1,11 +1,12 @@
 // Validation, structural alignability and selected-class construction.
 //
 // "Pruned CTC for Memory-Efficient Large-Vocabulary ASR Training":
-//  * App. B.1: a target with r_n adjacent identical label pairs needs at
-//    least |y_n| + r_n frames; this defines the alignable utterances.
-//  * App. B.1 / Sec. 3.2: the selected classes U are blank first, then the
-//    sorted distinct target labels of the batch; targets are relabelled with
-//    their index in U.
+//  * App. B.1: every repeated adjacent label pair forces one extra blank
+//    frame, so an utterance is alignable when T_n >= |y_n| + r_n (r_n such
+//    pairs in y_n).
+//  * App. B.1 / Sec. 3.2: U holds the blank at index 0 and after it the
+//    batch's distinct target labels in ascending order; each target label is
+//    replaced by its index in U.
 // Everything here is integer work; the results are unique and deterministic.
 #include "pcx_common.h"
 
