@@ -67,6 +67,16 @@ MUTANTS = [
      "flags[n] = (L + r < frame_counts[n]) ? 1 : 0;"),
     ("gradient_log_probability", "grad * (exp(lp[v]) - gam_row[v])",
      "grad * (lp[v] - gam_row[v])"),
+    ("gather_ignores_cols",
+     "Zn[(size_t)t * V + cols[c]] - lam[t];\n        if (gamma_cols)\n"
+     "          gamma_cols[(size_t)(row0 + t) * ncols + c] = gam[(size_t)t * V + cols[c]];",
+     "Zn[(size_t)t * V + c] - lam[t];\n        if (gamma_cols)\n"
+     "          gamma_cols[(size_t)(row0 + t) * ncols + c] = gam[(size_t)t * V + c];"),
+    ("logp_gather_ignores_cols", "Zn[(size_t)t * V + cols[c]] - lam[t];",
+     "Zn[(size_t)t * V + c] - lam[t];"),
+    ("gamma_gather_ignores_cols", "= gam[(size_t)t * V + cols[c]];", "= gam[(size_t)t * V + c];"),
+    ("gather_rows_of_first_utterance", "logp_cols[(size_t)(row0 + t) * ncols + c] =",
+     "logp_cols[(size_t)t * ncols + c] ="),
 ]
 
 

@@ -130,6 +130,44 @@ def test_brute_force_through_head():
     assert out["loss"] == pytest.approx(expected, rel=1e-12)
 
 
+def test_column_gather_at_unsorted_columns():
+    """logp_cols / gamma_cols at an unsorted, non-identity column list.
+
+    The scores S and occupancies Gamma of the reduced method are indexed by
+    the selected classes U ("Pruned CTC for Memory-Efficient Large-Vocabulary
+    ASR Training", Sec. 3.2), so the oracle's per-column outputs must be the
+    log-probability and occupancy of class cols[c], not of class c.  Checked
+    on a three-utterance batch against numpy's log-softmax of X W^T + b and
+    against brute-force occupancies of every utterance.
+    """
+    rng = np.random.default_rng(31)
+    V, D = 5, 3
+    T = [6, 5, 4]
+    ys = [[1, 3], [4, 4], [2]]
+    M = sum(T)
+    X = rng.normal(size=(M, D))
+    W = rng.normal(size=(V, D))
+    b = rng.normal(size=V)
+    off = np.concatenate([[0], np.cumsum([len(y) for y in ys])])
+    tgt = np.concatenate(ys)
+    cols = [V - 1, 0, 3, 2]
+    out = oracle.pcx(X, W, b, T, off, tgt, blank=0, cols=cols, want_gamma=True)
+    Z = X @ W.T + b
+    zmax = Z.max(1, keepdims=True)
+    logp = Z - zmax - np.log(np.sum(np.exp(Z - zmax), 1, keepdims=True))
+    np.testing.assert_allclose(out["logp_cols"], logp[:, cols], rtol=1e-13, atol=1e-13)
+    row = 0
+    for n, y in enumerate(ys):
+        rows = slice(row, row + T[n])
+        _, gamma, count, _ = brute_force(Z[rows], y, 0)
+        assert count > 0
+        np.testing.assert_allclose(out["gamma_cols"][rows], gamma[:, cols], rtol=1e-10,
+                                   atol=1e-13)
+        row += T[n]
+    # the gathered columns differ from the first len(cols) classes
+    assert not np.allclose(out["logp_cols"], logp[:, :len(cols)])
+
+
 # ----------------------------------------------------------- closed forms
 def test_readme_example_golden():
     g = json.load(open(os.path.join(GOLDEN, "readme_example.json")))
