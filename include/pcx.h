@@ -46,7 +46,10 @@ typedef enum {
   PCX_ERR_LENGTHS = 4, /* a frame count <= 0, or the counts do not sum to M */
   PCX_ERR_STATE = 5,   /* backward without a successful forward            */
   PCX_ERR_HIP = 6,     /* HIP runtime failure (allocation, launch, copy)   */
-  PCX_ERR_LIMIT = 7    /* a target longer than PCX_MAX_TARGET_LEN labels   */
+  PCX_ERR_LIMIT = 7,   /* a target longer than PCX_MAX_TARGET_LEN labels   */
+  PCX_ERR_WORKSPACE = 8 /* the allocation callback returned NULL, or the    */
+                        /* workspace would have to grow while the stream is */
+                        /* being captured into a graph                      */
 } pcx_status;
 
 /* How the normalizer and the gradient of the unselected classes are formed
@@ -85,13 +88,42 @@ typedef struct {
   int32_t lse_spans;       /* vocabulary spans of the forward normalizer fold */
 } pcx_fwd_info;
 
+/* Device-memory callbacks for a context's workspace, so that it can live in
+ * the caller's allocator and show in its memory accounting (the pages
+ * measure head-and-loss memory with the framework's allocated-memory
+ * counters, App. C.1; the PrunedCTC README keeps every tensor of a call on
+ * one device).
+ *   alloc(bytes, user, stream)  returns at least `bytes` bytes of device
+ *       memory on the current HIP device, for use by work ordered on
+ *       `stream` (a hipStream_t as void*, NULL = default stream), or NULL on
+ *       failure (the call then fails with PCX_ERR_WORKSPACE).
+ *   release(ptr, bytes, user, stream)  gives back a pointer alloc returned;
+ *       `stream` is the stream it was allocated on and `bytes` the size
+ *       asked for.  Every piece of library work that touches ptr is either
+ *       finished or ordered before the work already issued to `stream`, so
+ *       the memory may go to any work issued to that stream afterwards (the
+ *       contract of a stream-ordered caching allocator).
+ * Neither callback may call back into the library. */
+typedef void* (*pcx_alloc_fn)(size_t bytes, void* user, void* stream);
+typedef void (*pcx_free_fn)(void* ptr, size_t bytes, void* user, void* stream);
+
 /* Create / destroy a context.  The context owns its device workspace, which
- * grows on demand (hipMalloc) and is released by pcx_destroy.  A context may
- * be used by one thread at a time.  Its calls run in call order even when
- * they name different streams: a call on another stream than the previous
- * call's makes its stream wait for the previous one (except while that
- * stream is being captured into a graph, whose capture the caller orders). */
-pcx_status pcx_create(pcx_ctx** out_ctx);
+ * grows on demand and is released by pcx_destroy.
+ *   alloc, release  both NULL: the library allocates with hipMalloc, and
+ *                   growth waits for the whole device before hipFree;
+ *                   both set: the workspace comes from these callbacks, and
+ *                   growth waits for nothing when the buffer is released on
+ *                   the stream of the current call (otherwise the current
+ *                   stream is synchronised first).  One NULL and one set is
+ *                   PCX_ERR_ARG.
+ *   user            passed through to the callbacks.
+ * No HIP call is made here.  A context may be used by one thread at a time.
+ * Its calls run in call order even when they name different streams: a call
+ * on another stream than the previous call's makes its stream wait for the
+ * previous one (except while that stream is being captured into a graph,
+ * whose capture the caller orders).  pcx_destroy waits for the last call's
+ * stream before it releases the workspace. */
+pcx_status pcx_create(pcx_ctx** out_ctx, pcx_alloc_fn alloc, pcx_free_fn release, void* user);
 void pcx_destroy(pcx_ctx* ctx);
 
 /*
@@ -163,8 +195,13 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W,
  * Outputs are overwritten, not accumulated.  Rows of excluded utterances get
  * exact zeros.  May be called more than once per forward.  No host sync; once
  * a first call on ctx has sized its workspace for these shapes, a call makes
- * no allocation either (kernel launches on `stream` only), so it can be
- * captured in a HIP graph and replayed.
+ * no allocation either (kernel launches on `stream` only, no memset nodes),
+ * so it can be captured in a HIP graph and replayed.  A captured backward is
+ * valid only for the pcx_forward that preceded the capture: the graph holds
+ * that forward's workspace addresses, sizes (M, K) and X / W pointers, and
+ * the next pcx_forward on ctx may move or resize the workspace or change
+ * them, after which the graph must not be replayed.  Growth of the
+ * workspace during a capture fails with PCX_ERR_WORKSPACE.
  */
 pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
                         void* db, void* stream);

@@ -10,7 +10,10 @@
  *        int32 tgt_off[N+1], tgt[L_tot], frame_counts[N]
  *   out: float64 loss; int32 K, n_unalignable, n_nonfinite;
  *        float32 dX[M*D], dW[V*D], db[V]
- * usage: pcx_c_run IN OUT   (exit status 0 on success)
+ * usage: pcx_c_run IN OUT [callbacks]   (exit status 0 on success)
+ * With "callbacks" the context's workspace comes from allocation callbacks
+ * (hipMalloc / hipFree behind a counter); the program then fails unless
+ * every buffer the library allocated was released by pcx_destroy.
  */
 #include <stdio.h>
 #include <stdlib.h>
@@ -45,16 +48,45 @@ static void* read_block(FILE* f, size_t bytes) {
   return p;
 }
 
+/* Allocation callbacks: device memory from the HIP runtime, counted. */
+typedef struct {
+  long live;
+  long calls;
+  size_t bytes;
+} alloc_count;
+
+static void* count_alloc(size_t bytes, void* user, void* stream) {
+  alloc_count* c = (alloc_count*)user;
+  void* p = NULL;
+  (void)stream;
+  if (hipMalloc(&p, bytes) != hipSuccess) return NULL;
+  c->live += 1;
+  c->calls += 1;
+  c->bytes += bytes;
+  return p;
+}
+
+static void count_release(void* ptr, size_t bytes, void* user, void* stream) {
+  alloc_count* c = (alloc_count*)user;
+  (void)stream;
+  /* every library call ran on the default stream: wait for it, then free */
+  (void)hipDeviceSynchronize();
+  (void)hipFree(ptr);
+  c->live -= 1;
+  c->bytes -= bytes;
+}
+
 static int to_device(void** d, const void* h, size_t bytes) {
   if (hipMalloc(d, bytes ? bytes : 4) != hipSuccess) return 0;
   return bytes == 0 || hipMemcpy(*d, h, bytes, hipMemcpyHostToDevice) == hipSuccess;
 }
 
 int main(int argc, char** argv) {
-  if (argc != 3) {
-    fprintf(stderr, "usage: %s IN OUT\n", argv[0]);
+  if (argc != 3 && argc != 4) {
+    fprintf(stderr, "usage: %s IN OUT [callbacks]\n", argv[0]);
     return 1;
   }
+  const int use_callbacks = argc == 4;
   FILE* in = fopen(argv[1], "rb");
   if (!in) {
     perror(argv[1]);
@@ -92,7 +124,11 @@ int main(int argc, char** argv) {
   HIP_OK(hipMalloc(&gb, bb));
 
   pcx_ctx* ctx = NULL;
-  PCX_OK_(pcx_create(&ctx));
+  alloc_count counts_alloc = {0, 0, 0};
+  if (use_callbacks)
+    PCX_OK_(pcx_create(&ctx, count_alloc, count_release, &counts_alloc));
+  else
+    PCX_OK_(pcx_create(&ctx, NULL, NULL, NULL));
   double loss = 0.0;
   pcx_fwd_info info;
   PCX_OK_(pcx_forward(ctx, dX_in, dW_in, db_in, PCX_F32, M, D, V, N, (const int32_t*)d_off,
@@ -104,6 +140,11 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(W, gW, wb, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(b, gb, bb, hipMemcpyDeviceToHost));
   pcx_destroy(ctx);
+  if (use_callbacks && (counts_alloc.calls == 0 || counts_alloc.live != 0 || counts_alloc.bytes != 0)) {
+    fprintf(stderr, "allocation callbacks: %ld calls, %ld buffers / %zu bytes not released\n",
+            counts_alloc.calls, counts_alloc.live, counts_alloc.bytes);
+    return 4;
+  }
 
   FILE* out = fopen(argv[2], "wb");
   if (!out) {
@@ -127,6 +168,6 @@ int main(int argc, char** argv) {
     fprintf(stderr, "write failed\n");
     return 1;
   }
-  printf("loss %.17g K %d\n", loss, info.K);
+  printf("loss %.17g K %d callbacks %ld\n", loss, info.K, counts_alloc.calls);
   return 0;
 }

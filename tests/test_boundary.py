@@ -4,7 +4,9 @@
   Python binding's signature table covers exactly those functions;
 * argument validation that happens before any device work: NULL context,
   unsupported dtype (fp16), bad sizes, bad blank / chunk, backward or getters
-  before a forward pass (PCX_ERR_* codes, message via pcx_last_error).
+  before a forward pass (PCX_ERR_* codes, message via pcx_last_error);
+* the Python binding's checks of shapes, dtypes, contiguity and devices,
+  which reject a call before any pointer reaches the library.
 """
 import ctypes
 import os
@@ -47,7 +49,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 def _ctx(lib):
     h = ctypes.c_void_p()
-    assert lib.pcx_create(ctypes.byref(h)) == 0
+    assert lib.pcx_create(ctypes.byref(h), None, None, None) == 0
     return h
 
 
@@ -137,3 +139,77 @@ def test_missing_library_fails_loudly(tmp_path, monkeypatch):
         _lib.load()
     with pytest.raises(ImportError, match="not built"):
         pcx.Context()
+
+
+def test_create_rejects_half_an_allocator(lib):
+    h = ctypes.c_void_p()
+    from vocabulary_ctc_loss_amd import _lib
+    cb = _lib.ALLOC_FN(lambda n, u, st: None)
+    assert lib.pcx_create(ctypes.byref(h), ctypes.cast(cb, ctypes.c_void_p), None, None) == 1
+    assert b"callbacks" in lib.pcx_last_error()
+    assert lib.pcx_create(None, None, None, None) == 1
+
+
+def _cpu_batch():
+    import torch
+    M, D, V, N = 7, 4, 6, 2
+    return dict(X=torch.zeros(M, D), W=torch.zeros(V, D), b=torch.zeros(V),
+                tgt_off=torch.tensor([0, 1, 2], dtype=torch.int32),
+                tgt=torch.tensor([1, 2], dtype=torch.int32),
+                frame_counts=torch.tensor([3, 4], dtype=torch.int32))
+
+
+@pytest.mark.parametrize("change,match", [
+    (dict(X="half"), "dtypes"),
+    (dict(W="bf16"), "dtype of W"),               # fp32 b with a bf16 head
+    (dict(W="wide"), "V x D"),
+    (dict(X="1d"), "2-D"),
+    (dict(b="short"), "V = 6"),
+    (dict(tgt="i64"), "tgt must be a 1-D int32"),
+    (dict(frame_counts="i64"), "frame_counts must be a 1-D int32"),
+    (dict(tgt_off="short"), "N \\+ 1"),
+    (dict(X="strided"), "X must be contiguous"),
+    ({}, "must be on the GPU"),                    # every check passes but the device
+])
+def test_binding_rejects_bad_arguments(lib, change, match):
+    import torch
+    import vocabulary_ctc_loss_amd as pcx
+    a = _cpu_batch()
+    for k, how in change.items():
+        if how == "half":
+            a[k] = a[k].half()
+        elif how == "bf16":
+            a[k] = a[k].bfloat16()
+        elif how == "wide":
+            a[k] = torch.zeros(6, 5)
+        elif how == "1d":
+            a[k] = torch.zeros(28)
+        elif how == "short":
+            a[k] = a[k][:-1]
+        elif how == "i64":
+            a[k] = a[k].long()
+        elif how == "strided":
+            a[k] = torch.zeros(4, 7).t()
+    ctx = pcx.Context()
+    try:
+        with pytest.raises(ValueError, match=match):
+            ctx.forward(a["X"], a["W"], a["b"], a["tgt_off"], a["tgt"], a["frame_counts"], 0, 4)
+    finally:
+        ctx.close()
+
+
+def test_binding_rejects_bad_gradient_outputs():
+    import torch
+    from vocabulary_ctc_loss_amd import _check_grad_out
+    dev = torch.device("cpu")
+    _check_grad_out("dX", None, (3, 4), torch.float32, dev)
+    _check_grad_out("dX", torch.zeros(3, 4), (3, 4), torch.float32, dev)
+    with pytest.raises(ValueError, match="dX must be"):
+        _check_grad_out("dX", torch.zeros(3, 4, dtype=torch.bfloat16), (3, 4), torch.float32, dev)
+    with pytest.raises(ValueError, match="db must be"):
+        _check_grad_out("db", torch.zeros(5), (6,), torch.float32, dev)
+    with pytest.raises(ValueError, match="contiguous"):
+        _check_grad_out("dW", torch.zeros(4, 3).t(), (3, 4), torch.float32, dev)
+    with pytest.raises(ValueError, match="allocator"):
+        import vocabulary_ctc_loss_amd as pcx
+        pcx.Context(allocator="numpy")

@@ -3,7 +3,9 @@ __graft_entry__.build) takes device memory from the HIP runtime API, calls
 pcx_create / pcx_forward / pcx_backward / pcx_destroy with plain pointers and
 sizes as include/pcx.h declares them, and writes the loss and gradients to a
 file; no Python or PyTorch is in that process.  Its outputs are held to the
-fp32 bar against the oracle."""
+fp32 bar against the oracle, once with the library's own hipMalloc workspace
+(NULL callbacks) and once with the workspace taken from allocation callbacks
+of the program (which fails unless pcx_destroy released all of it)."""
 import os
 import subprocess
 
@@ -26,8 +28,9 @@ def _batch(name):
     return workloads.make_random(1, N=6, T_lo=40, T_hi=130, V=700, D=72, chunk=200)
 
 
-@pytest.mark.parametrize("name", ["readme", "tiles"])
-def test_c_program_matches_oracle(name, tmp_path):
+@pytest.mark.parametrize("name,callbacks", [("readme", False), ("tiles", False),
+                                            ("tiles", True)])
+def test_c_program_matches_oracle(name, callbacks, tmp_path):
     assert os.path.exists(EXE), "C ABI test program not built (run __graft_entry__.build())"
     bt = _batch(name)
     assert bt.dtype == "f32"
@@ -40,8 +43,9 @@ def test_c_program_matches_oracle(name, tmp_path):
             f.write(np.ascontiguousarray(a, np.float32).tobytes())
         for a in (bt.tgt_off, bt.tgt, bt.frame_counts):
             f.write(np.ascontiguousarray(a, np.int32).tobytes())
-    print("case", name, "M", bt.M, "V", bt.V, "D", bt.D, flush=True)
-    r = subprocess.run([EXE, str(src), str(dst)], capture_output=True, text=True, timeout=120)
+    print("case", name, "M", bt.M, "V", bt.V, "D", bt.D, "callbacks", callbacks, flush=True)
+    r = subprocess.run([EXE, str(src), str(dst)] + (["callbacks"] if callbacks else []),
+                       capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     raw = dst.read_bytes()
     loss = np.frombuffer(raw[:8], np.float64)[0]

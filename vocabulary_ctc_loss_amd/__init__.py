@@ -14,9 +14,8 @@ from typing import Optional, Sequence
 
 import numpy as np
 
-from ._lib import (FwdInfo, LIB_PATH, PCX_BF16, PCX_F32, PCX_F32_BF16W, PCX_FORM_DIRECT,  # noqa: F401
-                   PCX_FORM_GROUPED, PcxError, check,
-                   load)
+from ._lib import (ALLOC_FN, FREE_FN, FwdInfo, LIB_PATH, PCX_BF16, PCX_F32,  # noqa: F401
+                   PCX_F32_BF16W, PCX_FORM_DIRECT, PCX_FORM_GROUPED, PcxError, check, load)
 
 __all__ = ["Context", "PcxError", "pruned_ctc_loss", "pack_targets", "load", "LIB_PATH"]
 
@@ -28,8 +27,8 @@ def _torch():
 
 def _dtype_code(X, W) -> int:
     """pcx_dtype of an (X, W) pair: both fp32, both bf16, or fp32 X with a
-    bf16-stored head; anything else is passed through for the library to
-    reject."""
+    bf16-stored head (float16 is not supported, PrunedCTC README
+    constraints)."""
     torch = _torch()
     if X.dtype == torch.float32 and W.dtype == torch.float32:
         return PCX_F32
@@ -37,7 +36,84 @@ def _dtype_code(X, W) -> int:
         return PCX_BF16
     if X.dtype == torch.float32 and W.dtype == torch.bfloat16:
         return PCX_F32_BF16W
-    return 99
+    raise ValueError("X / W dtypes %s / %s are not supported (fp32 / fp32, bf16 / bf16, or "
+                     "fp32 / bf16 for a bf16-stored head)" % (X.dtype, W.dtype))
+
+
+def _check_forward_args(X, W, b, tgt_off, tgt, frame_counts):
+    """Reject, before anything reaches the library, what it would otherwise
+    read out of bounds or in the wrong element type: shapes, dtypes,
+    contiguity, and (last) that every tensor is on one GPU.  The targets,
+    offsets and lengths themselves are checked by the library on the device.
+    Returns the pcx_dtype code."""
+    torch = _torch()
+    if X.dim() != 2 or W.dim() != 2:
+        raise ValueError("X and W must be 2-D (M x D and V x D); got %s and %s"
+                         % (tuple(X.shape), tuple(W.shape)))
+    if W.shape[1] != X.shape[1]:
+        raise ValueError("W must be V x D with D = X.shape[1] = %d; got %s"
+                         % (X.shape[1], tuple(W.shape)))
+    code = _dtype_code(X, W)
+    if b is not None:
+        if b.dim() != 1 or b.shape[0] != W.shape[0]:
+            raise ValueError("b must have V = %d entries; got shape %s"
+                             % (W.shape[0], tuple(b.shape)))
+        if b.dtype != W.dtype:
+            raise ValueError("b must have the dtype of W (%s); got %s" % (W.dtype, b.dtype))
+    for name, t in (("tgt_off", tgt_off), ("tgt", tgt), ("frame_counts", frame_counts)):
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise ValueError("%s must be a 1-D int32 tensor; got %s %s"
+                             % (name, t.dtype, tuple(t.shape)))
+    if tgt_off.shape[0] != frame_counts.shape[0] + 1:
+        raise ValueError("tgt_off must have N + 1 = %d entries; got %d"
+                         % (frame_counts.shape[0] + 1, tgt_off.shape[0]))
+    for name, t in (("X", X), ("W", W), ("b", b), ("tgt_off", tgt_off), ("tgt", tgt),
+                    ("frame_counts", frame_counts)):
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % name)
+    dev = X.device
+    for name, t in (("X", X), ("W", W), ("b", b), ("tgt_off", tgt_off), ("tgt", tgt),
+                    ("frame_counts", frame_counts)):
+        if t is not None and (t.device.type != "cuda" or t.device != dev):
+            raise ValueError("%s must be on the GPU of X (%s); got %s" % (name, dev, t.device))
+    return code
+
+
+def _check_grad_out(name, out, like_shape, like_dtype, dev):
+    """A gradient output must match its input's shape and dtype, on its GPU."""
+    if out is None:
+        return
+    if tuple(out.shape) != tuple(like_shape) or out.dtype != like_dtype:
+        raise ValueError("%s must be %s %s; got %s %s" % (name, like_dtype, tuple(like_shape),
+                                                          out.dtype, tuple(out.shape)))
+    if not out.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if out.device != dev:
+        raise ValueError("%s must be on %s; got %s" % (name, dev, out.device))
+
+
+# Workspace through torch's caching allocator (pcx_create's callbacks): the
+# library's device memory then shows in torch.cuda.memory_allocated and is
+# reused like any tensor's.  A block is allocated on the stream of the call
+# and released on that same stream, the contract of torch's raw allocator.
+def _torch_alloc(nbytes, user, stream):
+    try:
+        torch = _torch()
+        return torch.cuda.caching_allocator_alloc(int(nbytes), torch.cuda.current_device(),
+                                                  int(stream or 0))
+    except Exception:
+        return None  # the library reports PCX_ERR_WORKSPACE
+
+
+def _torch_free(ptr, nbytes, user, stream):
+    try:
+        _torch().cuda.caching_allocator_delete(int(ptr))
+    except Exception:
+        pass
+
+
+_TORCH_ALLOC = ALLOC_FN(_torch_alloc)
+_TORCH_FREE = FREE_FN(_torch_free)
 
 
 def _ptr(t) -> Optional[int]:
@@ -62,19 +138,34 @@ def pack_targets(targets: Sequence[Sequence[int]], device=None):
 
 
 class Context:
-    """One pcx_ctx: workspace plus the forward state a backward pass needs."""
+    """One pcx_ctx: workspace plus the forward state a backward pass needs.
 
-    def __init__(self):
+    allocator="torch" (default) takes the workspace from torch's caching
+    allocator on the call's stream; None lets the library use hipMalloc.
+    """
+
+    def __init__(self, allocator: Optional[str] = "torch"):
         self._lib = load()
         h = ctypes.c_void_p()
-        check(self._lib.pcx_create(ctypes.byref(h)))
+        if allocator == "torch":
+            check(self._lib.pcx_create(ctypes.byref(h), ctypes.cast(_TORCH_ALLOC, ctypes.c_void_p),
+                                       ctypes.cast(_TORCH_FREE, ctypes.c_void_p), None))
+        elif allocator is None:
+            check(self._lib.pcx_create(ctypes.byref(h), None, None, None))
+        else:
+            raise ValueError("allocator must be 'torch' or None")
         self._h = h
         self.info = None
         self._shape = None
+        self._dev = None
 
     def close(self):
         if getattr(self, "_h", None) is not None and self._h.value:
-            self._lib.pcx_destroy(self._h)
+            if self._dev is not None:
+                with _torch().cuda.device(self._dev):
+                    self._lib.pcx_destroy(self._h)
+            else:
+                self._lib.pcx_destroy(self._h)
             self._h = None
 
     def __del__(self):
@@ -93,33 +184,48 @@ class Context:
     def forward(self, X, W, b, tgt_off, tgt, frame_counts, blank: int = 0,
                 chunk: int = 4096, stream=None):
         """Run pcx_forward; returns (summed loss as float, info dict)."""
-        for name, t in (("X", X), ("W", W), ("tgt_off", tgt_off), ("frame_counts", frame_counts)):
-            if not t.is_contiguous():
-                raise ValueError("%s must be contiguous" % name)
+        code = _check_forward_args(X, W, b, tgt_off, tgt, frame_counts)
+        if self._dev is not None and X.device != self._dev:
+            raise ValueError("this context runs on %s; X is on %s" % (self._dev, X.device))
         M, D = X.shape
         V = W.shape[0]
         N = frame_counts.shape[0]
         L_tot = tgt.shape[0]
         loss = ctypes.c_double(0.0)
         info = FwdInfo()
-        check(self._lib.pcx_forward(
-            self._h, _ptr(X), _ptr(W), _ptr(b), _dtype_code(X, W), M, D, V, N, _ptr(tgt_off),
-            _ptr(tgt) if L_tot else None, L_tot, _ptr(frame_counts), int(blank), int(chunk),
-            _stream_handle(stream), ctypes.byref(loss), ctypes.byref(info)))
+        with _torch().cuda.device(X.device):
+            check(self._lib.pcx_forward(
+                self._h, _ptr(X), _ptr(W), _ptr(b), code, M, D, V, N, _ptr(tgt_off),
+                _ptr(tgt) if L_tot else None, L_tot, _ptr(frame_counts), int(blank), int(chunk),
+                _stream_handle(stream), ctypes.byref(loss), ctypes.byref(info)))
+        self._dev = X.device
         self.info = {f: getattr(info, f) for f, _ in FwdInfo._fields_}
-        self._shape = dict(M=M, D=D, V=V, N=N, L_tot=L_tot, K=info.K)
+        self._shape = dict(M=M, D=D, V=V, N=N, L_tot=L_tot, K=info.K, X=(X.shape, X.dtype),
+                           W=(W.shape, W.dtype))
         return loss.value, self.info
 
     def backward(self, grad_loss: float = 1.0, dX=None, dW=None, db=None, stream=None):
-        check(self._lib.pcx_backward(self._h, float(grad_loss), _ptr(dX), _ptr(dW), _ptr(db),
-                                     _stream_handle(stream)))
+        """Run pcx_backward for the last forward: dX / dW / db (any may be None)
+        are overwritten; each must match its input's shape and dtype (db: V
+        entries in W's dtype)."""
+        if self._shape is not None:
+            sh = self._shape
+            _check_grad_out("dX", dX, *sh["X"], self._dev)
+            _check_grad_out("dW", dW, *sh["W"], self._dev)
+            _check_grad_out("db", db, (sh["V"],), sh["W"][1], self._dev)
+        dev = self._dev if self._dev is not None else _torch().cuda.current_device()
+        with _torch().cuda.device(dev):
+            check(self._lib.pcx_backward(self._h, float(grad_loss), _ptr(dX), _ptr(dW), _ptr(db),
+                                         _stream_handle(stream)))
 
     def blank_offset_grad(self, grad_loss: float = 1.0, stream=None) -> float:
         """d(loss)/d(eta) for an offset eta added to the blank logit of every
         frame (db[blank] without computing db); see pcx_blank_offset_grad."""
         out = ctypes.c_double(0.0)
-        check(self._lib.pcx_blank_offset_grad(self._h, float(grad_loss), ctypes.byref(out),
-                                              _stream_handle(stream)))
+        dev = self._dev if self._dev is not None else _torch().cuda.current_device()
+        with _torch().cuda.device(dev):
+            check(self._lib.pcx_blank_offset_grad(self._h, float(grad_loss), ctypes.byref(out),
+                                                  _stream_handle(stream)))
         return out.value
 
     # -------------------------------------------------------------- getters

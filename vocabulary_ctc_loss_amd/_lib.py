@@ -22,7 +22,13 @@ PCX_FORM_GROUPED = 1
 STATUS_NAMES = {
     0: "PCX_OK", 1: "PCX_ERR_ARG", 2: "PCX_ERR_DTYPE", 3: "PCX_ERR_TARGET",
     4: "PCX_ERR_LENGTHS", 5: "PCX_ERR_STATE", 6: "PCX_ERR_HIP", 7: "PCX_ERR_LIMIT",
+    8: "PCX_ERR_WORKSPACE",
 }
+
+# The allocation callbacks of pcx_create (pcx_alloc_fn / pcx_free_fn).
+ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p)
+FREE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                           ctypes.c_void_p)
 
 # Every function include/pcx.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
@@ -30,7 +36,7 @@ _I32 = ctypes.c_int32
 _I64 = ctypes.c_int64
 _D = ctypes.c_double
 SIGNATURES = {
-    "pcx_create": (_I32, [ctypes.POINTER(_P)]),
+    "pcx_create": (_I32, [ctypes.POINTER(_P), _P, _P, _P]),
     "pcx_destroy": (None, [_P]),
     "pcx_forward": (_I32, [_P, _P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _I64, _P,
                            _I32, _I32, _P, ctypes.POINTER(_D), _P]),

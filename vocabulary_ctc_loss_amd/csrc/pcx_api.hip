@@ -36,10 +36,12 @@ pcx_status fail(pcx_status st, const char* fmt, ...) {
       return fail(PCX_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_));          \
   } while (0)
 
-// A grow-only device buffer.
+// A grow-only device buffer, with the stream it was allocated on (for a
+// stream-ordered release through the caller's allocator).
 struct DevBuf {
   void* p = nullptr;
   size_t cap = 0;
+  hipStream_t st = nullptr;
 };
 
 // Kernel families timed by the optional event profiler.
@@ -65,6 +67,10 @@ struct pcx_ctx {
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
   DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32, other, gu, ou;
   Meta* host_meta = nullptr;  // pinned
+  // caller's allocator (both NULL: hipMalloc / hipFree)
+  pcx_alloc_fn alloc = nullptr;
+  pcx_free_fn release = nullptr;
+  void* user = nullptr;
   // forward state kept for backward / getters
   bool fwd_ok = false;
   bool bwd_done = false;
@@ -129,24 +135,47 @@ size_t total_bytes(const pcx_ctx* c) {
 pcx_status ensure(pcx_ctx* c, DevBuf& b, size_t bytes, hipStream_t st) {
   if (bytes == 0) bytes = 16;
   if (b.cap >= bytes) return PCX_OK;
+  {
+    // a graph must not record an allocation or a release
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    PCX_HIP(hipStreamIsCapturing(st, &cs));
+    if (cs != hipStreamCaptureStatusNone)
+      return fail(PCX_ERR_WORKSPACE,
+                  "the workspace would grow (%zu > %zu bytes) while the stream is being "
+                  "captured; run one call of the same shapes before the capture",
+                  bytes, b.cap);
+  }
   if (b.p) {
-    // the old buffer may still be read by work of an earlier call, possibly
-    // on another stream: wait for the whole device before freeing it (growth
-    // is rare; a sized workspace never gets here)
-    PCX_HIP(hipDeviceSynchronize());
-    PCX_HIP(hipFree(b.p));
+    if (c->release) {
+      // Every earlier call of this context is ordered before the work
+      // already issued to st (the stream hand-off); released on its own
+      // allocation stream, the buffer is then safe for that stream's later
+      // work.  Released from another stream's call, wait for st first.
+      if (b.st != st) PCX_HIP(hipStreamSynchronize(st));
+      c->release(b.p, b.cap, c->user, (void*)b.st);
+    } else {
+      // the old buffer may still be read by work of an earlier call, possibly
+      // on another stream: wait for the whole device before freeing it
+      // (growth is rare; a sized workspace never gets here)
+      PCX_HIP(hipDeviceSynchronize());
+      PCX_HIP(hipFree(b.p));
+    }
     b.p = nullptr;
     b.cap = 0;
   }
   bytes = (bytes + 255) & ~size_t(255);
-  hipError_t e = hipMalloc(&b.p, bytes);
-  if (e != hipSuccess) {
-    b.p = nullptr;
-    return fail(PCX_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+  if (c->alloc) {
+    b.p = c->alloc(bytes, c->user, (void*)st);
+    if (!b.p) return fail(PCX_ERR_WORKSPACE, "the allocation callback returned NULL for %zu bytes", bytes);
+  } else {
+    hipError_t e = hipMalloc(&b.p, bytes);
+    if (e != hipSuccess) {
+      b.p = nullptr;
+      return fail(PCX_ERR_HIP, "hipMalloc(%zu) failed: %s", bytes, hipGetErrorString(e));
+    }
   }
   b.cap = bytes;
-  (void)c;
-  (void)st;
+  b.st = st;
   return PCX_OK;
 }
 
@@ -227,26 +256,39 @@ extern "C" {
 
 const char* pcx_last_error(void) { return g_last_error.c_str(); }
 
-pcx_status pcx_create(pcx_ctx** out_ctx) {
+pcx_status pcx_create(pcx_ctx** out_ctx, pcx_alloc_fn alloc, pcx_free_fn release, void* user) {
   g_last_error.clear();
   if (!out_ctx) return fail(PCX_ERR_ARG, "out_ctx is NULL");
+  if ((alloc == nullptr) != (release == nullptr))
+    return fail(PCX_ERR_ARG, "alloc and release callbacks must both be set or both be NULL");
   // No HIP call here: device and pinned memory are taken on first use.
   pcx_ctx* c = new (std::nothrow) pcx_ctx();
   if (!c) return fail(PCX_ERR_ARG, "out of host memory");
+  c->alloc = alloc;
+  c->release = release;
+  c->user = user;
   *out_ctx = c;
   return PCX_OK;
 }
 
 void pcx_destroy(pcx_ctx* c) {
   if (!c) return;
-  if (c->host_meta || c->meta.p) (void)hipDeviceSynchronize();
   DevBuf* bufs[] = {&c->meta, &c->row_off, &c->flags, &c->dp_off, &c->col2sel, &c->U,
                     &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha, &c->beta,
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
                     &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta, &c->w32, &c->b32,
                     &c->other, &c->gu, &c->ou};
-  for (DevBuf* b : bufs)
-    if (b->p) (void)hipFree(b->p);
+  if (c->release) {
+    // every call of the context is ordered before the last call's stream
+    // tail: once that has finished, nothing of ours touches the workspace
+    if (c->stream_set) (void)hipStreamSynchronize(c->stream);
+    for (DevBuf* b : bufs)
+      if (b->p) c->release(b->p, b->cap, c->user, (void*)b->st);
+  } else {
+    if (c->host_meta || c->meta.p) (void)hipDeviceSynchronize();
+    for (DevBuf* b : bufs)
+      if (b->p) (void)hipFree(b->p);
+  }
   for (Pending& p : c->pending) {
     (void)hipEventDestroy(p.a);
     (void)hipEventDestroy(p.b);
@@ -490,9 +532,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   const size_t wesz = wdt == PCX_F32 ? 4 : 2;
   if (!dX && !dW && !db) return PCX_OK;
   if (M == 0) {
-    // No frames: every head gradient is zero.
-    if (dW) PCX_HIP(hipMemsetAsync(dW, 0, (size_t)V * D * wesz, st));
-    if (db) PCX_HIP(hipMemsetAsync(db, 0, (size_t)V * wesz, st));
+    // No frames: every head gradient is zero (a fill kernel, not a memset
+    // node, so that the call can be captured into a graph).
+    if (dW) LAUNCH(K_FILL, launch_fill_zero(st, dW, (long long)V * D, (int)wesz));
+    if (db) LAUNCH(K_FILL, launch_fill_zero(st, db, V, (int)wesz));
     return PCX_OK;
   }
   const float* S = (const float*)ctx->S.p;

@@ -219,5 +219,7 @@ hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int ma
 hipError_t launch_blank_grad(hipStream_t st, const float* S, const float* Gam, const double* g,
                              int M, double grad, double* out);
 hipError_t launch_fill_f32(hipStream_t st, float* p, long long n, float v);
+// Zero n elements of esz bytes each (esz 2 or 4; p aligned to esz).
+hipError_t launch_fill_zero(hipStream_t st, void* p, long long n, int esz);
 
 }  // namespace pcx

@@ -480,6 +480,12 @@ __global__ void k_fill_f32(float* __restrict__ p, long long n, float v) {
     p[i] = v;
 }
 
+__global__ void k_fill_zero_u16(uint16_t* __restrict__ p, long long n) {
+  for (long long i = blockIdx.x * (long long)blockDim.x + threadIdx.x; i < n;
+       i += (long long)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
 void dp_shape(int max_L, int& threads, int& spt) {
   const int Smax = 2 * max_L + 1;
   threads = ((Smax + 63) / 64) * 64;
@@ -567,6 +573,16 @@ hipError_t launch_fill_f32(hipStream_t st, float* p, long long n, float v) {
   if (g < 1) g = 1;
   if (g > 8192) g = 8192;
   k_fill_f32<<<(int)g, 256, 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(hipStream_t st, void* p, long long n, int esz) {
+  if (n == 0) return hipSuccess;
+  if (esz == 4) return launch_fill_f32(st, (float*)p, n, 0.f);
+  if (esz != 2) return hipErrorInvalidValue;
+  long long g = (n + 255) / 256;
+  if (g > 8192) g = 8192;
+  k_fill_zero_u16<<<(int)g, 256, 0, st>>>((uint16_t*)p, n);
   return hipGetLastError();
 }
 
