@@ -12,6 +12,7 @@ import zlib
 import numpy as np
 import pytest
 
+import oracle
 import workloads
 from pcx_harness import rel_fro, run_oracle, run_pcx, tolerance
 
@@ -230,6 +231,42 @@ def test_nonfinite_input_utterance_is_excluded(name):
     keep = np.ones(bt.M, bool)
     keep[row_off[2]:row_off[3]] = False
     assert rel_fro(got["dX"][keep], ref["dX"][keep]) <= tol
+
+
+@pytest.mark.parametrize("name,grouped,where", [
+    ("tiles", False, "unselected"), ("tiles", True, "unselected"), ("tiles", False, "selected"),
+    ("tiles", True, "selected"), ("bf16_big_grads", False, "unselected"),
+    ("bf16_big_grads", False, "bias")])
+def test_nonfinite_head_row_poisons_every_frame(name, grouped, where):
+    """A NaN row of the head (or a NaN bias entry) makes every logit of that
+    class NaN, so every frame's normalizer, and with it every alignable
+    utterance's loss, is nonfinite: the oracle marks them all nonfinite and
+    excludes them.  The library must do the same rather than let the maximum
+    and the clamped exponential drop the NaN and report a finite loss (the
+    pages replace nonfinite per-utterance losses by zero, App. B.1)."""
+    import dataclasses
+    bt = case(name)
+    U, _, _ = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
+    sel = set(int(u) for u in U)
+    v = int(U[-1]) if where == "selected" else next(c for c in range(bt.V) if c not in sel)
+    W = bt.W.copy()
+    b = None if bt.b is None else bt.b.copy()
+    if where == "bias":
+        if b is None:
+            b = np.zeros(bt.V, np.float32)
+        b[v] = np.nan
+    else:
+        W[v] = np.nan
+    bt = dataclasses.replace(bt, W=W, b=b)
+    print("case", name, "grouped", grouped, "nan", where, v, flush=True)
+    got = run_pcx(bt, want_dX=False, want_dW=False, want_db=False, getters="light",
+                  grouped=grouped)
+    ref = run_oracle(bt, want_dW=False, want_db=False)
+    assert np.all(ref["status"] != 0)
+    assert got["status"].tolist() == ref["status"].tolist()
+    assert got["loss"] == 0.0 and ref["loss"] == 0.0
+    assert got["info"]["n_nonfinite"] == int(np.sum(ref["status"] == 2))
+    assert np.all(got["utt_loss"] == 0.0)
 
 
 @pytest.mark.parametrize("name,grouped", [("tiles", False), ("tiles", True),

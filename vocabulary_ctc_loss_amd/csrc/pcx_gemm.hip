@@ -409,6 +409,17 @@ __device__ __forceinline__ int acc_col(int fj) {
   return (w % C::WGN) * C::WN + fj * 32 + (lane & 31);
 }
 
+// A tile partial with a NaN or infinite logit (chk is then NaN) becomes
+// (finite max, NaN sum): every later fold, and the normalizer built from it,
+// is then NaN, so the frame's utterance comes out nonfinite and is excluded.
+// (The max alone would drop a NaN, and the clamped exp maps it to 0.)
+__device__ __forceinline__ void nonfinite_partial(float chk, float& mx, double& sum) {
+  if (chk != chk) {
+    mx = (mx == -INFINITY || mx == INFINITY) ? 0.f : mx;
+    sum = __builtin_nan("");
+  }
+}
+
 // (m1, s1) <- fold of two log-sum-exp partials (max, sum of exp(z - max)).
 __device__ __forceinline__ void lse_fold(float& m1, double& s1, float m2, double s2) {
   if (m2 == -INFINITY) return;
@@ -541,6 +552,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
       float mx = -INFINITY;
+      float chk = 0.f;  // stays 0 unless a logit is NaN or infinite
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
@@ -552,6 +564,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = acc[fi][fj][4 * q + e] + b4[e];
+            chk = fmaf(z, 0.f, chk);
             // in the sum: every vocabulary row of the span, or (masked)
             // only the unselected ones
             acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
@@ -566,6 +579,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_fwd_lse(
           for (int r = 0; r < 16; ++r)
             sum += exp_nonpos((double)acc[fi][fj][r] - (double)mx);
       }
+      nonfinite_partial(chk, mx, sum);
       lse_fold(run_m[fj], run_s[fj], mx, sum);
     }
   }
@@ -638,7 +652,9 @@ __global__ void k_lambda_grouped(const float* __restrict__ Zsel, const double* _
   for (int j = 0; j < K; ++j) mx = fmax(mx, (double)Zsel[(long long)j * M + m]);
   double s = other[m] == -INFINITY ? 0.0 : exp_nonpos(other[m] - mx);
   for (int j = 0; j < K; ++j) s += exp_nonpos((double)Zsel[(long long)j * M + m] - mx);
-  const double l = mx + log(s);
+  double l = mx + log(s);
+  // a nonfinite logit in the frame made the other column NaN: so is lambda
+  if (other[m] != other[m]) l = other[m];
   lam[m] = l;
   lamf[m] = (float)l;
 }
@@ -1432,6 +1448,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     for (int fj = 0; fj < C::FN; ++fj) {
       const int frame = f0 + acc_col<C>(fj);
       float mx = -INFINITY;
+      float chk = 0.f;  // stays 0 unless a logit is NaN or infinite
 #pragma unroll
       for (int fi = 0; fi < C::FM; ++fi)
 #pragma unroll
@@ -1443,6 +1460,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float z = acc[fi][fj][4 * q + e] + b4[e];
+            chk = fmaf(z, 0.f, chk);
             // in the sum: every vocabulary row of the span, or (masked)
             // only the unselected ones
             acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
@@ -1461,6 +1479,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
           __builtin_amdgcn_sched_barrier(0);
         }
       }
+      nonfinite_partial(chk, mx, sum);
       lse_fold(run_m[fj], run_s[fj], mx, sum);
     }
   }
