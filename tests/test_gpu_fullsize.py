@@ -8,12 +8,20 @@ The oracle cannot redo a whole V = 180k or LLM-head batch in seconds, so:
   utterance itself);
 * dW and db, which mix all utterances, are checked by properties that hold
   at any size: every alignable frame's logit-gradient row sums to zero, so
-  sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding;
+  sum_v db_v = 0 and sum_v dW[v, :] = 0 up to rounding (and neither is all
+  zeros);
 * the grouped formulation is held to the same sampled bar and compared with
   the direct one on the whole batch;
 * the two small-vocabulary workloads (V = 500 and 5000), where the oracle
   runs the whole batch in seconds, are compared output by output: every
-  utterance's loss, and all of dX, dW and db.
+  utterance's loss, and all of dX, dW and db;
+* the V = 180k workload is compared output by output too: the oracle runs
+  it in five groups of five utterances (about half a minute each), every
+  utterance's loss and dX rows are checked per group, and dW and db against
+  the sum of the groups' head gradients (utterances contribute additively);
+* on the LLM head (dX alone, frames in two parts on the GPU) dX is compared
+  on the first and last utterances, on one more utterance wholly inside each
+  part, and on the utterance that straddles the part boundary.
 """
 import numpy as np
 import pytest
@@ -23,6 +31,17 @@ import workloads
 from pcx_harness import rel_fro, run_pcx, tolerance
 
 pytestmark = pytest.mark.gpu
+
+# GPU results of a full-size workload, computed once per module
+_GPU = {}
+
+
+def _gpu(name):
+    if name not in _GPU:
+        bt = workloads.make(name, seed=0)
+        print("workload", name, "M", bt.M, "V", bt.V, "D", bt.D, "N", bt.N, flush=True)
+        _GPU[name] = (bt, run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters="light"))
+    return _GPU[name]
 
 
 def _sample(bt):
@@ -37,9 +56,7 @@ def _sample(bt):
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["v500", "v5k", "v180k", "llm152k"])
 def test_full_size_sampled(name):
-    bt = workloads.make(name, seed=0)
-    print("workload", name, "M", bt.M, "V", bt.V, "D", bt.D, "N", bt.N, flush=True)
-    got = run_pcx(bt, want_dW=bt.want_dW, want_db=bt.want_db, getters="light")
+    bt, got = _gpu(name)
     U, rel, flags = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
     assert got["U"].tolist() == U.tolist()
     assert got["rel"].tolist() == rel.tolist()
@@ -59,11 +76,13 @@ def test_full_size_sampled(name):
     assert rel_fro(got["dX"][rows], ref["dX"]) <= tol
     if bt.want_db:
         db = got["db"]
+        assert np.abs(db).sum() > 0.0
         assert abs(db.sum()) <= 1e-5 * np.abs(db).sum()
     if bt.want_dW:
         dW = got["dW"]
         colsum = np.abs(dW.sum(0))
         scale = np.abs(dW).sum(0)
+        assert np.all(scale > 0.0)
         assert np.all(colsum <= 1e-5 * scale)
 
 
@@ -94,11 +113,104 @@ def test_full_size_grouped_matches_oracle_and_direct(name):
     assert rel_fro(g["dX"][rows], ref["dX"]) <= tol
 
 
+# utterance groups of the V = 180k batch (N = 25) for the oracle, and the sum
+# of their head gradients
+V180K_GROUPS = [list(range(5 * i, 5 * i + 5)) for i in range(5)]
+_V180K = {}       # group -> the oracle's per-utterance outputs
+_V180K_SUM = {}   # running sums of the groups' dW, db and loss
+
+
+def _v180k_group(i):
+    if i not in _V180K:
+        bt, _ = _gpu("v180k")
+        sb = workloads.sample_utterances(bt, V180K_GROUPS[i])
+        print("oracle on v180k utterances", V180K_GROUPS[i], "frames", sb.M, flush=True)
+        ref = oracle.pcx(sb.X, sb.W, sb.b, sb.frame_counts, sb.tgt_off, sb.tgt, sb.blank,
+                         want_lambda=False)
+        if not _V180K_SUM:
+            _V180K_SUM.update(dW=np.zeros_like(ref["dW"]), db=np.zeros_like(ref["db"]), loss=0.0)
+        _V180K_SUM["dW"] += ref["dW"]
+        _V180K_SUM["db"] += ref["db"]
+        _V180K_SUM["loss"] += ref["loss"]
+        _V180K[i] = {k: ref[k] for k in ("status", "utt_loss", "dX")}
+    return _V180K[i]
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("group", range(len(V180K_GROUPS)))
+def test_v180k_whole_batch_losses_and_dx(group):
+    """V = 180k at full size: the losses and dX rows of five utterances, from
+    the one whole-batch GPU run, against the oracle on those utterances."""
+    bt, got = _gpu("v180k")
+    ref = _v180k_group(group)
+    idx = V180K_GROUPS[group]
+    tol = tolerance(bt)
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    assert got["status"][idx].tolist() == ref["status"].tolist()
+    for j, n in enumerate(idx):
+        assert abs(got["utt_loss"][n] - ref["utt_loss"][j]) <= tol * abs(ref["utt_loss"][j])
+    rows = np.concatenate([np.arange(row_off[n], row_off[n + 1]) for n in idx])
+    e = rel_fro(got["dX"][rows], ref["dX"])
+    print("dX rows of", idx, "relative Frobenius error %.3g" % e, flush=True)
+    assert e <= tol
+
+
+@pytest.mark.timeout(900)
+def test_v180k_whole_batch_head_gradients():
+    """dW and db of the whole V = 180k batch (the split-frame dW reduction and
+    the 44 chunk reductions of the timed configuration) against the sum of
+    the oracle's per-group head gradients, and the summed loss."""
+    bt, got = _gpu("v180k")
+    for i in range(len(V180K_GROUPS)):
+        _v180k_group(i)
+    dW, db, loss = _V180K_SUM["dW"], _V180K_SUM["db"], _V180K_SUM["loss"]
+    tol = tolerance(bt)
+    assert abs(got["loss"] - loss) <= tol * abs(loss)
+    for k, want in (("dW", dW), ("db", db)):
+        assert np.linalg.norm(got[k]) > 0.0
+        e = rel_fro(got[k], want)
+        print(k, "relative Frobenius error %.3g" % e, flush=True)
+        assert e <= tol, (k, e)
+
+
+def _llm_samples(bt):
+    """Utterances of the LLM-head batch to check dX on: the first, the last,
+    the one holding the first row of the backward's second frame part, and
+    the shortest utterance wholly inside each part."""
+    M, rtile = bt.M, 256
+    split = ((M + 1) // 2 + rtile - 1) // rtile * rtile  # first row of part 2
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    n_split = int(np.searchsorted(row_off, split, side="right")) - 1
+    assert row_off[n_split] < split < row_off[n_split + 1]
+    part1 = [n for n in range(1, bt.N - 1) if row_off[n + 1] <= split and n != n_split]
+    part2 = [n for n in range(1, bt.N - 1) if row_off[n] >= split and n != n_split]
+    pick = lambda ns: min(ns, key=lambda n: bt.frame_counts[n])  # noqa: E731
+    return {"first": 0, "last": bt.N - 1, "straddle": n_split, "part1": pick(part1),
+            "part2": pick(part2)}
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("which", ["first", "part1", "straddle", "part2", "last"])
+def test_llm152k_dx_across_frame_parts(which):
+    bt, got = _gpu("llm152k")
+    n = _llm_samples(bt)[which]
+    sb = workloads.sample_utterances(bt, [n])
+    print("oracle on llm152k utterance", n, which, "frames", sb.M, flush=True)
+    ref = oracle.pcx(sb.X, sb.W, sb.b, sb.frame_counts, sb.tgt_off, sb.tgt, sb.blank,
+                     want_dW=False, want_db=False, want_lambda=False)
+    tol = tolerance(bt)
+    row_off = np.concatenate([[0], np.cumsum(bt.frame_counts)])
+    assert abs(got["utt_loss"][n] - ref["utt_loss"][0]) <= tol * abs(ref["utt_loss"][0])
+    e = rel_fro(got["dX"][row_off[n]:row_off[n + 1]], ref["dX"])
+    print("dX relative Frobenius error %.3g" % e, flush=True)
+    assert e <= tol
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["v500", "v5k"])
 def test_full_size_whole_batch(name):
-    """Full size, no sampling: the oracle on the whole batch, every output
-    held to the element-wise bar."""
+    """Full size, no sampling: the oracle on the whole batch; loss and every
+    gradient held to the relative Frobenius bar (1e-5 fp32)."""
     bt = workloads.make(name, seed=0)
     print("workload", name, "M", bt.M, "V", bt.V, "D", bt.D, "N", bt.N, flush=True)
     got = run_pcx(bt, want_dW=True, want_db=True, getters="light")
