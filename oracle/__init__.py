@@ -155,8 +155,30 @@ _default = None
 def _oracle() -> Oracle:
     global _default
     if _default is None:
-        _default = Oracle(build())
+        # PCX_ORACLE_LIB: a separately compiled copy of ctc_oracle.c (the
+        # sanitizer build of the tests) in place of liboracle.so
+        alt = os.environ.get("PCX_ORACLE_LIB")
+        _default = Oracle(alt if alt else build())
     return _default
+
+
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def build_sanitized(out_path: str, src_text: str = None) -> str:
+    """Compile ctc_oracle.c (or a test-modified copy of its text) with
+    AddressSanitizer and UndefinedBehaviorSanitizer (gcc; any finding aborts)
+    for the tests that run the pins under them."""
+    src = _SRC
+    if src_text is not None:
+        src = out_path + ".c"
+        with open(src, "w") as f:
+            f.write(src_text)
+    subprocess.run(["gcc", "-O1", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-std=c11",
+                    "-Wall", "-Wextra"] + SANITIZE_FLAGS +
+                   ["-o", out_path, src, "-lm"], check=True)
+    return out_path
 
 
 def compile_variant(src_text: str, out_path: str) -> str:

@@ -20,7 +20,7 @@ def flags():
         "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
         # packed fp32 math stays off on this target
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wall", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
+        "-Wall", "-Werror", "-Wno-unused-result", "-I", os.path.join(ROOT, "include"),
     ]
 
 
