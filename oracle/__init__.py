@@ -52,6 +52,12 @@ def _bind(path):
     lib.oracle_pcx.argtypes = [I, I, I, I, I, P, P, P, P, P, P, ctypes.c_double, P, P, P, P,
                                I, P, P, P, P, P, P]
     lib.oracle_pcx.restype = I
+    lib.oracle_ctc_beam.argtypes = [I, I, I, P, P, I, ctypes.c_double, ctypes.c_double, P, P,
+                                    P, P, P, P, P]
+    lib.oracle_ctc_beam.restype = I
+    lib.oracle_pcx_beam.argtypes = [I, I, I, I, I, P, P, P, P, P, P, ctypes.c_double,
+                                    ctypes.c_double, P, P, P, P, P, P, I, P, P, P, P, P, P]
+    lib.oracle_pcx_beam.restype = I
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = I
     return lib
@@ -109,13 +115,39 @@ class Oracle:
             raise ValueError("oracle_ctc_logits failed (code %d)" % rc)
         return {"loss": loss.value, "status": st.value, "lambda": lam, "dZ": dZ, "gamma": gam}
 
+    def ctc_beam(self, Z, y, blank, beam, grad=1.0, want_grad=True):
+        """Finite-beam CTC of one utterance from its raw logits Z (T x V): loss
+        over the retained alignments, the unpruned loss, the pruning margin,
+        occupancies and logit gradient (see oracle_ctc_beam)."""
+        Z = _f64(Z)
+        T, V = Z.shape
+        y = _i32(y)
+        loss = ctypes.c_double(0.0)
+        full = ctypes.c_double(0.0)
+        margin = ctypes.c_double(0.0)
+        st = ctypes.c_int(0)
+        lam = np.zeros(T)
+        dZ = np.zeros((T, V)) if want_grad else None
+        gam = np.zeros((T, V)) if want_grad else None
+        rc = self.lib.oracle_ctc_beam(T, V, blank, _ptr(Z), _ptr(y) if y.size else None,
+                                      int(y.shape[0]), float(beam), float(grad),
+                                      ctypes.byref(loss), ctypes.byref(st), ctypes.byref(full),
+                                      _ptr(lam), _ptr(dZ), _ptr(gam), ctypes.byref(margin))
+        if rc != 0:
+            raise ValueError("oracle_ctc_beam failed (code %d)" % rc)
+        return {"loss": loss.value, "status": st.value, "full_loss": full.value,
+                "margin": margin.value, "lambda": lam, "dZ": dZ, "gamma": gam}
+
     def pcx(self, X, W, b, frame_counts, tgt_off, tgt, blank, grad=1.0, cols=None,
-            want_dX=True, want_dW=True, want_db=True, want_gamma=False, want_lambda=True):
+            want_dX=True, want_dW=True, want_db=True, want_gamma=False, want_lambda=True,
+            beam=None):
         """Full path: head projection, summed CTC loss and gradients in FP64.
 
         X (M x D), W (V x D), b (V or None) are upcast exactly to FP64.  Returns
         a dict with loss, utt_loss, status, lambda, logp_cols/gamma_cols (at the
-        columns ``cols``), dX, dW and db.
+        columns ``cols``), dX, dW and db.  With ``beam`` (a number, inf
+        included) the finite-beam objective is used and the dict also holds
+        delta (discarded posterior mass per utterance) and margin.
         """
         X, W = _f64(X), _f64(W)
         bb = None if b is None else _f64(b)
@@ -134,15 +166,28 @@ class Oracle:
         dX = np.zeros((M, D)) if want_dX else None
         dW = np.zeros((V, D)) if want_dW else None
         db = np.zeros(V) if want_db else None
-        rc = self.lib.oracle_pcx(N, M, D, V, blank, _ptr(X), _ptr(W), _ptr(bb), _ptr(fc),
-                                 _ptr(off), _ptr(y) if y.size else _ptr(np.zeros(1, np.int32)),
-                                 float(grad), ctypes.byref(loss), _ptr(utt), _ptr(st),
-                                 _ptr(lam), nc, _ptr(cols) if nc else None, _ptr(lpc),
-                                 _ptr(gmc), _ptr(dX), _ptr(dW), _ptr(db))
+        yy = _ptr(y) if y.size else _ptr(np.zeros(1, np.int32))
+        if beam is None:
+            rc = self.lib.oracle_pcx(N, M, D, V, blank, _ptr(X), _ptr(W), _ptr(bb), _ptr(fc),
+                                     _ptr(off), yy, float(grad), ctypes.byref(loss), _ptr(utt),
+                                     _ptr(st), _ptr(lam), nc, _ptr(cols) if nc else None,
+                                     _ptr(lpc), _ptr(gmc), _ptr(dX), _ptr(dW), _ptr(db))
+        else:
+            delta = np.zeros(max(1, N))
+            margin = np.zeros(max(1, N))
+            rc = self.lib.oracle_pcx_beam(N, M, D, V, blank, _ptr(X), _ptr(W), _ptr(bb), _ptr(fc),
+                                          _ptr(off), yy, float(beam), float(grad),
+                                          ctypes.byref(loss), _ptr(utt), _ptr(st), _ptr(delta),
+                                          _ptr(margin), _ptr(lam), nc,
+                                          _ptr(cols) if nc else None, _ptr(lpc), _ptr(gmc),
+                                          _ptr(dX), _ptr(dW), _ptr(db))
         if rc != 0:
             raise ValueError("oracle_pcx failed (code %d)" % rc)
         out = {"loss": loss.value, "utt_loss": utt[:N].copy(), "status": st[:N].copy(),
                "dX": dX, "dW": dW, "db": db}
+        if beam is not None:
+            out["delta"] = delta[:N].copy()
+            out["margin"] = margin[:N].copy()
         out["lambda"] = lam[:M].copy() if want_lambda else None
         out["logp_cols"] = lpc[:M, :nc].copy() if nc else None
         out["gamma_cols"] = gmc[:M, :nc].copy() if gmc is not None else None
@@ -208,8 +253,12 @@ def ctc_logits(Z, y, blank, grad=1.0, want_grad=True):
     return _oracle().ctc_logits(Z, y, blank, grad=grad, want_grad=want_grad)
 
 
+def ctc_beam(Z, y, blank, beam, grad=1.0, want_grad=True):
+    return _oracle().ctc_beam(Z, y, blank, beam, grad=grad, want_grad=want_grad)
+
+
 def pcx(X, W, b, frame_counts, tgt_off, tgt, blank, grad=1.0, cols=None, want_dX=True,
-        want_dW=True, want_db=True, want_gamma=False, want_lambda=True):
+        want_dW=True, want_db=True, want_gamma=False, want_lambda=True, beam=None):
     return _oracle().pcx(X, W, b, frame_counts, tgt_off, tgt, blank, grad=grad, cols=cols,
                          want_dX=want_dX, want_dW=want_dW, want_db=want_db,
-                         want_gamma=want_gamma, want_lambda=want_lambda)
+                         want_gamma=want_gamma, want_lambda=want_lambda, beam=beam)

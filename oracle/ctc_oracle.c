@@ -28,6 +28,11 @@
  * whose loss comes out nonfinite contribute zero loss and zero gradient
  * (App. B.1; PrunedCTC README, return value).
  *
+ * With a finite alignment beam (oracle_ctc_beam, oracle_pcx_beam) the same
+ * quantities are formed over the alignments that survive log-score lattice
+ * pruning relative to the best alignment (the pages' finite-beam objective
+ * L_beta, App. B.1; the reading is stated at oracle_ctc_beam).
+ *
  * Parity pins for every function here live in tests/test_oracle_pins.py
  * (brute-force alignment enumeration, closed forms, finite differences,
  * the reduced-vocabulary identity of Proposition 1, and invariants).
@@ -234,6 +239,216 @@ int oracle_ctc_logits(int T, int V, int blank, const double* Z,
 }
 
 /*
+ * Finite-beam CTC for one utterance from raw logits Z (T x V): the pages'
+ * pruned objective L_beta ("Pruned CTC for Memory-Efficient
+ * Large-Vocabulary ASR Training", App. B.1 finite-beam computation, the
+ * finite-beam gap analysis of App. B, and the PrunedCTC README's
+ * "alignment pruning" with a log-score beam, output_beam).
+ *
+ * The body of the objective's equation is missing from the pages; the
+ * reading taken here is lattice pruning relative to the best alignment:
+ *   * the lattice of utterance n has a node (t, s) per frame t and state s of
+ *     the blank-interleaved labels, an initial arc into (0, 0) and (0, 1), an
+ *     arc (t-1, s') -> (t, s) for every CTC transition (stay, advance, skip a
+ *     blank between different labels), and a final arc out of (T-1, S-1) and
+ *     (T-1, S-2); entering (t, s) scores the log-probability logp[t][l'_s];
+ *   * the score of an arc is that of the best complete alignment through it:
+ *     (vf[t-1][s'] + logp[t][l'_s]) + vb[t][s], with vf the best score of a
+ *     prefix ending in a node (its emission included) and vb the best score
+ *     of the suffix after it (its emission excluded); the initial arc into
+ *     (0, s) scores vf[0][s] + vb[0][s], the final arc out of (T-1, s)
+ *     scores vf[T-1][s];
+ *   * an arc is kept when its score is at least B - beam, B the best
+ *     alignment's score (evaluated in IEEE FP64 in exactly the association
+ *     written above); an alignment is retained when all of its arcs are;
+ *   * L_beta = -log of the summed probability of the retained alignments,
+ *     by the forward / backward recursions restricted to kept arcs; with
+ *     the retained lattice held fixed, the logit gradient is
+ *     grad * (p_v(m) - gamma^beta_v(m)), gamma^beta the occupancy over the
+ *     retained alignments (App. B.1: "with the retained lattice locally
+ *     fixed").
+ * beam = INFINITY keeps every arc.  A nonfinite L_beta (an empty retained
+ * lattice, or nonfinite scores) is replaced by zero loss and zero gradient
+ * (App. B.1), status 2; unalignable utterances give status 1.
+ *
+ * Outputs besides those of oracle_ctc_logits:
+ *   full_loss_out  the unpruned loss L_n of the same utterance (NaN when the
+ *                  unpruned loss is excluded)
+ *   margin_out     the smallest |arc score - (B - beam)| over arcs with a
+ *                  finite score (INFINITY for an infinite beam or without
+ *                  arcs): how far the pruning decision is from a tie.
+ */
+int oracle_ctc_beam(int T, int V, int blank, const double* Z, const int32_t* y,
+                    int L, double beam, double grad, double* loss_out,
+                    int* status_out, double* full_loss_out, double* lambda_out,
+                    double* dZ, double* gamma, double* margin_out) {
+  if (T <= 0 || V <= 0 || L < 0 || blank < 0 || blank >= V || !(beam >= 0.0))
+    return ORACLE_ERR_ARG;
+  /* normalizer and unpruned loss from the full-vocabulary routine above */
+  double* lam = (double*)malloc(sizeof(double) * (size_t)T);
+  if (!lam) return ORACLE_ERR_NOMEM;
+  double full = 0.0;
+  int full_status = 0;
+  int rc = oracle_ctc_logits(T, V, blank, Z, y, L, grad, &full, &full_status,
+                             lam, NULL, NULL);
+  if (rc != ORACLE_OK) {
+    free(lam);
+    return rc;
+  }
+  if (lambda_out) memcpy(lambda_out, lam, sizeof(double) * (size_t)T);
+  if (full_loss_out) *full_loss_out = full_status == 0 ? full : NAN;
+  if (margin_out) *margin_out = INFINITY;
+  *loss_out = 0.0;
+  *status_out = full_status;
+  if (dZ) memset(dZ, 0, sizeof(double) * (size_t)T * V);
+  if (gamma) memset(gamma, 0, sizeof(double) * (size_t)T * V);
+  if (full_status == 1) { /* not structurally alignable: nothing to prune */
+    free(lam);
+    return ORACLE_OK;
+  }
+
+  const int S = 2 * L + 1;
+  /* per node: label, and its incoming arcs (predecessor states) */
+  int32_t* lab = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
+  int32_t* npred = (int32_t*)malloc(sizeof(int32_t) * (size_t)S);
+  int32_t* pred = (int32_t*)malloc(sizeof(int32_t) * 3 * (size_t)S);
+  double* em = (double*)malloc(sizeof(double) * (size_t)T * S);   /* logp at nodes */
+  double* vf = (double*)malloc(sizeof(double) * (size_t)T * S);
+  double* vb = (double*)malloc(sizeof(double) * (size_t)T * S);
+  double* fa = (double*)malloc(sizeof(double) * (size_t)T * S);   /* pruned alpha */
+  double* fb = (double*)malloc(sizeof(double) * (size_t)T * S);   /* pruned beta */
+  unsigned char* keep = (unsigned char*)malloc((size_t)T * S * 3); /* kept in-arcs */
+  unsigned char* kinit = (unsigned char*)calloc((size_t)S, 1);
+  unsigned char* kfin = (unsigned char*)calloc((size_t)S, 1);
+  if (!lab || !npred || !pred || !em || !vf || !vb || !fa || !fb || !keep || !kinit ||
+      !kfin) {
+    free(lam); free(lab); free(npred); free(pred); free(em); free(vf); free(vb);
+    free(fa); free(fb); free(keep); free(kinit); free(kfin);
+    return ORACLE_ERR_NOMEM;
+  }
+  for (int s = 0; s < S; ++s) {
+    lab[s] = (s & 1) ? y[s / 2] : blank;
+    int k = 0;
+    pred[3 * s + k++] = s;                          /* stay */
+    if (s >= 1) pred[3 * s + k++] = s - 1;          /* advance */
+    /* skip over a blank, only into a label that differs from the one before */
+    if (s >= 2 && lab[s] != blank && y[s / 2 - 1] != lab[s]) pred[3 * s + k++] = s - 2;
+    npred[s] = k;
+  }
+  for (int t = 0; t < T; ++t)
+    for (int s = 0; s < S; ++s)
+      em[(size_t)t * S + s] = Z[(size_t)t * V + lab[s]] - lam[t];
+  const int first_final = S >= 2 ? S - 2 : 0;
+
+  /* best prefix scores (emission included) */
+  for (int s = 0; s < S; ++s) vf[s] = s <= 1 ? em[s] : -INFINITY;
+  for (int t = 1; t < T; ++t)
+    for (int s = 0; s < S; ++s) {
+      double m = -INFINITY;
+      for (int k = 0; k < npred[s]; ++k) {
+        const double c = vf[(size_t)(t - 1) * S + pred[3 * s + k]];
+        if (c > m) m = c;
+      }
+      vf[(size_t)t * S + s] = m + em[(size_t)t * S + s];
+    }
+  /* best suffix scores (emission of the node itself excluded) */
+  for (int s = 0; s < S; ++s) vb[(size_t)(T - 1) * S + s] = s >= first_final ? 0.0 : -INFINITY;
+  for (int t = T - 2; t >= 0; --t) {
+    for (int s = 0; s < S; ++s) vb[(size_t)t * S + s] = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2)
+      for (int k = 0; k < npred[s2]; ++k) {
+        const int s = pred[3 * s2 + k];
+        const double c = em[(size_t)(t + 1) * S + s2] + vb[(size_t)(t + 1) * S + s2];
+        if (c > vb[(size_t)t * S + s]) vb[(size_t)t * S + s] = c;
+      }
+  }
+  double best = -INFINITY;
+  for (int s = first_final; s < S; ++s)
+    if (vf[(size_t)(T - 1) * S + s] > best) best = vf[(size_t)(T - 1) * S + s];
+  const double thr = best - beam;
+
+  /* which arcs are kept */
+  double margin = INFINITY;
+#define ORACLE_KEEP(score, flag)                                   \
+  do {                                                             \
+    const double sc_ = (score);                                    \
+    (flag) = sc_ >= thr;                                           \
+    if (isfinite(sc_) && isfinite(thr) && fabs(sc_ - thr) < margin) \
+      margin = fabs(sc_ - thr);                                    \
+  } while (0)
+  for (int s = 0; s <= 1 && s < S; ++s) ORACLE_KEEP(vf[s] + vb[s], kinit[s]);
+  for (int s = first_final; s < S; ++s) ORACLE_KEEP(vf[(size_t)(T - 1) * S + s], kfin[s]);
+  for (int t = 1; t < T; ++t)
+    for (int s = 0; s < S; ++s)
+      for (int k = 0; k < npred[s]; ++k) {
+        const double sc = (vf[(size_t)(t - 1) * S + pred[3 * s + k]] + em[(size_t)t * S + s]) +
+                          vb[(size_t)t * S + s];
+        ORACLE_KEEP(sc, keep[((size_t)t * S + s) * 3 + k]);
+      }
+#undef ORACLE_KEEP
+  if (margin_out) *margin_out = margin;
+
+  /* forward recursion over kept arcs */
+  for (int s = 0; s < S; ++s) fa[s] = (s <= 1 && kinit[s]) ? em[s] : -INFINITY;
+  for (int t = 1; t < T; ++t)
+    for (int s = 0; s < S; ++s) {
+      double a = -INFINITY;
+      for (int k = 0; k < npred[s]; ++k)
+        if (keep[((size_t)t * S + s) * 3 + k])
+          a = log_add(a, fa[(size_t)(t - 1) * S + pred[3 * s + k]]);
+      fa[(size_t)t * S + s] = a + em[(size_t)t * S + s];
+    }
+  double logP = -INFINITY;
+  for (int s = first_final; s < S; ++s)
+    if (kfin[s]) logP = log_add(logP, fa[(size_t)(T - 1) * S + s]);
+  /* backward recursion over the same arcs (emission of the node included) */
+  for (int s = 0; s < S; ++s)
+    fb[(size_t)(T - 1) * S + s] =
+        (s >= first_final && kfin[s]) ? em[(size_t)(T - 1) * S + s] : -INFINITY;
+  for (int t = T - 2; t >= 0; --t) {
+    for (int s = 0; s < S; ++s) fb[(size_t)t * S + s] = -INFINITY;
+    for (int s2 = 0; s2 < S; ++s2)
+      for (int k = 0; k < npred[s2]; ++k)
+        if (keep[((size_t)(t + 1) * S + s2) * 3 + k]) {
+          const int s = pred[3 * s2 + k];
+          fb[(size_t)t * S + s] = log_add(fb[(size_t)t * S + s], fb[(size_t)(t + 1) * S + s2]);
+        }
+    for (int s = 0; s < S; ++s) fb[(size_t)t * S + s] += em[(size_t)t * S + s];
+  }
+
+  if (!isfinite(logP)) {
+    *status_out = 2;
+  } else {
+    *status_out = 0;
+    *loss_out = -logP;
+    if (dZ || gamma) {
+      double* occ = (double*)calloc((size_t)V, sizeof(double));
+      if (!occ) {
+        free(lam); free(lab); free(npred); free(pred); free(em); free(vf); free(vb);
+        free(fa); free(fb); free(keep); free(kinit); free(kfin);
+        return ORACLE_ERR_NOMEM;
+      }
+      for (int t = 0; t < T; ++t) {
+        for (int v = 0; v < V; ++v) occ[v] = 0.0;
+        for (int s = 0; s < S; ++s) {
+          const size_t o = (size_t)t * S + s;
+          occ[lab[s]] += exp(fa[o] + fb[o] - em[o] - logP);
+        }
+        for (int v = 0; v < V; ++v) {
+          const double pv = exp(Z[(size_t)t * V + v] - lam[t]);
+          if (gamma) gamma[(size_t)t * V + v] = occ[v];
+          if (dZ) dZ[(size_t)t * V + v] = grad * (pv - occ[v]);
+        }
+      }
+      free(occ);
+    }
+  }
+  free(lam); free(lab); free(npred); free(pred); free(em); free(vf); free(vb);
+  free(fa); free(fb); free(keep); free(kinit); free(kfin);
+  return ORACLE_OK;
+}
+
+/*
  * The whole path: head projection, CTC loss and gradients for a batch of N
  * utterances stacked without padding into X (M x D, row-major; utterance n
  * owns rows [o_n, o_n + T_n) with o_n = T_0 + ... + T_{n-1}).  W is V x D
@@ -253,13 +468,13 @@ int oracle_ctc_logits(int T, int V, int blank, const double* Z,
  * block is materialised in FP64 (the dense reference groups whole
  * utterances, App. B "accuracy" paragraph).
  */
-int oracle_pcx(int N, int M, int D, int V, int blank, const double* X,
-               const double* W, const double* b, const int32_t* frame_counts,
-               const int32_t* tgt_off, const int32_t* tgt, double grad,
-               double* loss_out, double* utt_loss, int32_t* status,
-               double* lambda, int ncols, const int32_t* cols,
-               double* logp_cols, double* gamma_cols, double* dX, double* dW,
-               double* db) {
+static int pcx_batch(int N, int M, int D, int V, int blank, const double* X,
+                     const double* W, const double* b, const int32_t* frame_counts,
+                     const int32_t* tgt_off, const int32_t* tgt, double beam, double grad,
+                     double* loss_out, double* utt_loss, int32_t* status, double* delta,
+                     double* margin, double* lambda, int ncols, const int32_t* cols,
+                     double* logp_cols, double* gamma_cols, double* dX, double* dW,
+                     double* db) {
   if (N < 0 || M < 0 || D <= 0 || V <= 0 || blank < 0 || blank >= V)
     return ORACLE_ERR_ARG;
   long long sumT = 0;
@@ -304,16 +519,23 @@ int oracle_pcx(int N, int M, int D, int V, int blank, const double* X,
         Zn[(size_t)t * V + v] = acc + (b ? b[v] : 0.0);
       }
     }
-    double loss_n = 0.0;
+    double loss_n = 0.0, full_n = 0.0, margin_n = INFINITY;
     int st = 0;
-    int rc = oracle_ctc_logits(T, V, blank, Zn, tgt + tgt_off[n], L, grad,
-                               &loss_n, &st, lam, dZn, gam);
+    int rc = beam == INFINITY
+                 ? oracle_ctc_logits(T, V, blank, Zn, tgt + tgt_off[n], L, grad,
+                                     &loss_n, &st, lam, dZn, gam)
+                 : oracle_ctc_beam(T, V, blank, Zn, tgt + tgt_off[n], L, beam, grad,
+                                   &loss_n, &st, &full_n, lam, dZn, gam, &margin_n);
+    if (beam == INFINITY) full_n = st == 0 ? loss_n : NAN;
     if (rc != ORACLE_OK) {
       free(Zn); free(lam); free(dZn); free(gam);
       return rc;
     }
     if (utt_loss) utt_loss[n] = loss_n;
     if (status) status[n] = st;
+    /* posterior mass of the discarded alignments, 1 - exp(-(L_beta - L)) */
+    if (delta) delta[n] = st == 0 ? -expm1(-(loss_n - full_n)) : NAN;
+    if (margin) margin[n] = margin_n;
     if (st == 0) total += loss_n;
     if (lambda) memcpy(lambda + row0, lam, sizeof(double) * (size_t)T);
     for (int t = 0; t < T; ++t) {
@@ -358,6 +580,40 @@ int oracle_pcx(int N, int M, int D, int V, int blank, const double* X,
   }
   *loss_out = total;
   return ORACLE_OK;
+}
+
+int oracle_pcx(int N, int M, int D, int V, int blank, const double* X,
+               const double* W, const double* b, const int32_t* frame_counts,
+               const int32_t* tgt_off, const int32_t* tgt, double grad,
+               double* loss_out, double* utt_loss, int32_t* status,
+               double* lambda, int ncols, const int32_t* cols,
+               double* logp_cols, double* gamma_cols, double* dX, double* dW,
+               double* db) {
+  return pcx_batch(N, M, D, V, blank, X, W, b, frame_counts, tgt_off, tgt, INFINITY, grad,
+                   loss_out, utt_loss, status, NULL, NULL, lambda, ncols, cols, logp_cols,
+                   gamma_cols, dX, dW, db);
+}
+
+/*
+ * The whole path with the finite-beam objective L_beta (oracle_ctc_beam per
+ * utterance; beam = INFINITY gives oracle_pcx).  Extra outputs (may be NULL):
+ *   delta[N]   1 - exp(-(L_beta,n - L_n)), the posterior mass of the
+ *              alignments the pruning discards (the pages' delta_n); NaN for
+ *              excluded utterances
+ *   margin[N]  per utterance, the distance of the nearest arc score from the
+ *              pruning threshold (see oracle_ctc_beam)
+ */
+int oracle_pcx_beam(int N, int M, int D, int V, int blank, const double* X,
+                    const double* W, const double* b, const int32_t* frame_counts,
+                    const int32_t* tgt_off, const int32_t* tgt, double beam, double grad,
+                    double* loss_out, double* utt_loss, int32_t* status, double* delta,
+                    double* margin, double* lambda, int ncols, const int32_t* cols,
+                    double* logp_cols, double* gamma_cols, double* dX, double* dW,
+                    double* db) {
+  if (!(beam >= 0.0)) return ORACLE_ERR_ARG;
+  return pcx_batch(N, M, D, V, blank, X, W, b, frame_counts, tgt_off, tgt, beam, grad,
+                   loss_out, utt_loss, status, delta, margin, lambda, ncols, cols, logp_cols,
+                   gamma_cols, dX, dW, db);
 }
 
 /* Number of threads OpenMP will use for the parallel loops above. */

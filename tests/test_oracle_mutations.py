@@ -77,6 +77,29 @@ MUTANTS = [
     ("gamma_gather_ignores_cols", "= gam[(size_t)t * V + cols[c]];", "= gam[(size_t)t * V + c];"),
     ("gather_rows_of_first_utterance", "logp_cols[(size_t)(row0 + t) * ncols + c] =",
      "logp_cols[(size_t)t * ncols + c] ="),
+    # finite-beam pruning (oracle_ctc_beam).  Dropping the check of the
+    # initial or of the final arcs is no mistake under this reading: an arc
+    # out of a first-frame node (into a last-frame node) never scores above
+    # the initial (final) arc of that node, so those checks never decide.
+    ("beam_threshold_sign", "const double thr = best - beam;", "const double thr = best + beam;"),
+    ("beam_suffix_includes_emission",
+     "vb[(size_t)(T - 1) * S + s] = s >= first_final ? 0.0 : -INFINITY;",
+     "vb[(size_t)(T - 1) * S + s] = s >= first_final ? em[(size_t)(T - 1) * S + s] : -INFINITY;"),
+    ("beam_backward_unmasked", "if (keep[((size_t)(t + 1) * S + s2) * 3 + k]) {", "if (1) {"),
+    ("beam_forward_unmasked", "if (keep[((size_t)t * S + s) * 3 + k])\n          a = log_add",
+     "if (1)\n          a = log_add"),
+    ("beam_arc_score_drops_suffix",
+     "em[(size_t)t * S + s]) +\n                          vb[(size_t)t * S + s];",
+     "em[(size_t)t * S + s]);"),
+    ("beam_skip_between_repeats", "if (s >= 2 && lab[s] != blank && y[s / 2 - 1] != lab[s]) pred",
+     "if (s >= 2 && lab[s] != blank) pred"),
+    ("beam_viterbi_sums", "        if (c > m) m = c;", "        m = log_add(m, c);"),
+    ("beam_delta_sign", "-expm1(-(loss_n - full_n))", "-expm1(loss_n - full_n)"),
+    ("beam_occupancy_double_emission", "occ[lab[s]] += exp(fa[o] + fb[o] - em[o] - logP);",
+     "occ[lab[s]] += exp(fa[o] + fb[o] - logP);"),
+    ("beam_best_over_all_states",
+     "for (int s = first_final; s < S; ++s)\n    if (vf[(size_t)(T - 1) * S + s] > best)",
+     "for (int s = 0; s < S; ++s)\n    if (vf[(size_t)(T - 1) * S + s] > best)"),
 ]
 
 

@@ -168,6 +168,237 @@ def test_column_gather_at_unsorted_columns():
     assert not np.allclose(out["logp_cols"], logp[:, :len(cols)])
 
 
+# ------------------------------------------------------------ finite beam
+def node_states(seq, blank):
+    """State of each frame of an alignment in the blank-interleaved label
+    sequence: 2k on a blank after k emitted labels, 2k - 1 on the k-th label
+    (the node of the alignment lattice the frame visits)."""
+    out = []
+    k = 0
+    prev = None
+    for v in seq:
+        if v != blank and v != prev:
+            k += 1
+        out.append(2 * k if v == blank else 2 * k - 1)
+        prev = v
+    return out
+
+
+def brute_force_beam(Z, y, blank, beam):
+    """Retained-alignment sum by enumeration: an alignment is kept when every
+    arc it uses (the initial arc into its first node, each frame-to-frame arc,
+    the final arc out of its last node) lies on some alignment scoring within
+    `beam` of the best one.  Returns (P_beta, gamma_beta, P, B, n_kept)."""
+    T, V = Z.shape
+    zmax = Z.max(1, keepdims=True)
+    logp = Z - zmax - np.log(np.sum(np.exp(Z - zmax), 1, keepdims=True))
+    paths = []
+    for seq in itertools.product(range(V), repeat=T):
+        if collapse(seq, blank) == list(y):
+            sc = sum(logp[t, v] for t, v in enumerate(seq))
+            st = node_states(seq, blank)
+            arcs = [("init", st[0]), ("final", st[-1])] + \
+                   [(t, st[t - 1], st[t]) for t in range(1, T)]
+            paths.append((seq, sc, arcs))
+    best = max(sc for _, sc, _ in paths)
+    arc_best = {}
+    for _, sc, arcs in paths:
+        for a in arcs:
+            arc_best[a] = max(arc_best.get(a, -np.inf), sc)
+    P = Pb = 0.0
+    gam = np.zeros((T, V))
+    kept = 0
+    for seq, sc, arcs in paths:
+        P += math.exp(sc)
+        if all(arc_best[a] >= best - beam for a in arcs):
+            kept += 1
+            Pb += math.exp(sc)
+            for t, v in enumerate(seq):
+                gam[t, v] += math.exp(sc)
+    return Pb, gam / Pb if Pb > 0 else gam, P, best, kept
+
+
+@pytest.mark.parametrize("T,V,y,blank,seed,beam", [
+    (6, 4, [1, 2], 0, 40, 1.0),
+    (6, 4, [1, 2], 0, 40, 3.0),
+    (7, 3, [1, 1], 0, 41, 2.0),
+    (6, 4, [2, 1, 2], 3, 42, 1.5),
+    (7, 4, [3], 1, 43, 4.0),
+    (6, 4, [], 0, 44, 0.7),
+    (8, 3, [1, 2, 1], 0, 45, 2.5),
+])
+def test_beam_brute_force_retained_alignments(T, V, y, blank, seed, beam):
+    """Loss over the retained alignments and their occupancies, against the
+    enumeration of every alignment and of the best alignment through each
+    lattice arc."""
+    rng = np.random.default_rng(seed)
+    Z = rng.normal(scale=2.0, size=(T, V))
+    Pb, gam, P, best, kept = brute_force_beam(Z, y, blank, beam)
+    r = oracle.ctc_beam(Z, y, blank, beam)
+    assert r["margin"] > 1e-9          # no arc within rounding of the threshold
+    assert r["status"] == 0 and kept > 0
+    assert r["loss"] == pytest.approx(-math.log(Pb), rel=1e-12, abs=1e-12)
+    assert r["full_loss"] == pytest.approx(-math.log(P), rel=1e-12, abs=1e-12)
+    np.testing.assert_allclose(r["gamma"], gam, rtol=1e-10, atol=1e-13)
+    p = np.exp(Z - r["lambda"][:, None])
+    np.testing.assert_allclose(r["dZ"], p - gam, rtol=1e-10, atol=1e-13)
+
+
+def test_beam_best_is_over_complete_alignments():
+    """With the blank strongly favoured, the best-scoring prefix at the last
+    frame ends in an unfinished state (all blanks); the threshold must come
+    from the best complete alignment, as the enumeration's does."""
+    rng = np.random.default_rng(50)
+    T, V, y, beam = 7, 4, [1, 2, 3], 2.0
+    Z = rng.normal(size=(T, V))
+    Z[:, 0] += 4.0
+    Pb, gam, P, best, kept = brute_force_beam(Z, y, 0, beam)
+    r = oracle.ctc_beam(Z, y, 0, beam)
+    lp = Z - r["lambda"][:, None]
+    assert lp[:, 0].sum() > best + beam      # the all-blank prefix beats every alignment
+    assert r["status"] == 0 and r["margin"] > 1e-9
+    assert r["loss"] == pytest.approx(-math.log(Pb), rel=1e-12)
+    np.testing.assert_allclose(r["gamma"], gam, rtol=1e-10, atol=1e-13)
+
+
+def test_beam_prunes_something_in_the_brute_force_cases():
+    """The parameter sets above do prune (retained fewer than all), and keep
+    more than the best alignment alone in some."""
+    fewer = more = 0
+    for T, V, y, blank, seed, beam in [(6, 4, [1, 2], 0, 40, 1.0), (7, 3, [1, 1], 0, 41, 2.0),
+                                       (8, 3, [1, 2, 1], 0, 45, 2.5)]:
+        Z = np.random.default_rng(seed).normal(scale=2.0, size=(T, V))
+        Pb, _, P, _, kept = brute_force_beam(Z, y, blank, beam)
+        total = math.comb(T + len(y) - repeats(y), 2 * len(y))
+        fewer += kept < total
+        more += kept > 1
+    assert fewer == 3 and more >= 2
+
+
+def test_beam_limits():
+    """An unbounded beam is the unpruned loss; a beam just above zero (1e-9:
+    at exactly zero, rounding of the arc scores can put the best alignment's
+    own arcs below its score and empty the lattice) keeps only the best
+    alignment (unique here), so the loss is minus its score; the loss never
+    increases as the beam widens and never drops below the unpruned one."""
+    rng = np.random.default_rng(46)
+    T, V, y = 9, 4, [1, 3, 3]
+    Z = rng.normal(scale=2.0, size=(T, V))
+    full = oracle.ctc_logits(Z, y, 0)
+    inf = oracle.ctc_beam(Z, y, 0, math.inf)
+    assert inf["loss"] == full["loss"] and inf["full_loss"] == full["loss"]
+    np.testing.assert_array_equal(inf["dZ"], full["dZ"])
+    Pb, _, _, best, kept = brute_force_beam(Z, y, 0, 1e-9)
+    assert kept == 1
+    zero = oracle.ctc_beam(Z, y, 0, 1e-9)
+    assert zero["status"] == 0
+    assert zero["loss"] == pytest.approx(-best, rel=1e-12)
+    gam = zero["gamma"]
+    assert np.all((gam == 0.0) | (np.abs(gam - 1.0) < 1e-12))  # one path: one-hot
+    prev = math.inf
+    for beam in [1e-9, 0.5, 1.0, 2.0, 4.0, 8.0, 16.0, 64.0, math.inf]:
+        r = oracle.ctc_beam(Z, y, 0, beam, want_grad=False)
+        assert r["loss"] <= prev + 1e-12 and r["loss"] >= full["loss"] - 1e-12
+        prev = r["loss"]
+    assert prev == full["loss"]
+
+
+def test_beam_occupancy_mixture_bound():
+    """The full occupancy mixes the retained and the discarded ones with
+    weight delta, so per frame the L1 distance between gamma and gamma_beta is
+    at most 2 delta (the pages' finite-beam gap analysis), with delta = 1 -
+    exp(-(L_beta - L)) = 1 - P_beta / P."""
+    rng = np.random.default_rng(47)
+    T, V, y = 12, 5, [2, 4, 4, 1]
+    Z = rng.normal(scale=2.5, size=(T, V))
+    full = oracle.ctc_logits(Z, y, 0)
+    seen = 0
+    for beam in [1.0, 2.0, 3.0, 5.0]:
+        r = oracle.ctc_beam(Z, y, 0, beam)
+        gap = r["loss"] - full["loss"]
+        delta = -math.expm1(-gap)
+        assert gap >= -1e-12 and 0.0 <= delta < 1.0
+        l1 = np.abs(full["gamma"] - r["gamma"]).sum(1)
+        assert np.all(l1 <= 2 * delta + 1e-12)
+        seen += delta > 1e-6
+    assert seen >= 2
+
+
+def test_beam_finite_differences():
+    """Gradient of L_beta with the retained lattice held fixed (the pages'
+    "locally fixed" lattice): central differences of the loss through the
+    head, at a beam whose pruning decisions are far from ties."""
+    rng = np.random.default_rng(48)
+    V, D = 5, 3
+    T = [7, 6]
+    ys = [[1, 3], [2, 2]]
+    M = sum(T)
+    X = rng.normal(size=(M, D))
+    W = rng.normal(size=(V, D))
+    b = rng.normal(size=V)
+    off = np.concatenate([[0], np.cumsum([len(y) for y in ys])])
+    tgt = np.concatenate(ys)
+    beam = 1.5
+    out = oracle.pcx(X, W, b, T, off, tgt, 0, grad=1.0, beam=beam)
+    assert out["status"].tolist() == [0, 0]
+    assert np.all(out["margin"] > 1e-3) and np.all(out["delta"] > 1e-4)
+
+    def f(X_, W_, b_):
+        return oracle.pcx(X_, W_, b_, T, off, tgt, 0, want_dX=False, want_dW=False,
+                          want_db=False, beam=beam)["loss"]
+
+    h = 1e-6
+    for name, arr, grad in (("X", X, out["dX"]), ("W", W, out["dW"]), ("b", b, out["db"])):
+        num = np.zeros_like(arr)
+        it = np.nditer(arr, flags=["multi_index"])
+        for _ in it:
+            idx = it.multi_index
+            ap = arr.copy(); ap[idx] += h
+            am = arr.copy(); am[idx] -= h
+            args_p = {"X": (ap, W, b), "W": (X, ap, b), "b": (X, W, ap)}[name]
+            args_m = {"X": (am, W, b), "W": (X, am, b), "b": (X, W, am)}[name]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        err = np.linalg.norm(num - grad) / np.linalg.norm(grad)
+        assert err < 1e-6, (name, err)
+
+
+def test_beam_batch_matches_per_utterance_and_delta():
+    """The batch routine with a beam: per-utterance losses, the discarded mass
+    delta_n = 1 - P_beta / P (by enumeration), exclusion of an unalignable
+    utterance, and the empty-target utterance (a single alignment, never
+    pruned)."""
+    rng = np.random.default_rng(49)
+    V, D = 4, 3
+    T = [6, 2, 5, 6]
+    ys = [[1, 2], [3, 3], [], [2, 1]]  # the second needs 3 frames
+    M = sum(T)
+    X = rng.normal(size=(M, D))
+    W = rng.normal(scale=2.0, size=(V, D))
+    b = rng.normal(size=V)
+    off = np.concatenate([[0], np.cumsum([len(y) for y in ys])])
+    tgt = np.concatenate([np.asarray(y, np.int64) for y in ys])
+    beam = 1.2
+    out = oracle.pcx(X, W, b, T, off, tgt, 0, beam=beam, cols=[0, 1, 2, 3], want_gamma=True)
+    assert out["status"].tolist() == [0, 1, 0, 0]
+    assert out["utt_loss"][1] == 0.0 and math.isnan(out["delta"][1])
+    assert np.all(out["dX"][6:8] == 0.0)
+    row = 0
+    total = 0.0
+    for n, y in enumerate(ys):
+        Zn = X[row:row + T[n]] @ W.T + b
+        if n != 1:
+            Pb, gam, P, _, _ = brute_force_beam(Zn, y, 0, beam)
+            assert out["utt_loss"][n] == pytest.approx(-math.log(Pb), rel=1e-12)
+            assert out["delta"][n] == pytest.approx(1.0 - Pb / P, rel=1e-9, abs=1e-15)
+            np.testing.assert_allclose(out["gamma_cols"][row:row + T[n]], gam, rtol=1e-10,
+                                       atol=1e-13)
+            total += -math.log(Pb)
+        row += T[n]
+    assert out["delta"][2] == 0.0
+    assert out["delta"][0] > 1e-6 or out["delta"][3] > 1e-6
+    assert out["loss"] == pytest.approx(total, rel=1e-12)
+
+
 # ----------------------------------------------------------- closed forms
 def test_readme_example_golden():
     g = json.load(open(os.path.join(GOLDEN, "readme_example.json")))
