@@ -6,7 +6,9 @@
  * ASR Training" (Sec. 3.1 problem statement, Eq. 1-2; Sec. 3.2 selected
  * classes and Proposition 1; Sec. 3.3 / App. B.1 chunked projection, FP64
  * normalizer and backward recomputation) with an unbounded alignment beam,
- * i.e. the pages' "unpruned reduced CTC".  The calls mirror the interface of
+ * i.e. the pages' "unpruned reduced CTC", by default, and with the pages'
+ * finite-beam objective L_beta (App. B.1) after pcx_set_beam.  The calls
+ * mirror the interface of
  * the PrunedCTC README (pruned_ctc_loss: encoder states, head weight and
  * bias, ragged targets, frame counts, chunk size, blank id; the return value
  * is the plain sum of per-utterance losses; fp32 or bf16 inputs, gradients
@@ -221,6 +223,42 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW,
  */
 pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta,
                                  void* stream);
+
+/*
+ * Alignment beam of the following pcx_forward calls of this context (the
+ * PrunedCTC README's output_beam; "Pruned CTC for Memory-Efficient
+ * Large-Vocabulary ASR Training", App. B.1 finite-beam computation and the
+ * finite-beam gap analysis).  beam = +inf (the default) keeps every
+ * alignment: the exact loss.  A finite beam >= 0 prunes the alignment
+ * lattice of each utterance relative to its best alignment: the arc
+ * (t-1, s') -> (t, s) between states of the blank-interleaved labels is kept
+ * when the best complete alignment through it scores at least B_n - beam
+ * (scores are sums of the FP32 log-probabilities S in FP64; the arc's score
+ * is (best prefix score at (t-1, s') + S_t(s)) + best suffix score after
+ * (t, s), evaluated in that order), B_n being the best alignment's score;
+ * the initial and final arcs likewise.  The loss of an utterance is then
+ * -log of the summed probability of the alignments all of whose arcs are
+ * kept, and pcx_backward differentiates it with the kept arcs held fixed
+ * (gamma is the occupancy over the retained alignments).  An utterance
+ * whose retained lattice comes out empty, or whose loss is not finite,
+ * contributes zero loss and gradient and is counted in n_nonfinite.  Costs
+ * two extra passes over the lattice in the forward call (best scores, arc
+ * masks: one byte per lattice node of workspace).  PCX_ERR_ARG for a
+ * negative or NaN beam.
+ */
+pcx_status pcx_set_beam(pcx_ctx* ctx, double beam);
+
+/*
+ * Posterior mass of the alignments the beam of the last pcx_forward
+ * discarded, per utterance: delta_n = 1 - exp(-(L_beta,n - L_n)), with L_n
+ * the unpruned loss on the same scores S (the pages' delta_n estimate; both
+ * losses in FP64).  0 for every included utterance after an unbounded beam;
+ * NaN for excluded utterances (unalignable, or a nonfinite pruned or
+ * unpruned loss).  Runs the unpruned forward recursion (losses only; the
+ * workspace of the pruned backward is untouched) and synchronises the
+ * context's stream.  out: N doubles (capacity >= N).
+ */
+pcx_status pcx_get_discarded_mass(pcx_ctx* ctx, double* out, int64_t capacity);
 
 /*
  * Formulation used by the following pcx_forward calls of this context

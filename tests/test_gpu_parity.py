@@ -412,9 +412,8 @@ def test_device_side_validation_errors():
         badfc[1] = 21
         c.forward(X, W, b, off, tgt, badfc, 0, 4)
     assert e.value.status == 4
-    with pytest.raises(PcxError) as e:
+    with pytest.raises(ValueError, match="dtypes"):   # fp16: the binding refuses it
         c.forward(X.half(), W.half(), b.half(), off, tgt, fc, 0, 4)
-    assert e.value.status == 2
     with pytest.raises(PcxError) as e:   # failed forward leaves no state for backward
         c.backward(1.0, torch.empty_like(X))
     assert e.value.status == 5

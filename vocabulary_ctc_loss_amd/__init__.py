@@ -175,6 +175,17 @@ class Context:
             pass
 
     # -------------------------------------------------------------- calls
+    def set_beam(self, beam: float = float("inf")):
+        """Alignment beam of the following forward calls (inf: every
+        alignment, the exact loss; a finite beam: the pruned objective
+        L_beta, see pcx_set_beam)."""
+        check(self._lib.pcx_set_beam(self._h, float(beam)))
+
+    def discarded_mass(self):
+        """delta_n = 1 - exp(-(L_beta,n - L_n)) of the last forward, per
+        utterance (NaN for excluded ones)."""
+        return self._get(self._lib.pcx_get_discarded_mass, self._shape["N"], np.float64)
+
     def set_formulation(self, grouped: bool):
         """Direct (default) or grouped ("other"-column) normalizer and
         complement gradient for the following forward calls."""
@@ -326,8 +337,9 @@ def _make_function():
 
     class PcxLossFunction(torch.autograd.Function):
         @staticmethod
-        def forward(fctx, X, W, b, tgt_off, tgt, frame_counts, blank, chunk):
+        def forward(fctx, X, W, b, tgt_off, tgt, frame_counts, blank, chunk, beam):
             lease = _Lease(X.device.index)
+            lease.ctx.set_beam(beam)
             loss, _ = lease.ctx.forward(X, W, b, tgt_off, tgt, frame_counts, blank, chunk)
             fctx.lease = lease
             fctx.shapes = (X, W, b)
@@ -341,7 +353,7 @@ def _make_function():
             dW = torch.empty_like(W) if need[1] else None
             db = torch.empty_like(b) if (b is not None and need[2]) else None
             fctx.lease.ctx.backward(float(grad.item()), dX, dW, db)
-            return dX, dW, db, None, None, None, None, None
+            return dX, dW, db, None, None, None, None, None, None
 
     return PcxLossFunction
 
@@ -350,13 +362,14 @@ _FN = None
 
 
 def pruned_ctc_loss(X, weight, bias, targets, frame_counts, blank_id: int = 0,
-                    chunk_size: int = 4096):
+                    chunk_size: int = 4096, output_beam: float = float("inf")):
     """Summed CTC loss of the affine head (X weight^T + bias) over ragged targets.
 
     X: (M, D) stacked head inputs (fp32 or bf16) on the GPU; weight (V, D); bias
     (V,) or None; targets: list of label lists or an (offsets, labels) pair of
-    int32 device tensors; frame_counts: (N,) frame counts.  Returns a float32
-    scalar; gradients flow to X, weight and bias in their own dtypes.
+    int32 device tensors; frame_counts: (N,) frame counts; output_beam: the
+    alignment beam (inf: exact; finite: the pruned objective).  Returns a
+    float32 scalar; gradients flow to X, weight and bias in their own dtypes.
     """
     global _FN
     torch = _torch()
@@ -371,4 +384,4 @@ def pruned_ctc_loss(X, weight, bias, targets, frame_counts, blank_id: int = 0,
     fc = frame_counts.to(device=X.device, dtype=torch.int32).contiguous()
     return _FN.apply(X.contiguous(), weight.contiguous(),
                      None if bias is None else bias.contiguous(), tgt_off, tgt, fc,
-                     int(blank_id), int(chunk_size))
+                     int(blank_id), int(chunk_size), float(output_beam))

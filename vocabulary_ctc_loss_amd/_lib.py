@@ -43,6 +43,8 @@ SIGNATURES = {
     "pcx_backward": (_I32, [_P, _D, _P, _P, _P, _P]),
     "pcx_blank_offset_grad": (_I32, [_P, _D, ctypes.POINTER(_D), _P]),
     "pcx_set_formulation": (_I32, [_P, _I32]),
+    "pcx_set_beam": (_I32, [_P, _D]),
+    "pcx_get_discarded_mass": (_I32, [_P, _P, _I64]),
     "pcx_last_error": (ctypes.c_char_p, []),
     "pcx_get_selected": (_I32, [_P, _P, _I64]),
     "pcx_get_relabeled": (_I32, [_P, _P, _I64]),

@@ -3,6 +3,7 @@
 // event timing, and the inspection getters.  Declarations: include/pcx.h.
 #include <hip/hip_runtime.h>
 #include <limits.h>
+#include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -47,12 +48,14 @@ struct DevBuf {
 // Kernel families timed by the optional event profiler.
 enum Kid {
   K_PREPARE, K_FWD_LSE, K_LAMBDA, K_SCORES, K_ALPHA_BETA, K_LOSS, K_FILL, K_OCC,
-  K_RECOMPUTE, K_DX, K_DW, K_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_ROWSCALE, K_COUNT
+  K_RECOMPUTE, K_DX, K_DW, K_REDUCE, K_CAST, K_BLANK, K_WIDEN, K_ROWSCALE, K_VITERBI,
+  K_BEAM_MASK, K_COUNT
 };
 const char* kKidNames[K_COUNT] = {
     "prepare_select", "fwd_gemm_lse", "lambda", "scores", "ctc_alpha_beta", "loss_sum",
     "fill", "occupancy", "bwd_recompute_dz", "dx_gemm", "dw_gemm",
-    "grad_reduce", "cast", "blank_offset_grad", "widen_head", "grouped_rowscale"};
+    "grad_reduce", "cast", "blank_offset_grad", "widen_head", "grouped_rowscale",
+    "ctc_viterbi", "beam_mask"};
 
 struct Pending {
   int kid;
@@ -66,6 +69,7 @@ struct pcx_ctx {
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
   DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32, other, gu, ou;
+  DevBuf arcmask, ubest, loss_full, logp_full, status_full;  // finite beam
   Meta* host_meta = nullptr;  // pinned
   // caller's allocator (both NULL: hipMalloc / hipFree)
   pcx_alloc_fn alloc = nullptr;
@@ -83,6 +87,8 @@ struct pcx_ctx {
   int dtype = 0;
   int form = PCX_FORM_DIRECT;      // for the next forward
   int fwd_form = PCX_FORM_DIRECT;  // of the last forward
+  double beam = INFINITY;          // alignment beam of the next forward
+  double fwd_beam = INFINITY;      // of the last forward
   int M = 0, D = 0, V = 0, N = 0, blank = 0, chunk = 1, K = 0, max_L = 0, max_T = 0;
   long long L_tot = 0, dp_total = 0;
   int nspan = 0;
@@ -126,7 +132,8 @@ size_t total_bytes(const pcx_ctx* c) {
                           &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha,
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
                           &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta,
-                          &c->w32, &c->b32, &c->other, &c->gu, &c->ou};
+                          &c->w32, &c->b32, &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest,
+                          &c->loss_full, &c->logp_full, &c->status_full};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -277,7 +284,8 @@ void pcx_destroy(pcx_ctx* c) {
                     &c->tgt_rel, &c->tgt_off, &c->part, &c->lam, &c->lamf, &c->S, &c->alpha, &c->beta,
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
                     &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta, &c->w32, &c->b32,
-                    &c->other, &c->gu, &c->ou};
+                    &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest, &c->loss_full,
+                    &c->logp_full, &c->status_full};
   if (c->release) {
     // every call of the context is ordered before the last call's stream
     // tail: once that has finished, nothing of ours touches the workspace
@@ -429,6 +437,28 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                                              (double*)ctx->lam.p, (float*)ctx->lamf.p));
     LAUNCH(K_SCORES, launch_scores(st, (float*)ctx->S.p, (const double*)ctx->lam.p, K, iM));
   }
+  // A finite alignment beam: best prefix / suffix scores (max-plus, into
+  // the alpha / beta buffers), then the kept-arc masks; the recursions
+  // below then run over the kept arcs only.
+  const bool pruned = !isinf(ctx->beam);
+  if (pruned) {
+    ENSURE(arcmask, (size_t)hm.dp_total);
+    ENSURE(ubest, (size_t)(N + 1) * sizeof(double));
+    LAUNCH(K_VITERBI,
+           launch_alpha_beta(st, (const float*)ctx->S.p, iM, N, hm.max_L,
+                             (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                             (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
+                             (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
+                             (double*)ctx->beta.p, nullptr, nullptr, nullptr, 2, nullptr,
+                             (double*)ctx->ubest.p, 0));
+    LAUNCH(K_BEAM_MASK,
+           launch_beam_mask(st, (const float*)ctx->S.p, iM, N, hm.dp_total,
+                            (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                            (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
+                            (const long long*)ctx->dp_off.p, (const double*)ctx->alpha.p,
+                            (const double*)ctx->beta.p, (const double*)ctx->ubest.p,
+                            ctx->beam, (uint8_t*)ctx->arcmask.p));
+  }
   // The backward recursion runs here too, beside the forward one (it only
   // reads S): on the otherwise idle compute units it costs no extra time.
   LAUNCH(K_ALPHA_BETA,
@@ -437,7 +467,9 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                            (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
                            (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
                            (double*)ctx->beta.p, (double*)ctx->utt_loss.p,
-                           (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p));
+                           (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p,
+                           pruned ? 1 : 0, pruned ? (const uint8_t*)ctx->arcmask.p : nullptr,
+                           nullptr, 0));
   LAUNCH(K_LOSS, launch_loss_sum(st, N, (const double*)ctx->utt_loss.p,
                                  (const int*)ctx->utt_status.p, dmeta));
   PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
@@ -449,6 +481,7 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ctx->b = b;
   ctx->dtype = dtype;
   ctx->fwd_form = grouped ? PCX_FORM_GROUPED : PCX_FORM_DIRECT;
+  ctx->fwd_beam = ctx->beam;
   ctx->M = iM;
   ctx->D = iD;
   ctx->V = iV;
@@ -647,6 +680,53 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (dX && cdt != PCX_F32)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;
+  return PCX_OK;
+}
+
+pcx_status pcx_set_beam(pcx_ctx* ctx, double beam) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (!(beam >= 0.0)) return fail(PCX_ERR_ARG, "the alignment beam must be >= 0 (or +inf)");
+  ctx->beam = beam;
+  return PCX_OK;
+}
+
+pcx_status pcx_get_discarded_mass(pcx_ctx* ctx, double* out, int64_t capacity) {
+  g_last_error.clear();
+  if (!ctx) return fail(PCX_ERR_ARG, "ctx is NULL");
+  if (!ctx->fwd_ok) return fail(PCX_ERR_STATE, "no completed forward pass");
+  const int N = ctx->N;
+  if (!out || capacity < N)
+    return fail(PCX_ERR_ARG, "output buffer too small (%lld < %d)", (long long)capacity, N);
+  if (N == 0) return PCX_OK;
+  hipStream_t st = ctx->stream;
+  std::vector<double> lb(N), lf(N, 0.0);
+  std::vector<int> sb(N), sf(N, UTT_OK);
+  if (!isinf(ctx->fwd_beam)) {
+    // the unpruned losses of the same scores: the forward recursion alone,
+    // nothing stored but the losses
+    ENSURE(loss_full, (size_t)(N + 1) * sizeof(double));
+    ENSURE(logp_full, (size_t)(N + 1) * sizeof(double));
+    ENSURE(status_full, (size_t)(N + 1) * sizeof(int));
+    LAUNCH(K_ALPHA_BETA,
+           launch_alpha_beta(st, (const float*)ctx->S.p, ctx->M, N, ctx->max_L,
+                             (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
+                             (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
+                             (const long long*)ctx->dp_off.p, nullptr, nullptr,
+                             (double*)ctx->loss_full.p, (double*)ctx->logp_full.p,
+                             (int*)ctx->status_full.p, 0, nullptr, nullptr, 1));
+  }
+  PCX_HIP(hipStreamSynchronize(st));
+  PCX_HIP(hipMemcpy(lb.data(), ctx->utt_loss.p, N * sizeof(double), hipMemcpyDeviceToHost));
+  PCX_HIP(hipMemcpy(sb.data(), ctx->utt_status.p, N * sizeof(int), hipMemcpyDeviceToHost));
+  if (!isinf(ctx->fwd_beam)) {
+    PCX_HIP(hipMemcpy(lf.data(), ctx->loss_full.p, N * sizeof(double), hipMemcpyDeviceToHost));
+    PCX_HIP(hipMemcpy(sf.data(), ctx->status_full.p, N * sizeof(int), hipMemcpyDeviceToHost));
+  } else {
+    lf = lb;
+  }
+  for (int n = 0; n < N; ++n)
+    out[n] = (sb[n] == UTT_OK && sf[n] == UTT_OK) ? -expm1(-(lb[n] - lf[n])) : NAN;
   return PCX_OK;
 }
 

@@ -203,10 +203,23 @@ hipError_t launch_widen(hipStream_t st, const void* src, float* dst, long long n
 
 // Alignment DP (pcx_ctc.hip).
 // Forward and backward recursions of every utterance in one launch.
+// mode: 0 log-sum over every transition; 1 log-sum over the arcs kept by a
+// finite beam (mask: one byte per lattice node, from launch_beam_mask);
+// 2 max-plus (alpha <- best prefix scores, beta <- best suffix scores
+// without the node's emission, best[n] <- best alignment score).
+// fwd_only: the forward recursion alone (alpha may then be NULL: losses
+// only).
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
                              const uint8_t* flags, const long long* dp_off, double* alpha,
-                             double* beta, double* utt_loss, double* utt_logp, int* utt_status);
+                             double* beta, double* utt_loss, double* utt_logp, int* utt_status,
+                             int mode = 0, const uint8_t* mask = nullptr,
+                             double* best = nullptr, int fwd_only = 0);
+// Arc masks of a finite alignment beam from the max-plus scores.
+hipError_t launch_beam_mask(hipStream_t st, const float* S, int M, int N, long long dp_total,
+                            const int* row_off, const int* tgt_off, const int* tgt_rel,
+                            const uint8_t* flags, const long long* dp_off, const double* vf,
+                            const double* vb, const double* best, double beam, uint8_t* mask);
 hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss,
                            const int* utt_status, Meta* meta);
 hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int max_T,

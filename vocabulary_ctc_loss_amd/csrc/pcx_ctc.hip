@@ -98,29 +98,56 @@ __device__ __forceinline__ double lse2(double a, double b) {
   return m + log_1to4(1.0 + exp_nonpos_lat(x - m));
 }
 
+// What a recursion computes over the lattice of an utterance:
+//   DP_SUM     log-sum of the forward (backward) scores over every CTC
+//              transition: the unpruned alpha (beta) of the loss;
+//   DP_PRUNED  the same over the arcs a finite alignment beam keeps (bit
+//              masks from k_beam_mask, one byte per lattice node);
+//   DP_MAX     best prefix scores vf (emission included) and best suffix
+//              scores vb (emission of the node excluded) in FP64 max-plus,
+//              and the best complete alignment's score per utterance.
+enum : int { DP_SUM = 0, DP_PRUNED = 1, DP_MAX = 2 };
+
+// Arc bits of a lattice node (t, s): bits 0-2 the arcs into it from s
+// (stay), s - 1 (advance) and s - 2 (skip); bits 3-5 the arcs out of it to
+// s, s + 1 and s + 2.  At t = 0 bit 0 is the initial arc, at t = T - 1 bit 3
+// the final arc.
+constexpr int ARC_IN_STAY = 1, ARC_IN_ADV = 2, ARC_IN_SKIP = 4;
+constexpr int ARC_OUT_STAY = 8, ARC_OUT_ADV = 16, ARC_OUT_SKIP = 32;
+
+__device__ __forceinline__ double max3(double a, double b, double c) {
+  return fmax(a, fmax(b, c));
+}
+
 // Forward recursion of utterance n; alpha[t][s] (including the emission at
-// t) is stored for the backward pass.
-template <int SPT>
+// t) is stored for the backward pass (not when alpha is NULL: the loss
+// alone).  DP_MAX stores vf in alpha and the best complete score in best[n].
+template <int SPT, int MODE>
 __device__ __forceinline__ void alpha_utt(
     int n, double* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
-    double* __restrict__ alpha, double* __restrict__ utt_loss, double* __restrict__ utt_logp,
-    int* __restrict__ utt_status) {
+    const uint8_t* __restrict__ mask, double* __restrict__ alpha, double* __restrict__ utt_loss,
+    double* __restrict__ utt_logp, int* __restrict__ utt_status, double* __restrict__ best) {
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   if (!flags[n]) {
     if (threadIdx.x == 0) {
-      utt_loss[n] = 0.0;
-      utt_logp[n] = -INFINITY;
-      utt_status[n] = UTT_UNALIGNABLE;
+      if (MODE == DP_MAX) {
+        best[n] = -INFINITY;
+      } else {
+        utt_loss[n] = 0.0;
+        utt_logp[n] = -INFINITY;
+        utt_status[n] = UTT_UNALIGNABLE;
+      }
     }
     return;
   }
   const int cap = SPT * blockDim.x;
   double* buf0 = sh;
   double* buf1 = sh + cap;
-  double* out = alpha + dp_off[n];
+  double* out = alpha != nullptr ? alpha + dp_off[n] : nullptr;
+  const uint8_t* mk = MODE == DP_PRUNED ? mask + dp_off[n] : nullptr;
   int sidx[SPT];
   long long ebase[SPT];
   bool skip[SPT];
@@ -138,18 +165,25 @@ __device__ __forceinline__ void alpha_utt(
     ebase[j] = (long long)cls * M + row0;
   }
   float ecur[SPT][PF], enxt[SPT][PF];
+  int mcur[SPT][PF], mnxt[SPT][PF];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) ecur[j][u] = (sidx[j] < Sn && u < T) ? S[ebase[j] + u] : 0.f;
-  // frame 0: only the first blank and the first label can start.
+    for (int u = 0; u < PF; ++u) {
+      const bool in = sidx[j] < Sn && u < T;
+      ecur[j][u] = in ? S[ebase[j] + u] : 0.f;
+      mcur[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)u * Sn + sidx[j]] : 0;
+    }
+  // frame 0: only the first blank and the first label can start (pruned:
+  // if their initial arcs are kept).
 #pragma unroll
   for (int j = 0; j < SPT; ++j) {
     const int s = sidx[j];
     if (s < Sn) {
-      const double a = (s <= 1) ? (double)ecur[j][0] : -INFINITY;
+      const bool start = s <= 1 && (MODE != DP_PRUNED || (mcur[j][0] & ARC_IN_STAY));
+      const double a = start ? (double)ecur[j][0] : -INFINITY;
       buf0[s] = a;
-      out[s] = a;
+      if (out) out[s] = a;
     }
   }
   lds_barrier();
@@ -160,7 +194,9 @@ __device__ __forceinline__ void alpha_utt(
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           const int t = tb + PF + u;
-          enxt[j][u] = (sidx[j] < Sn && t < T) ? S[ebase[j] + t] : 0.f;
+          const bool in = sidx[j] < Sn && t < T;
+          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
+          mnxt[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
         }
     }
 #pragma unroll
@@ -174,12 +210,19 @@ __device__ __forceinline__ void alpha_utt(
       for (int j = 0; j < SPT; ++j) {
         const int s = sidx[j];
         if (s < Sn) {
-          const double a0 = prev[s];
-          const double a1 = s >= 1 ? prev[s - 1] : -INFINITY;
-          const double a2 = skip[j] ? prev[s - 2] : -INFINITY;
-          const double v = lse3(a0, a1, a2) + (double)ecur[j][u];
+          double a0 = prev[s];
+          double a1 = s >= 1 ? prev[s - 1] : -INFINITY;
+          double a2 = skip[j] ? prev[s - 2] : -INFINITY;
+          if (MODE == DP_PRUNED) {
+            const int m = mcur[j][u];
+            a0 = (m & ARC_IN_STAY) ? a0 : -INFINITY;
+            a1 = (m & ARC_IN_ADV) ? a1 : -INFINITY;
+            a2 = (m & ARC_IN_SKIP) ? a2 : -INFINITY;
+          }
+          const double v =
+              (MODE == DP_MAX ? max3(a0, a1, a2) : lse3(a0, a1, a2)) + (double)ecur[j][u];
           cur[s] = v;
-          out[(long long)t * Sn + s] = v;
+          if (out) out[(long long)t * Sn + s] = v;
         }
       }
       lds_barrier();
@@ -187,11 +230,24 @@ __device__ __forceinline__ void alpha_utt(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) ecur[j][u] = enxt[j][u];
+      for (int u = 0; u < PF; ++u) {
+        ecur[j][u] = enxt[j][u];
+        mcur[j][u] = mnxt[j][u];
+      }
   }
   if (threadIdx.x == 0) {
     const double* last = ((T - 1) & 1) ? buf1 : buf0;
-    const double logP = Sn > 1 ? lse2(last[Sn - 1], last[Sn - 2]) : last[0];
+    double e1 = last[Sn - 1], e2 = Sn > 1 ? last[Sn - 2] : -INFINITY;
+    if (MODE == DP_MAX) {
+      best[n] = fmax(e1, e2);
+      return;
+    }
+    if (MODE == DP_PRUNED) {  // final arcs
+      const uint8_t* lm = mk + (long long)(T - 1) * Sn;
+      if (!(lm[Sn - 1] & ARC_OUT_STAY)) e1 = -INFINITY;
+      if (Sn > 1 && !(lm[Sn - 2] & ARC_OUT_STAY)) e2 = -INFINITY;
+    }
+    const double logP = Sn > 1 ? lse2(e1, e2) : e1;
     utt_logp[n] = logP;
     if (isfinite(logP)) {
       utt_loss[n] = -logP;
@@ -206,12 +262,14 @@ __device__ __forceinline__ void alpha_utt(
 // Backward recursion of utterance n; beta[t][s] includes the emission at
 // t.  Run for every structurally alignable utterance (an utterance whose
 // loss turns out nonfinite gets no gradient: the occupancy pass skips it).
-template <int SPT>
+// DP_MAX stores vb, the best suffix score after the node (its own emission
+// excluded), while the recursion carries vb + emission.
+template <int SPT, int MODE>
 __device__ __forceinline__ void beta_utt(
     int n, double* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
-    double* __restrict__ beta) {
+    const uint8_t* __restrict__ mask, double* __restrict__ beta) {
   if (!flags[n]) return;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
@@ -219,6 +277,7 @@ __device__ __forceinline__ void beta_utt(
   double* buf0 = sh;
   double* buf1 = sh + cap;
   double* out = beta + dp_off[n];
+  const uint8_t* mk = MODE == DP_PRUNED ? mask + dp_off[n] : nullptr;
   int sidx[SPT];
   long long ebase[SPT];
   bool skip[SPT];
@@ -237,12 +296,15 @@ __device__ __forceinline__ void beta_utt(
   }
   // Frames are visited downwards; block b covers frames T-1-b*PF-u, u < PF.
   float ecur[SPT][PF], enxt[SPT][PF];
+  int mcur[SPT][PF], mnxt[SPT][PF];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int t = T - 1 - u;
-      ecur[j][u] = (sidx[j] < Sn && t >= 0) ? S[ebase[j] + t] : 0.f;
+      const bool in = sidx[j] < Sn && t >= 0;
+      ecur[j][u] = in ? S[ebase[j] + t] : 0.f;
+      mcur[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
     }
   const int tl = T - 1;
   double* lastbuf = (tl & 1) ? buf1 : buf0;
@@ -250,9 +312,10 @@ __device__ __forceinline__ void beta_utt(
   for (int j = 0; j < SPT; ++j) {
     const int s = sidx[j];
     if (s < Sn) {
-      const double b = (s >= Sn - 2) ? (double)ecur[j][0] : -INFINITY;
+      const bool fin = s >= Sn - 2 && (MODE != DP_PRUNED || (mcur[j][0] & ARC_OUT_STAY));
+      const double b = fin ? (double)ecur[j][0] : -INFINITY;  // DP_MAX: 0 + emission
       lastbuf[s] = b;
-      out[(long long)tl * Sn + s] = b;
+      out[(long long)tl * Sn + s] = MODE == DP_MAX ? (fin ? 0.0 : -INFINITY) : b;
     }
   }
   lds_barrier();
@@ -263,7 +326,9 @@ __device__ __forceinline__ void beta_utt(
 #pragma unroll
         for (int u = 0; u < PF; ++u) {
           const int t = T - 1 - (tb + PF + u);
-          enxt[j][u] = (sidx[j] < Sn && t >= 0) ? S[ebase[j] + t] : 0.f;
+          const bool in = sidx[j] < Sn && t >= 0;
+          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
+          mnxt[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
         }
     }
 #pragma unroll
@@ -277,12 +342,24 @@ __device__ __forceinline__ void beta_utt(
       for (int j = 0; j < SPT; ++j) {
         const int s = sidx[j];
         if (s < Sn) {
-          const double b0 = nxt[s];
-          const double b1 = s + 1 < Sn ? nxt[s + 1] : -INFINITY;
-          const double b2 = skip[j] ? nxt[s + 2] : -INFINITY;
-          const double v = lse3(b0, b1, b2) + (double)ecur[j][u];
-          cur[s] = v;
-          out[(long long)t * Sn + s] = v;
+          double b0 = nxt[s];
+          double b1 = s + 1 < Sn ? nxt[s + 1] : -INFINITY;
+          double b2 = skip[j] ? nxt[s + 2] : -INFINITY;
+          if (MODE == DP_PRUNED) {
+            const int m = mcur[j][u];
+            b0 = (m & ARC_OUT_STAY) ? b0 : -INFINITY;
+            b1 = (m & ARC_OUT_ADV) ? b1 : -INFINITY;
+            b2 = (m & ARC_OUT_SKIP) ? b2 : -INFINITY;
+          }
+          if (MODE == DP_MAX) {
+            const double m = max3(b0, b1, b2);
+            cur[s] = m + (double)ecur[j][u];
+            out[(long long)t * Sn + s] = m;
+          } else {
+            const double v = lse3(b0, b1, b2) + (double)ecur[j][u];
+            cur[s] = v;
+            out[(long long)t * Sn + s] = v;
+          }
         }
       }
       lds_barrier();
@@ -290,28 +367,97 @@ __device__ __forceinline__ void beta_utt(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) ecur[j][u] = enxt[j][u];
+      for (int u = 0; u < PF; ++u) {
+        ecur[j][u] = enxt[j][u];
+        mcur[j][u] = mnxt[j][u];
+      }
   }
 }
 
 // Both recursions in one launch: work-groups 0..N-1 run the forward
-// recursion of utterance n, work-groups N..2N-1 the backward recursion of
-// utterance n - N.  The two only read S, so they run side by side (the loss
-// pass needs the forward ones only; the backward pass reads both).
-template <int SPT>
+// recursion of utterance n, work-groups N..2N-1 (when launched) the backward
+// recursion of utterance n - N.  The two only read S (and the arc masks), so
+// they run side by side (the loss pass needs the forward ones only; the
+// backward pass reads both).
+template <int SPT, int MODE>
 __global__ __launch_bounds__(1024) void k_alpha_beta(
     const float* __restrict__ S, int M, int N, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
-    double* __restrict__ alpha, double* __restrict__ beta, double* __restrict__ utt_loss,
-    double* __restrict__ utt_logp, int* __restrict__ utt_status) {
+    const uint8_t* __restrict__ mask, double* __restrict__ alpha, double* __restrict__ beta,
+    double* __restrict__ utt_loss, double* __restrict__ utt_logp, int* __restrict__ utt_status,
+    double* __restrict__ best) {
   extern __shared__ double sh[];
   const int b = blockIdx.x;
   if (b < N)
-    alpha_utt<SPT>(b, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, alpha, utt_loss,
-                   utt_logp, utt_status);
+    alpha_utt<SPT, MODE>(b, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask, alpha,
+                         utt_loss, utt_logp, utt_status, best);
   else
-    beta_utt<SPT>(b - N, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, beta);
+    beta_utt<SPT, MODE>(b - N, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask, beta);
+}
+
+// Arc masks of a finite alignment beam.  An arc is kept when the best
+// complete alignment through it scores at least B_n - beam, B_n the best
+// alignment of utterance n ("Pruned CTC for Memory-Efficient Large-
+// Vocabulary ASR Training", App. B.1 finite-beam computation; pruning
+// relative to the best path, as a log-score output beam).  The score of the
+// arc (t-1, s') -> (t, s) is (vf[t-1][s'] + e_t(s)) + vb[t][s] in FP64, in
+// that association; the initial arc into (0, s) scores vf[0][s] + vb[0][s]
+// and the final arc out of (T-1, s) scores vf[T-1][s].  Every node writes
+// the bits of its incoming and of its outgoing arcs (the same decisions,
+// read by the forward and by the backward recursion).  Work-group (n, k):
+// nodes k, k + blockDim.x * gridDim.y, ... of utterance n.
+__global__ __launch_bounds__(256) void k_beam_mask(
+    const float* __restrict__ S, int M, const int* __restrict__ row_off,
+    const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
+    const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
+    const double* __restrict__ vf, const double* __restrict__ vb,
+    const double* __restrict__ best, double beam, uint8_t* __restrict__ mask) {
+  const int n = blockIdx.x;
+  if (!flags[n]) return;
+  const int row0 = row_off[n], T = row_off[n + 1] - row0;
+  const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
+  const long long base = dp_off[n];
+  const double thr = best[n] - beam;
+  const long long nodes = (long long)T * Sn;
+  for (long long i = blockIdx.y * (long long)blockDim.x + threadIdx.x; i < nodes;
+       i += (long long)gridDim.y * blockDim.x) {
+    const int t = (int)(i / Sn), s = (int)(i - (long long)t * Sn);
+    const int cls = (s & 1) ? tgt_rel[y0 + (s >> 1)] : 0;
+    const double* f = vf + base;
+    const double* g = vb + base;
+    int bits = 0;
+    if (t == 0) {
+      if (s <= 1 && f[s] + g[s] >= thr) bits |= ARC_IN_STAY;  // initial arc
+    } else {
+      const double e = (double)S[(long long)cls * M + row0 + t];
+      const double* fp = f + (long long)(t - 1) * Sn;
+      const double gs = g[(long long)t * Sn + s];
+      if ((fp[s] + e) + gs >= thr) bits |= ARC_IN_STAY;
+      if (s >= 1 && (fp[s - 1] + e) + gs >= thr) bits |= ARC_IN_ADV;
+      if ((s & 1) && s >= 3 && cls != tgt_rel[y0 + (s >> 1) - 1] && (fp[s - 2] + e) + gs >= thr)
+        bits |= ARC_IN_SKIP;
+    }
+    const double fs = f[(long long)t * Sn + s];
+    if (t == T - 1) {
+      if (s >= Sn - 2 && fs >= thr) bits |= ARC_OUT_STAY;  // final arc
+    } else {
+      const double* gn = g + (long long)(t + 1) * Sn;
+      const long long r1 = row0 + t + 1;
+      const double e0 = (double)S[(long long)cls * M + r1];
+      if ((fs + e0) + gn[s] >= thr) bits |= ARC_OUT_STAY;
+      if (s + 1 < Sn) {
+        const int c1 = ((s + 1) & 1) ? tgt_rel[y0 + ((s + 1) >> 1)] : 0;
+        if ((fs + (double)S[(long long)c1 * M + r1]) + gn[s + 1] >= thr) bits |= ARC_OUT_ADV;
+      }
+      if ((s & 1) && s + 2 < Sn) {
+        const int c2 = tgt_rel[y0 + ((s + 2) >> 1)];
+        if (c2 != cls && (fs + (double)S[(long long)c2 * M + r1]) + gn[s + 2] >= thr)
+          bits |= ARC_OUT_SKIP;
+      }
+    }
+    mask[base + i] = (uint8_t)bits;
+  }
 }
 
 // Occupancies on the selected classes for OCC_FRAMES frames of one
@@ -499,30 +645,48 @@ void dp_shape(int max_L, int& threads, int& spt) {
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
                              const uint8_t* flags, const long long* dp_off, double* alpha,
-                             double* beta, double* utt_loss, double* utt_logp, int* utt_status) {
+                             double* beta, double* utt_loss, double* utt_logp, int* utt_status,
+                             int mode, const uint8_t* mask, double* best, int fwd_only) {
   if (N == 0) return hipSuccess;
   int threads, spt;
   dp_shape(max_L, threads, spt);
   const size_t shm = 2 * (size_t)spt * threads * sizeof(double);
+  const int grid = fwd_only ? N : 2 * N;
+#define PCX_AB(SPT_, MODE_)                                                                  \
+  k_alpha_beta<SPT_, MODE_><<<grid, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel,  \
+                                                        flags, dp_off, mask, alpha, beta,    \
+                                                        utt_loss, utt_logp, utt_status, best)
+#define PCX_AB_MODE(SPT_)                              \
+  switch (mode) {                                      \
+    case DP_SUM: PCX_AB(SPT_, DP_SUM); break;          \
+    case DP_PRUNED: PCX_AB(SPT_, DP_PRUNED); break;    \
+    case DP_MAX: PCX_AB(SPT_, DP_MAX); break;          \
+    default: return hipErrorInvalidValue;              \
+  }
   switch (spt) {
-    case 1:
-      k_alpha_beta<1><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
-                                                   dp_off, alpha, beta, utt_loss, utt_logp,
-                                                   utt_status);
-      break;
-    case 2:
-      k_alpha_beta<2><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
-                                                   dp_off, alpha, beta, utt_loss, utt_logp,
-                                                   utt_status);
-      break;
-    case 4:
-      k_alpha_beta<4><<<2 * N, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel, flags,
-                                                   dp_off, alpha, beta, utt_loss, utt_logp,
-                                                   utt_status);
-      break;
+    case 1: PCX_AB_MODE(1); break;
+    case 2: PCX_AB_MODE(2); break;
+    case 4: PCX_AB_MODE(4); break;
     default:
       return hipErrorInvalidValue;
   }
+#undef PCX_AB_MODE
+#undef PCX_AB
+  return hipGetLastError();
+}
+
+hipError_t launch_beam_mask(hipStream_t st, const float* S, int M, int N, long long dp_total,
+                            const int* row_off, const int* tgt_off, const int* tgt_rel,
+                            const uint8_t* flags, const long long* dp_off, const double* vf,
+                            const double* vb, const double* best, double beam, uint8_t* mask) {
+  if (N == 0 || dp_total == 0) return hipSuccess;
+  // about four nodes per thread on average, at least one work-group per
+  // utterance, at most 64
+  long long per = (dp_total / N + 1023) / 1024;
+  if (per < 1) per = 1;
+  if (per > 64) per = 64;
+  k_beam_mask<<<dim3(N, (unsigned)per), 256, 0, st>>>(S, M, row_off, tgt_off, tgt_rel, flags,
+                                                       dp_off, vf, vb, best, beam, mask);
   return hipGetLastError();
 }
 
