@@ -834,10 +834,25 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
   }
   lds_barrier();
+  // A tile whose columns are all selected needs no recomputed logit (their
+  // dZ comes from S, Gamma and g alone, the pages' reuse of S): its product
+  // is skipped.  (Small vocabularies, where K is close to V, and the densely
+  // selected low ids of Zipf-distributed labels.)
+  bool any_unsel = false;
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) any_unsel |= n0 + c < c1 && s_sel[c] < 0;
+  const bool need_product = __syncthreads_or(any_unsel) != 0;
   SelPre<C> pre;
   sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam, ldS);
   f32x16 acc[C::FM][C::FN];
-  gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc, smem);
+  if (need_product) {
+    gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc,
+                                 smem);
+  } else {
+#pragma unroll
+    for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj) acc[fi][fj] = f32x16{};
+  }
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
   const bool rows_full = m0 + BM <= M;
   // Many selected columns in some wavefront: the whole work-group takes the
