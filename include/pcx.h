@@ -225,6 +225,33 @@ pcx_status pcx_blank_offset_grad(pcx_ctx* ctx, double grad_loss, double* d_eta,
                                  void* stream);
 
 /*
+ * pcx_forward followed by pcx_backward in one call that allocates nothing,
+ * for callers that cannot allocate device memory (code being captured into
+ * a graph, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device array of PCX_STATIC_SCRATCH_BYTES bytes, one
+ * copy per GPU the library runs on, held until the process ends; no context
+ * is involved and no hipMalloc, hipFree or allocation callback is called.
+ *   Arguments as pcx_forward (X ... chunk, stream, loss, info) and
+ *   pcx_backward (grad_loss, dX, dW, db), with the same layouts, dtypes,
+ *   ownership and results: the same kernels run with the same launch shapes.
+ *   info->workspace_bytes reports the part of the scratch the call used.
+ * A call whose workspace would exceed the scratch fails with
+ * PCX_ERR_WORKSPACE without writing dX, dW or db (the loss and info of its
+ * forward part may have been written).  The call synchronises the
+ * stream twice, as pcx_forward does.  Every call on one GPU uses that GPU's
+ * one scratch array: calls that overlap on a GPU (from two host threads, or
+ * on two streams without ordering between them) race and give wrong
+ * results; calls in order on one stream do not.
+ */
+#define PCX_STATIC_SCRATCH_BYTES (64u << 20)
+pcx_status pcx_loss_grad_static(const void* X, const void* W, const void* b, int32_t dtype,
+                                int64_t M, int64_t D, int64_t V, int32_t N,
+                                const int32_t* tgt_off, const int32_t* tgt, int64_t L_tot,
+                                const int32_t* frame_counts, int32_t blank, int32_t chunk,
+                                double grad_loss, void* dX, void* dW, void* db, void* stream,
+                                double* loss, pcx_fwd_info* info);
+
+/*
  * Alignment beam of the following pcx_forward calls of this context (the
  * PrunedCTC README's output_beam; "Pruned CTC for Memory-Efficient
  * Large-Vocabulary ASR Training", App. B.1 finite-beam computation and the

@@ -44,6 +44,8 @@ SIGNATURES = {
     "pcx_blank_offset_grad": (_I32, [_P, _D, ctypes.POINTER(_D), _P]),
     "pcx_set_formulation": (_I32, [_P, _I32]),
     "pcx_set_beam": (_I32, [_P, _D]),
+    "pcx_loss_grad_static": (_I32, [_P, _P, _P, _I32, _I64, _I64, _I64, _I32, _P, _P, _I64, _P,
+                                    _I32, _I32, _D, _P, _P, _P, _P, ctypes.POINTER(_D), _P]),
     "pcx_get_discarded_mass": (_I32, [_P, _P, _I64]),
     "pcx_last_error": (ctypes.c_char_p, []),
     "pcx_get_selected": (_I32, [_P, _P, _I64]),

@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -75,6 +76,11 @@ struct pcx_ctx {
   pcx_alloc_fn alloc = nullptr;
   pcx_free_fn release = nullptr;
   void* user = nullptr;
+  // fixed workspace (the static-scratch entry point): buffers are carved in
+  // order from [fixed_base, fixed_base + fixed_cap) and never released
+  bool fixed = false;
+  char* fixed_base = nullptr;
+  size_t fixed_cap = 0, fixed_used = 0;
   // forward state kept for backward / getters
   bool fwd_ok = false;
   bool bwd_done = false;
@@ -142,6 +148,19 @@ size_t total_bytes(const pcx_ctx* c) {
 pcx_status ensure(pcx_ctx* c, DevBuf& b, size_t bytes, hipStream_t st) {
   if (bytes == 0) bytes = 16;
   if (b.cap >= bytes) return PCX_OK;
+  if (c->fixed) {
+    bytes = (bytes + 255) & ~size_t(255);
+    if (bytes > c->fixed_cap - c->fixed_used)
+      return fail(PCX_ERR_WORKSPACE,
+                  "the call needs more workspace than the %zu-byte static scratch (%zu in use, "
+                  "%zu more asked for); use pcx_forward / pcx_backward",
+                  c->fixed_cap, c->fixed_used, bytes);
+    b.p = c->fixed_base + c->fixed_used;
+    b.cap = bytes;
+    b.st = st;
+    c->fixed_used += bytes;
+    return PCX_OK;
+  }
   {
     // a graph must not record an allocation or a release
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -257,6 +276,18 @@ struct Timed {
     if (s_ != PCX_OK) return s_;                                \
   } while (0)
 
+}  // namespace
+
+// Static scratch of pcx_loss_grad_static: one copy per GPU, held until the
+// process ends.  Host code uses the address hipGetSymbolAddress returns for
+// the current device, never the symbol itself.
+__device__ __align__(256) unsigned char scratch[PCX_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+Meta g_static_meta[kMaxDevices];  // host copy of the device summary, per GPU
 }  // namespace
 
 extern "C" {
@@ -681,6 +712,46 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;
   return PCX_OK;
+}
+
+pcx_status pcx_loss_grad_static(const void* X, const void* W, const void* b, int32_t dtype,
+                                int64_t M, int64_t D, int64_t V, int32_t N,
+                                const int32_t* tgt_off, const int32_t* tgt, int64_t L_tot,
+                                const int32_t* frame_counts, int32_t blank, int32_t chunk,
+                                double grad_loss, void* dX, void* dW, void* db, void* stream,
+                                double* loss, pcx_fwd_info* info) {
+  g_last_error.clear();
+  int dev = 0;
+  PCX_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(PCX_ERR_ARG, "device %d out of range", dev);
+  void* base = nullptr;
+  {
+    // once per device, with that device current: the device address of its
+    // copy of the scratch array
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+      void* p = nullptr;
+      const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || p == nullptr)
+        return fail(PCX_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      g_scratch_ptr[dev] = p;
+    }
+    base = g_scratch_ptr[dev];
+  }
+  // A context on the stack whose workspace is carved from the scratch; its
+  // host summary lives in static host memory.  It owns no allocation, so it
+  // is simply dropped at the end.
+  pcx_ctx c;
+  c.fixed = true;
+  c.fixed_base = (char*)base;
+  c.fixed_cap = PCX_STATIC_SCRATCH_BYTES;
+  c.host_meta = &g_static_meta[dev];
+  pcx_status s = pcx_forward(&c, X, W, b, dtype, M, D, V, N, tgt_off, tgt, L_tot, frame_counts,
+                             blank, chunk, stream, loss, info);
+  if (s == PCX_OK) s = pcx_backward(&c, grad_loss, dX, dW, db, stream);
+  if (s == PCX_OK && info) info->workspace_bytes = c.fixed_used;
+  c.host_meta = nullptr;
+  return s;
 }
 
 pcx_status pcx_set_beam(pcx_ctx* ctx, double beam) {
