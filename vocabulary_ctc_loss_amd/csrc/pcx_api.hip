@@ -71,6 +71,7 @@ struct pcx_ctx {
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
   DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32, other, gu, ou;
   DevBuf arcmask, ubest, loss_full, logp_full, status_full;  // finite beam
+  DevBuf alpha_e, beta_e, utt_pm, utt_pe, pm_full, pe_full;   // scaled-value exponents
   Meta* host_meta = nullptr;  // pinned
   // caller's allocator (both NULL: hipMalloc / hipFree)
   pcx_alloc_fn alloc = nullptr;
@@ -139,7 +140,8 @@ size_t total_bytes(const pcx_ctx* c) {
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
                           &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta,
                           &c->w32, &c->b32, &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest,
-                          &c->loss_full, &c->logp_full, &c->status_full};
+                          &c->loss_full, &c->logp_full, &c->status_full, &c->alpha_e,
+                          &c->beta_e, &c->utt_pm, &c->utt_pe, &c->pm_full, &c->pe_full};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -316,7 +318,8 @@ void pcx_destroy(pcx_ctx* c) {
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
                     &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta, &c->w32, &c->b32,
                     &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest, &c->loss_full,
-                    &c->logp_full, &c->status_full};
+                    &c->logp_full, &c->status_full, &c->alpha_e, &c->beta_e, &c->utt_pm,
+                    &c->utt_pe, &c->pm_full, &c->pe_full};
   if (c->release) {
     // every call of the context is ordered before the last call's stream
     // tail: once that has finished, nothing of ours touches the workspace
@@ -429,6 +432,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(S, (size_t)K * M * sizeof(float));
   ENSURE(alpha, (size_t)hm.dp_total * sizeof(double));
   ENSURE(beta, (size_t)hm.dp_total * sizeof(double));
+  ENSURE(alpha_e, (size_t)hm.dp_total * sizeof(int));
+  ENSURE(beta_e, (size_t)hm.dp_total * sizeof(int));
+  ENSURE(utt_pm, (size_t)(N + 1) * sizeof(double));
+  ENSURE(utt_pe, (size_t)(N + 1) * sizeof(int));
   ENSURE(utt_loss, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_logp, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_status, (size_t)(N + 1) * sizeof(int));
@@ -479,11 +486,11 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
            launch_alpha_beta(st, (const float*)ctx->S.p, iM, N, hm.max_L,
                              (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                              (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
-                             (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
-                             (double*)ctx->beta.p, nullptr, nullptr, nullptr, 2, nullptr,
-                             (double*)ctx->ubest.p, 0));
+                             (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p, nullptr,
+                             (double*)ctx->beta.p, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             nullptr, 2, nullptr, (double*)ctx->ubest.p, 0));
     LAUNCH(K_BEAM_MASK,
-           launch_beam_mask(st, (const float*)ctx->S.p, iM, N, hm.dp_total,
+           launch_beam_mask(st, (const float*)ctx->S.p, iM, N, hm.dp_total, hm.max_T, hm.max_L,
                             (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                             (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
                             (const long long*)ctx->dp_off.p, (const double*)ctx->alpha.p,
@@ -497,10 +504,11 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                            (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                            (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
                            (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
-                           (double*)ctx->beta.p, (double*)ctx->utt_loss.p,
-                           (double*)ctx->utt_logp.p, (int*)ctx->utt_status.p,
-                           pruned ? 1 : 0, pruned ? (const uint8_t*)ctx->arcmask.p : nullptr,
-                           nullptr, 0));
+                           (int*)ctx->alpha_e.p, (double*)ctx->beta.p, (int*)ctx->beta_e.p,
+                           (double*)ctx->utt_loss.p, (double*)ctx->utt_logp.p,
+                           (double*)ctx->utt_pm.p, (int*)ctx->utt_pe.p,
+                           (int*)ctx->utt_status.p, pruned ? 1 : 0,
+                           pruned ? (const uint8_t*)ctx->arcmask.p : nullptr, nullptr, 0));
   LAUNCH(K_LOSS, launch_loss_sum(st, N, (const double*)ctx->utt_loss.p,
                                  (const int*)ctx->utt_status.p, dmeta));
   PCX_HIP(hipMemcpyAsync(ctx->host_meta, dmeta, sizeof(Meta), hipMemcpyDeviceToHost, st));
@@ -540,11 +548,12 @@ static pcx_status run_occupancy(pcx_ctx* ctx, hipStream_t st) {
   ENSURE(Gam, (size_t)K * M * sizeof(float));
   ENSURE(g, (size_t)M * sizeof(double));
   LAUNCH(K_FILL, launch_fill_f32(st, (float*)ctx->Gam.p, (long long)K * M, 0.f));
-  LAUNCH(K_OCC, launch_occupancy(st, (const float*)ctx->S.p, M, N, ctx->max_T, ctx->max_L,
-                                 (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
-                                 (const int*)ctx->tgt_rel.p, (const int*)ctx->utt_status.p,
-                                 (const double*)ctx->utt_logp.p, (const long long*)ctx->dp_off.p,
-                                 (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
+  LAUNCH(K_OCC, launch_occupancy(st, M, N, ctx->max_T, ctx->max_L, (const int*)ctx->row_off.p,
+                                 (const int*)ctx->tgt_off.p, (const int*)ctx->tgt_rel.p,
+                                 (const int*)ctx->utt_status.p, (const double*)ctx->utt_pm.p,
+                                 (const int*)ctx->utt_pe.p, (const long long*)ctx->dp_off.p,
+                                 (const double*)ctx->alpha.p, (const int*)ctx->alpha_e.p,
+                                 (const double*)ctx->beta.p, (const int*)ctx->beta_e.p,
                                  (float*)ctx->Gam.p, (double*)ctx->g.p));
   return PCX_OK;
 }
@@ -779,12 +788,15 @@ pcx_status pcx_get_discarded_mass(pcx_ctx* ctx, double* out, int64_t capacity) {
     ENSURE(loss_full, (size_t)(N + 1) * sizeof(double));
     ENSURE(logp_full, (size_t)(N + 1) * sizeof(double));
     ENSURE(status_full, (size_t)(N + 1) * sizeof(int));
+    ENSURE(pm_full, (size_t)(N + 1) * sizeof(double));
+    ENSURE(pe_full, (size_t)(N + 1) * sizeof(int));
     LAUNCH(K_ALPHA_BETA,
            launch_alpha_beta(st, (const float*)ctx->S.p, ctx->M, N, ctx->max_L,
                              (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                              (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
-                             (const long long*)ctx->dp_off.p, nullptr, nullptr,
+                             (const long long*)ctx->dp_off.p, nullptr, nullptr, nullptr, nullptr,
                              (double*)ctx->loss_full.p, (double*)ctx->logp_full.p,
+                             (double*)ctx->pm_full.p, (int*)ctx->pe_full.p,
                              (int*)ctx->status_full.p, 0, nullptr, nullptr, 1));
   }
   PCX_HIP(hipStreamSynchronize(st));

@@ -203,31 +203,33 @@ hipError_t launch_widen(hipStream_t st, const void* src, float* dst, long long n
 
 // Alignment DP (pcx_ctc.hip).
 // Forward and backward recursions of every utterance in one launch.
-// mode: 0 log-sum over every transition; 1 log-sum over the arcs kept by a
-// finite beam (mask: one byte per lattice node, from launch_beam_mask);
-// 2 max-plus (alpha <- best prefix scores, beta <- best suffix scores
-// without the node's emission, best[n] <- best alignment score).
-// fwd_only: the forward recursion alone (alpha may then be NULL: losses
-// only).
+// mode 0: sums over every transition, as scaled probabilities (am, ae: the
+// forward values, emission included; bm, be: the backward values without
+// the node's emission; utt_pm, utt_pe: the total per utterance);
+// mode 1: the same over the arcs kept by a finite beam (mask: one byte per
+// lattice node, from launch_beam_mask);
+// mode 2: max-plus in the log domain (am <- best prefix scores, bm <- best
+// suffix scores without the node's emission, best[n] <- best alignment
+// score; ae, be, utt_* unused).
+// fwd_only: the forward recursion alone (am may then be NULL: losses only).
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
-                             const uint8_t* flags, const long long* dp_off, double* alpha,
-                             double* beta, double* utt_loss, double* utt_logp, int* utt_status,
-                             int mode = 0, const uint8_t* mask = nullptr,
-                             double* best = nullptr, int fwd_only = 0);
+                             const uint8_t* flags, const long long* dp_off, double* am, int* ae,
+                             double* bm, int* be, double* utt_loss, double* utt_logp,
+                             double* utt_pm, int* utt_pe, int* utt_status, int mode,
+                             const uint8_t* mask, double* best, int fwd_only);
 // Arc masks of a finite alignment beam from the max-plus scores.
 hipError_t launch_beam_mask(hipStream_t st, const float* S, int M, int N, long long dp_total,
-                            const int* row_off, const int* tgt_off, const int* tgt_rel,
+                            int max_T, int max_L, const int* row_off, const int* tgt_off, const int* tgt_rel,
                             const uint8_t* flags, const long long* dp_off, const double* vf,
                             const double* vb, const double* best, double beam, uint8_t* mask);
 hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss,
                            const int* utt_status, Meta* meta);
-hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int max_T,
-                            int max_L, const int* row_off, const int* tgt_off,
-                            const int* tgt_rel, const int* utt_status,
-                            const double* utt_logp, const long long* dp_off,
-                            const double* alpha, const double* beta, float* Gam,
-                            double* g);
+hipError_t launch_occupancy(hipStream_t st, int M, int N, int max_T, int max_L,
+                            const int* row_off, const int* tgt_off, const int* tgt_rel,
+                            const int* utt_status, const double* utt_pm, const int* utt_pe,
+                            const long long* dp_off, const double* am, const int* ae,
+                            const double* bm, const int* be, float* Gam, double* g);
 // d_eta (device double) = grad * sum_m (g_m exp(S[0][m]) - Gamma[0][m]).
 hipError_t launch_blank_grad(hipStream_t st, const float* S, const float* Gam, const double* g,
                              int M, double grad, double* out);

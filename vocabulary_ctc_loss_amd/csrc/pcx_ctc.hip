@@ -99,14 +99,88 @@ __device__ __forceinline__ double lse2(double a, double b) {
 }
 
 // What a recursion computes over the lattice of an utterance:
-//   DP_SUM     log-sum of the forward (backward) scores over every CTC
-//              transition: the unpruned alpha (beta) of the loss;
+//   DP_SUM     the forward (backward) sums over every CTC transition: the
+//              unpruned alpha (beta) of the loss, as scaled probabilities;
 //   DP_PRUNED  the same over the arcs a finite alignment beam keeps (bit
 //              masks from k_beam_mask, one byte per lattice node);
 //   DP_MAX     best prefix scores vf (emission included) and best suffix
-//              scores vb (emission of the node excluded) in FP64 max-plus,
-//              and the best complete alignment's score per utterance.
+//              scores vb (emission of the node excluded) in FP64 max-plus
+//              (log domain), and the best complete alignment's score per
+//              utterance.
 enum : int { DP_SUM = 0, DP_PRUNED = 1, DP_MAX = 2 };
+
+// Scaled probabilities.  The sums of the recursions are kept in the
+// probability domain as an FP64 mantissa and a separate int32 exponent,
+// x = m 2^e, so that they neither underflow (an alignment sum of 1,100
+// frames can lie far below 2^-1074) nor need an exp and a log per
+// transition: a step is an exponent maximum, three exact rescalings, two
+// additions and a multiplication by the emission, then one renormalisation.
+// Rounding: one relative error of at most about 2^-52 per addition and
+// multiplication, which in the log domain is an absolute error of the same
+// size (the log-domain form also rounds its exp and log).  Zero is m = 0
+// with the exponent ZERO_E, far below any reachable exponent, so that a
+// rescaling by it gives exactly 0 without overflowing.
+constexpr int ZERO_E = -(1 << 29);
+
+struct Sc {
+  double m;
+  int e;
+};
+
+__device__ __forceinline__ Sc sc_make(double v, int e) {
+  if (v == 0.0) return {0.0, ZERO_E};
+  int ex = 0;
+  const double mant = frexp(v, &ex);
+  return {mant, e + ex};
+}
+
+// a + b + c of scaled values, exponent-aligned to the largest.
+__device__ __forceinline__ double sc_sum3(const Sc& a, const Sc& b, const Sc& c, int& emax) {
+  emax = max(a.e, max(b.e, c.e));
+  return ldexp(a.m, a.e - emax) + ldexp(b.m, b.e - emax) + ldexp(c.m, c.e - emax);
+}
+
+// exp(S) of a log-probability S as m 2^n: Cody-Waite reduction S = n ln2 + r
+// (ln2 in a 32-bit head and a tail), |r| <= ln2 / 2, and e^r by its
+// degree-13 Taylor polynomial (truncation < 1e-17 relative), Estrin's
+// scheme.  S below -1e6 is taken as -1e6 (probability 2^-1.4e6, still a
+// scaled value); a NaN stays NaN.
+__device__ __forceinline__ Sc sc_exp(float s) {
+  double x = (double)s;
+  x = x < -1e6 ? -1e6 : x;
+  const double n = rint(x * 0x1.71547652b82fep+0);
+  double r = fma(-n, 0x1.62e42ff000000p-1, x);
+  r = fma(-n, -0x1.718432a1b0e26p-35, r);
+  const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
+  const double p01 = r + 1.0;
+  const double p23 = fma(r, 0x1.5555555555555p-3, 0.5);
+  const double p45 = fma(r, 0x1.1111111111111p-7, 0x1.5555555555555p-5);
+  const double p67 = fma(r, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10);
+  const double p89 = fma(r, 0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16);
+  const double pab = fma(r, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22);
+  const double pcd = fma(r, 0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29);
+  const double q0 = fma(r2, p23, p01), q1 = fma(r2, p67, p45), q2 = fma(r2, pab, p89);
+  const double s0 = fma(r4, q1, q0), s1 = fma(r4, pcd, q2);
+  return {fma(r8, s1, s0), (int)n};
+}
+
+// Buffers of the recursions.  Sum modes: am / ae the forward values
+// (emission of the node included), bm / be the backward values without the
+// node's emission, so that alpha * beta / P is the posterior of the node;
+// utt_pm / utt_pe the total P.  DP_MAX: am the best prefix scores vf, bm the
+// best suffix scores vb (log domain), best the best complete scores.
+struct DpBufs {
+  double* am;
+  int* ae;
+  double* bm;
+  int* be;
+  double* utt_loss;
+  double* utt_logp;
+  double* utt_pm;
+  int* utt_pe;
+  int* utt_status;
+  double* best;
+};
 
 // Arc bits of a lattice node (t, s): bits 0-2 the arcs into it from s
 // (stay), s - 1 (advance) and s - 2 (skip); bits 3-5 the arcs out of it to
@@ -374,6 +448,289 @@ __device__ __forceinline__ void beta_utt(
   }
 }
 
+// Forward sums of utterance n as scaled probabilities; the values (emission
+// included) are stored for the occupancy pass unless am is NULL (the loss
+// alone).  PRUNED: transitions masked by the kept-arc bits.
+template <int SPT, bool PRUNED>
+__device__ __forceinline__ void alpha_sum(
+    int n, char* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
+    const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
+    const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
+    const uint8_t* __restrict__ mask, const DpBufs& b) {
+  const int row0 = row_off[n], T = row_off[n + 1] - row0;
+  const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
+  if (!flags[n]) {
+    if (threadIdx.x == 0) {
+      b.utt_loss[n] = 0.0;
+      b.utt_logp[n] = -INFINITY;
+      b.utt_pm[n] = 0.0;
+      b.utt_pe[n] = ZERO_E;
+      b.utt_status[n] = UTT_UNALIGNABLE;
+    }
+    return;
+  }
+  const int cap = SPT * blockDim.x;
+  double* mb0 = reinterpret_cast<double*>(sh);
+  double* mb1 = mb0 + cap;
+  int* eb0 = reinterpret_cast<int*>(mb1 + cap);
+  int* eb1 = eb0 + cap;
+  const long long o0 = dp_off[n];
+  double* om = b.am != nullptr ? b.am + o0 : nullptr;
+  int* oe = b.am != nullptr ? b.ae + o0 : nullptr;
+  const uint8_t* mk = PRUNED ? mask + o0 : nullptr;
+  int sidx[SPT];
+  long long ebase[SPT];
+  bool skip[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = threadIdx.x + j * blockDim.x;
+    sidx[j] = s;
+    int cls = 0;
+    bool sk = false;
+    if (s < Sn && (s & 1)) {
+      cls = tgt_rel[y0 + (s >> 1)];
+      sk = s >= 3 && cls != tgt_rel[y0 + (s >> 1) - 1];
+    }
+    skip[j] = sk;
+    ebase[j] = (long long)cls * M + row0;
+  }
+  float ecur[SPT][PF], enxt[SPT][PF];
+  int mcur[SPT][PF], mnxt[SPT][PF];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const bool in = sidx[j] < Sn && u < T;
+      ecur[j][u] = in ? S[ebase[j] + u] : 0.f;
+      mcur[j][u] = (PRUNED && in) ? mk[(long long)u * Sn + sidx[j]] : 0;
+    }
+  // frame 0: only the first blank and the first label can start (pruned:
+  // if their initial arcs are kept).
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = sidx[j];
+    if (s < Sn) {
+      const bool start = s <= 1 && (!PRUNED || (mcur[j][0] & ARC_IN_STAY));
+      Sc a{0.0, ZERO_E};
+      if (start) {
+        const Sc p = sc_exp(ecur[j][0]);
+        a = sc_make(p.m, p.e);
+      }
+      mb0[s] = a.m;
+      eb0[s] = a.e;
+      if (om) {
+        om[s] = a.m;
+        oe[s] = a.e;
+      }
+    }
+  }
+  lds_barrier();
+  for (int tb = 0; tb < T; tb += PF) {
+    if (tb + PF < T) {
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int t = tb + PF + u;
+          const bool in = sidx[j] < Sn && t < T;
+          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
+          mnxt[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int t = tb + u;
+      if (t >= T) break;
+      if (t == 0) continue;
+      const double* pm = (t & 1) ? mb0 : mb1;
+      const int* pe = (t & 1) ? eb0 : eb1;
+      double* cm = (t & 1) ? mb1 : mb0;
+      int* ce = (t & 1) ? eb1 : eb0;
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int s = sidx[j];
+        if (s < Sn) {
+          // the emission is ready before the chain needs it
+          const Sc p = sc_exp(ecur[j][u]);
+          const int m = mcur[j][u];
+          const bool k0 = !PRUNED || (m & ARC_IN_STAY);
+          const bool k1 = s >= 1 && (!PRUNED || (m & ARC_IN_ADV));
+          const bool k2 = skip[j] && (!PRUNED || (m & ARC_IN_SKIP));
+          const Sc a0 = k0 ? Sc{pm[s], pe[s]} : Sc{0.0, ZERO_E};
+          const Sc a1 = k1 ? Sc{pm[s - 1], pe[s - 1]} : Sc{0.0, ZERO_E};
+          const Sc a2 = k2 ? Sc{pm[s - 2], pe[s - 2]} : Sc{0.0, ZERO_E};
+          int emax;
+          const double sum = sc_sum3(a0, a1, a2, emax);
+          const Sc v = sc_make(sum * p.m, emax + p.e);
+          cm[s] = v.m;
+          ce[s] = v.e;
+          if (om) {
+            om[(long long)t * Sn + s] = v.m;
+            oe[(long long)t * Sn + s] = v.e;
+          }
+        }
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        ecur[j][u] = enxt[j][u];
+        mcur[j][u] = mnxt[j][u];
+      }
+  }
+  if (threadIdx.x == 0) {
+    const int l = (T - 1) & 1;
+    const double* lm = l ? mb1 : mb0;
+    const int* le = l ? eb1 : eb0;
+    Sc f1{lm[Sn - 1], le[Sn - 1]};
+    Sc f2 = Sn > 1 ? Sc{lm[Sn - 2], le[Sn - 2]} : Sc{0.0, ZERO_E};
+    if (PRUNED) {  // final arcs
+      const uint8_t* fm = mk + (long long)(T - 1) * Sn;
+      if (!(fm[Sn - 1] & ARC_OUT_STAY)) f1 = Sc{0.0, ZERO_E};
+      if (Sn > 1 && !(fm[Sn - 2] & ARC_OUT_STAY)) f2 = Sc{0.0, ZERO_E};
+    }
+    int emax;
+    const double sum = sc_sum3(f1, f2, Sc{0.0, ZERO_E}, emax);
+    const Sc P = sc_make(sum, emax);
+    const double logP = P.m > 0.0 ? log(P.m) + (double)P.e * 0x1.62e42fefa39efp-1 : -INFINITY;
+    b.utt_logp[n] = logP;
+    b.utt_pm[n] = P.m;
+    b.utt_pe[n] = P.e;
+    if (isfinite(logP)) {
+      b.utt_loss[n] = -logP;
+      b.utt_status[n] = UTT_OK;
+    } else {
+      b.utt_loss[n] = 0.0;
+      b.utt_status[n] = UTT_NONFINITE;
+    }
+  }
+}
+
+// Backward sums of utterance n as scaled probabilities.  The stored value of
+// a node excludes its own emission (alpha * beta / P is then its posterior);
+// the recursion carries the value with the emission.
+template <int SPT, bool PRUNED>
+__device__ __forceinline__ void beta_sum(
+    int n, char* sh, const float* __restrict__ S, int M, const int* __restrict__ row_off,
+    const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
+    const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
+    const uint8_t* __restrict__ mask, const DpBufs& b) {
+  if (!flags[n]) return;
+  const int row0 = row_off[n], T = row_off[n + 1] - row0;
+  const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
+  const int cap = SPT * blockDim.x;
+  double* mb0 = reinterpret_cast<double*>(sh);
+  double* mb1 = mb0 + cap;
+  int* eb0 = reinterpret_cast<int*>(mb1 + cap);
+  int* eb1 = eb0 + cap;
+  const long long o0 = dp_off[n];
+  double* om = b.bm + o0;
+  int* oe = b.be + o0;
+  const uint8_t* mk = PRUNED ? mask + o0 : nullptr;
+  int sidx[SPT];
+  long long ebase[SPT];
+  bool skip[SPT];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = threadIdx.x + j * blockDim.x;
+    sidx[j] = s;
+    int cls = 0;
+    bool sk = false;
+    if (s < Sn && (s & 1)) {
+      cls = tgt_rel[y0 + (s >> 1)];
+      sk = s + 2 < Sn && cls != tgt_rel[y0 + (s >> 1) + 1];
+    }
+    skip[j] = sk;
+    ebase[j] = (long long)cls * M + row0;
+  }
+  // Frames are visited downwards; block b covers frames T-1-b*PF-u, u < PF.
+  float ecur[SPT][PF], enxt[SPT][PF];
+  int mcur[SPT][PF], mnxt[SPT][PF];
+#pragma unroll
+  for (int j = 0; j < SPT; ++j)
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int t = T - 1 - u;
+      const bool in = sidx[j] < Sn && t >= 0;
+      ecur[j][u] = in ? S[ebase[j] + t] : 0.f;
+      mcur[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+    }
+  const int tl = T - 1;
+  double* lm = (tl & 1) ? mb1 : mb0;
+  int* le = (tl & 1) ? eb1 : eb0;
+#pragma unroll
+  for (int j = 0; j < SPT; ++j) {
+    const int s = sidx[j];
+    if (s < Sn) {
+      const bool fin = s >= Sn - 2 && (!PRUNED || (mcur[j][0] & ARC_OUT_STAY));
+      // beta = 1 on the final states (0.5 * 2^1), times the emission
+      const Sc p = sc_exp(ecur[j][0]);
+      const Sc u = fin ? sc_make(p.m, p.e) : Sc{0.0, ZERO_E};
+      lm[s] = u.m;
+      le[s] = u.e;
+      om[(long long)tl * Sn + s] = fin ? 0.5 : 0.0;
+      oe[(long long)tl * Sn + s] = fin ? 1 : ZERO_E;
+    }
+  }
+  lds_barrier();
+  for (int tb = 0; tb < T; tb += PF) {
+    if (tb + PF < T) {
+#pragma unroll
+      for (int j = 0; j < SPT; ++j)
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+          const int t = T - 1 - (tb + PF + u);
+          const bool in = sidx[j] < Sn && t >= 0;
+          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
+          mnxt[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < PF; ++u) {
+      const int t = T - 1 - (tb + u);
+      if (t < 0) break;
+      if (t == T - 1) continue;
+      const double* nm = ((t + 1) & 1) ? mb1 : mb0;
+      const int* ne = ((t + 1) & 1) ? eb1 : eb0;
+      double* cm = (t & 1) ? mb1 : mb0;
+      int* ce = (t & 1) ? eb1 : eb0;
+#pragma unroll
+      for (int j = 0; j < SPT; ++j) {
+        const int s = sidx[j];
+        if (s < Sn) {
+          const Sc p = sc_exp(ecur[j][u]);
+          const int m = mcur[j][u];
+          const bool k0 = !PRUNED || (m & ARC_OUT_STAY);
+          const bool k1 = s + 1 < Sn && (!PRUNED || (m & ARC_OUT_ADV));
+          const bool k2 = skip[j] && (!PRUNED || (m & ARC_OUT_SKIP));
+          const Sc b0 = k0 ? Sc{nm[s], ne[s]} : Sc{0.0, ZERO_E};
+          const Sc b1 = k1 ? Sc{nm[s + 1], ne[s + 1]} : Sc{0.0, ZERO_E};
+          const Sc b2 = k2 ? Sc{nm[s + 2], ne[s + 2]} : Sc{0.0, ZERO_E};
+          int emax;
+          const double sum = sc_sum3(b0, b1, b2, emax);
+          const Sc v = sc_make(sum * p.m, emax + p.e);
+          cm[s] = v.m;
+          ce[s] = v.e;
+          // stored without the emission: the sum itself (not renormalised;
+          // at most 3 times a power of two)
+          om[(long long)t * Sn + s] = sum;
+          oe[(long long)t * Sn + s] = sum == 0.0 ? ZERO_E : emax;
+        }
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int j = 0; j < SPT; ++j)
+#pragma unroll
+      for (int u = 0; u < PF; ++u) {
+        ecur[j][u] = enxt[j][u];
+        mcur[j][u] = mnxt[j][u];
+      }
+  }
+}
+
 // Both recursions in one launch: work-groups 0..N-1 run the forward
 // recursion of utterance n, work-groups N..2N-1 (when launched) the backward
 // recursion of utterance n - N.  The two only read S (and the arc masks), so
@@ -384,16 +741,25 @@ __global__ __launch_bounds__(1024) void k_alpha_beta(
     const float* __restrict__ S, int M, int N, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
-    const uint8_t* __restrict__ mask, double* __restrict__ alpha, double* __restrict__ beta,
-    double* __restrict__ utt_loss, double* __restrict__ utt_logp, int* __restrict__ utt_status,
-    double* __restrict__ best) {
+    const uint8_t* __restrict__ mask, DpBufs bufs) {
   extern __shared__ double sh[];
   const int b = blockIdx.x;
-  if (b < N)
-    alpha_utt<SPT, MODE>(b, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask, alpha,
-                         utt_loss, utt_logp, utt_status, best);
-  else
-    beta_utt<SPT, MODE>(b - N, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask, beta);
+  if (MODE == DP_MAX) {
+    if (b < N)
+      alpha_utt<SPT, DP_MAX>(b, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask,
+                             bufs.am, nullptr, nullptr, nullptr, bufs.best);
+    else
+      beta_utt<SPT, DP_MAX>(b - N, sh, S, M, row_off, tgt_off, tgt_rel, flags, dp_off, mask,
+                            bufs.bm);
+  } else {
+    char* shc = reinterpret_cast<char*>(sh);
+    if (b < N)
+      alpha_sum<SPT, MODE == DP_PRUNED>(b, shc, S, M, row_off, tgt_off, tgt_rel, flags, dp_off,
+                                        mask, bufs);
+    else
+      beta_sum<SPT, MODE == DP_PRUNED>(b - N, shc, S, M, row_off, tgt_off, tgt_rel, flags,
+                                       dp_off, mask, bufs);
+  }
 }
 
 // Arc masks of a finite alignment beam.  An arc is kept when the best
@@ -405,65 +771,85 @@ __global__ __launch_bounds__(1024) void k_alpha_beta(
 // that association; the initial arc into (0, s) scores vf[0][s] + vb[0][s]
 // and the final arc out of (T-1, s) scores vf[T-1][s].  Every node writes
 // the bits of its incoming and of its outgoing arcs (the same decisions,
-// read by the forward and by the backward recursion).  Work-group (n, k):
-// nodes k, k + blockDim.x * gridDim.y, ... of utterance n.
-__global__ __launch_bounds__(256) void k_beam_mask(
+// read by the forward and by the backward recursion).
+//
+// Work-group (n, frame tile, state tile): MASK_TF frames x MASK_TS states of
+// utterance n.  The emissions of the tile (and of the next frame and the
+// next two states, for the outgoing arcs) are staged in LDS first, each
+// state's frames read as one contiguous run of S (class-major); then thread
+// j walks the tile's frames for state s0 + j, so that the best-score tables
+// ([t][s], s contiguous) are read across the threads of a wavefront.
+constexpr int MASK_TF = 16, MASK_TS = 256;
+
+__global__ __launch_bounds__(MASK_TS) void k_beam_mask(
     const float* __restrict__ S, int M, const int* __restrict__ row_off,
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     const double* __restrict__ vf, const double* __restrict__ vb,
     const double* __restrict__ best, double beam, uint8_t* __restrict__ mask) {
+  constexpr int ET = MASK_TF + 1, ES = MASK_TS + 2;
+  __shared__ float e_sh[ES][ET + 1];  // [state][frame], padded
+  __shared__ int c_sh[ES];            // class of each state of the tile
   const int n = blockIdx.x;
   if (!flags[n]) return;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
+  const int t0 = blockIdx.y * MASK_TF, s0 = blockIdx.z * MASK_TS;
+  if (t0 >= T || s0 >= Sn) return;
+  for (int k = threadIdx.x; k < ES; k += MASK_TS) {
+    const int s = s0 + k;
+    c_sh[k] = (s < Sn && (s & 1)) ? tgt_rel[y0 + (s >> 1)] : 0;
+  }
+  lds_barrier();
+  for (int k = threadIdx.x; k < ES * ET; k += MASK_TS) {
+    const int ss = k / ET, tt = k - ss * ET;
+    const int s = s0 + ss, t = t0 + tt;
+    e_sh[ss][tt] = (s < Sn && t < T) ? S[(long long)c_sh[ss] * M + row0 + t] : 0.f;
+  }
+  lds_barrier();
+  const int j = threadIdx.x, s = s0 + j;
+  if (s >= Sn) return;
   const long long base = dp_off[n];
   const double thr = best[n] - beam;
-  const long long nodes = (long long)T * Sn;
-  for (long long i = blockIdx.y * (long long)blockDim.x + threadIdx.x; i < nodes;
-       i += (long long)gridDim.y * blockDim.x) {
-    const int t = (int)(i / Sn), s = (int)(i - (long long)t * Sn);
-    const int cls = (s & 1) ? tgt_rel[y0 + (s >> 1)] : 0;
-    const double* f = vf + base;
-    const double* g = vb + base;
+  const int cls = c_sh[j];
+  const bool skip_in = (s & 1) && s >= 3 && cls != tgt_rel[y0 + (s >> 1) - 1];
+  const bool skip_out = (s & 1) && s + 2 < Sn && c_sh[j + 2] != cls;
+  const double* f = vf + base;
+  const double* g = vb + base;
+  const int t1 = min(T, t0 + MASK_TF);
+  for (int t = t0; t < t1; ++t) {
+    const int tt = t - t0;
     int bits = 0;
     if (t == 0) {
       if (s <= 1 && f[s] + g[s] >= thr) bits |= ARC_IN_STAY;  // initial arc
     } else {
-      const double e = (double)S[(long long)cls * M + row0 + t];
+      const double e = (double)e_sh[j][tt];
       const double* fp = f + (long long)(t - 1) * Sn;
       const double gs = g[(long long)t * Sn + s];
       if ((fp[s] + e) + gs >= thr) bits |= ARC_IN_STAY;
       if (s >= 1 && (fp[s - 1] + e) + gs >= thr) bits |= ARC_IN_ADV;
-      if ((s & 1) && s >= 3 && cls != tgt_rel[y0 + (s >> 1) - 1] && (fp[s - 2] + e) + gs >= thr)
-        bits |= ARC_IN_SKIP;
+      if (skip_in && (fp[s - 2] + e) + gs >= thr) bits |= ARC_IN_SKIP;
     }
     const double fs = f[(long long)t * Sn + s];
     if (t == T - 1) {
       if (s >= Sn - 2 && fs >= thr) bits |= ARC_OUT_STAY;  // final arc
     } else {
       const double* gn = g + (long long)(t + 1) * Sn;
-      const long long r1 = row0 + t + 1;
-      const double e0 = (double)S[(long long)cls * M + r1];
-      if ((fs + e0) + gn[s] >= thr) bits |= ARC_OUT_STAY;
-      if (s + 1 < Sn) {
-        const int c1 = ((s + 1) & 1) ? tgt_rel[y0 + ((s + 1) >> 1)] : 0;
-        if ((fs + (double)S[(long long)c1 * M + r1]) + gn[s + 1] >= thr) bits |= ARC_OUT_ADV;
-      }
-      if ((s & 1) && s + 2 < Sn) {
-        const int c2 = tgt_rel[y0 + ((s + 2) >> 1)];
-        if (c2 != cls && (fs + (double)S[(long long)c2 * M + r1]) + gn[s + 2] >= thr)
-          bits |= ARC_OUT_SKIP;
-      }
+      if ((fs + (double)e_sh[j][tt + 1]) + gn[s] >= thr) bits |= ARC_OUT_STAY;
+      if (s + 1 < Sn && (fs + (double)e_sh[j + 1][tt + 1]) + gn[s + 1] >= thr)
+        bits |= ARC_OUT_ADV;
+      if (skip_out && (fs + (double)e_sh[j + 2][tt + 1]) + gn[s + 2] >= thr)
+        bits |= ARC_OUT_SKIP;
     }
-    mask[base + i] = (uint8_t)bits;
+    mask[base + (long long)t * Sn + s] = (uint8_t)bits;
   }
 }
 
 // Occupancies on the selected classes for OCC_FRAMES frames of one
-// utterance: q(t, s) = exp(alpha + beta - emission - log P) per state,
-// gamma of a class = sum of q over its states (fixed order), g_m = sum_s q.
-// Rows of excluded utterances get g = 0 (Gamma was zero-filled).
+// utterance: q(t, s) = alpha * beta / P per state (scaled probabilities;
+// beta excludes the node's emission), gamma of a class = sum of q over its
+// states (fixed order), g_m = sum_s q.  Rows of excluded utterances get
+// g = 0 (Gamma was zero-filled).
 //
 // The frames are taken F at a time (F = 1, 2, 4 or 8, as many as the LDS
 // holds for the longest utterance), so that the loads of F frames are in
@@ -474,12 +860,12 @@ constexpr int OCC_THREADS = 256;
 
 template <int F>
 __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
-    const float* __restrict__ S, int M, const int* __restrict__ row_off,
-    const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
-    const int* __restrict__ utt_status, const double* __restrict__ utt_logp,
-    const long long* __restrict__ dp_off, const double* __restrict__ alpha,
-    const double* __restrict__ beta, float* __restrict__ Gam, double* __restrict__ g,
-    int Lcap) {
+    int M, const int* __restrict__ row_off, const int* __restrict__ tgt_off,
+    const int* __restrict__ tgt_rel, const int* __restrict__ utt_status,
+    const double* __restrict__ utt_pm, const int* __restrict__ utt_pe,
+    const long long* __restrict__ dp_off, const double* __restrict__ am,
+    const int* __restrict__ ae, const double* __restrict__ bm, const int* __restrict__ be,
+    float* __restrict__ Gam, double* __restrict__ g, int Lcap) {
   static_assert(OCC_THREADS % F == 0 && 64 % F == 0, "frames per round");
   extern __shared__ double sh[];
   constexpr int NW = OCC_THREADS / 64;
@@ -516,9 +902,12 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     s_seg[i] = before == 0 ? (less << 16) | same : -1;
   }
   lds_barrier();
-  const double logP = utt_logp[n];
-  const double* A = alpha + dp_off[n];
-  const double* B = beta + dp_off[n];
+  const double invP = 1.0 / utt_pm[n];
+  const int Pe = utt_pe[n];
+  const double* Am = am + dp_off[n];
+  const int* Ae = ae + dp_off[n];
+  const double* Bm = bm + dp_off[n];
+  const int* Be = be + dp_off[n];
   const int f = threadIdx.x % F;  // this thread's frame within a round
   for (int tb = t0; tb < t1; tb += F) {
     const int t = tb + f;
@@ -529,10 +918,8 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     for (int s = threadIdx.x / F; s < Sn; s += OCC_THREADS / F) {
       double q = 0.0;
       if (live) {
-        const int cls = (s & 1) ? s_y[s >> 1] : 0;
-        const double e = (double)S[(long long)cls * M + row0 + t];
         const long long o = (long long)t * Sn + s;
-        q = exp(A[o] + B[o] - e - logP);
+        q = ldexp(Am[o] * Bm[o] * invP, Ae[o] + Be[o] - Pe);
       }
       s_q[s * F + f] = q;
       tot += q;
@@ -644,18 +1031,20 @@ void dp_shape(int max_L, int& threads, int& spt) {
 
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
-                             const uint8_t* flags, const long long* dp_off, double* alpha,
-                             double* beta, double* utt_loss, double* utt_logp, int* utt_status,
-                             int mode, const uint8_t* mask, double* best, int fwd_only) {
+                             const uint8_t* flags, const long long* dp_off, double* am, int* ae,
+                             double* bm, int* be, double* utt_loss, double* utt_logp,
+                             double* utt_pm, int* utt_pe, int* utt_status, int mode,
+                             const uint8_t* mask, double* best, int fwd_only) {
   if (N == 0) return hipSuccess;
   int threads, spt;
   dp_shape(max_L, threads, spt);
-  const size_t shm = 2 * (size_t)spt * threads * sizeof(double);
+  // two frames of values: FP64 (and, for the sums, an int32 exponent each)
+  const size_t shm = 2 * (size_t)spt * threads * (sizeof(double) + (mode == 2 ? 0 : sizeof(int)));
   const int grid = fwd_only ? N : 2 * N;
+  const DpBufs bufs{am, ae, bm, be, utt_loss, utt_logp, utt_pm, utt_pe, utt_status, best};
 #define PCX_AB(SPT_, MODE_)                                                                  \
   k_alpha_beta<SPT_, MODE_><<<grid, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel,  \
-                                                        flags, dp_off, mask, alpha, beta,    \
-                                                        utt_loss, utt_logp, utt_status, best)
+                                                        flags, dp_off, mask, bufs)
 #define PCX_AB_MODE(SPT_)                              \
   switch (mode) {                                      \
     case DP_SUM: PCX_AB(SPT_, DP_SUM); break;          \
@@ -676,17 +1065,13 @@ hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int m
 }
 
 hipError_t launch_beam_mask(hipStream_t st, const float* S, int M, int N, long long dp_total,
-                            const int* row_off, const int* tgt_off, const int* tgt_rel,
+                            int max_T, int max_L, const int* row_off, const int* tgt_off, const int* tgt_rel,
                             const uint8_t* flags, const long long* dp_off, const double* vf,
                             const double* vb, const double* best, double beam, uint8_t* mask) {
-  if (N == 0 || dp_total == 0) return hipSuccess;
-  // about four nodes per thread on average, at least one work-group per
-  // utterance, at most 64
-  long long per = (dp_total / N + 1023) / 1024;
-  if (per < 1) per = 1;
-  if (per > 64) per = 64;
-  k_beam_mask<<<dim3(N, (unsigned)per), 256, 0, st>>>(S, M, row_off, tgt_off, tgt_rel, flags,
-                                                       dp_off, vf, vb, best, beam, mask);
+  if (N == 0 || dp_total == 0 || max_T <= 0) return hipSuccess;
+  const dim3 grid(N, (max_T + MASK_TF - 1) / MASK_TF, (2 * max_L + 1 + MASK_TS - 1) / MASK_TS);
+  k_beam_mask<<<grid, MASK_TS, 0, st>>>(S, M, row_off, tgt_off, tgt_rel, flags, dp_off, vf, vb,
+                                        best, beam, mask);
   return hipGetLastError();
 }
 
@@ -696,11 +1081,11 @@ hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss, const 
   return hipGetLastError();
 }
 
-hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int max_T, int max_L,
+hipError_t launch_occupancy(hipStream_t st, int M, int N, int max_T, int max_L,
                             const int* row_off, const int* tgt_off, const int* tgt_rel,
-                            const int* utt_status, const double* utt_logp,
-                            const long long* dp_off, const double* alpha, const double* beta,
-                            float* Gam, double* g) {
+                            const int* utt_status, const double* utt_pm, const int* utt_pe,
+                            const long long* dp_off, const double* am, const int* ae,
+                            const double* bm, const int* be, float* Gam, double* g) {
   if (N == 0 || max_T <= 0) return hipSuccess;
   const int Lcap = max_L > 0 ? max_L : 1;
   // frames per round: the most whose q block leaves room for four
@@ -713,8 +1098,9 @@ hipError_t launch_occupancy(hipStream_t st, const float* S, int M, int N, int ma
   const size_t shm = shm_of(F);
   dim3 grid(N, (max_T + OCC_FRAMES - 1) / OCC_FRAMES);
 #define PCX_OCC(FR)                                                                          \
-  k_occupancy<FR><<<grid, OCC_THREADS, shm, st>>>(S, M, row_off, tgt_off, tgt_rel, utt_status, \
-                                                  utt_logp, dp_off, alpha, beta, Gam, g, Lcap)
+  k_occupancy<FR><<<grid, OCC_THREADS, shm, st>>>(M, row_off, tgt_off, tgt_rel, utt_status,    \
+                                                  utt_pm, utt_pe, dp_off, am, ae, bm, be, Gam, g, \
+                                                  Lcap)
   switch (F) {
     case 8: PCX_OCC(8); break;
     case 4: PCX_OCC(4); break;
