@@ -52,8 +52,9 @@ KERNEL_SRC = {"fwd_gemm_lse": GEMM_SRC, "bwd_recompute_dz": GEMM_SRC, "dx_gemm":
 
 # Kernel families whose work is a slice of the head GEMMs: FLOPs per step.
 GEMM_KERNELS = ("fwd_gemm_lse", "bwd_recompute_dz", "dx_gemm", "dw_gemm")
-# The CTC recursions: per (frame, extended-label state) each writes its FP64
-# value (alpha, beta: 2 x 8 B) and reads one fp32 emission (2 x 4 B).
+# The CTC recursions: per (frame, extended-label state) each writes its value
+# (alpha, beta: 2 x 8 B, an fp32 mantissa and an int32 exponent) and reads
+# one fp32 emission (2 x 4 B).
 DP_KERNEL = "ctc_alpha_beta"
 DP_BYTES_PER_STATE = 24
 
@@ -65,19 +66,22 @@ DP_BYTES_PER_STATE = 24
 #                   (16 B each), lambda written in FP64 and fp32 (12 B/frame);
 #   scores          Zsel read and S written in place (K x M fp32 each), lambda
 #                   read (8 B/frame);
-#   occupancy       alpha and beta read (16 B/state), S read (4 B/state), the
-#                   occupancy written (4 B/state), g written (8 B/frame);
+#   occupancy       alpha and beta read (16 B/state), the occupancy written
+#                   (4 B per frame and distinct class of the utterance, blank
+#                   included), g written (8 B/frame);
 #   ctc_viterbi     as ctc_alpha_beta (best prefix / suffix scores);
 #   beam_mask       the two best-score tables read (16 B/state), the emission
 #                   (4 B/state), the arc mask written (1 B/state).
 def pass_bytes(bt, K, nspan, pruned=False):
     L = np.diff(bt.tgt_off).astype(np.int64)
     states = int(np.sum(bt.frame_counts.astype(np.int64) * (2 * L + 1)))
+    classes = sum(int(t) * (len(np.unique(bt.tgt[bt.tgt_off[n]:bt.tgt_off[n + 1]])) + 1)
+                  for n, t in enumerate(bt.frame_counts))
     out = {
         DP_KERNEL: (DP_BYTES_PER_STATE + (2 if pruned else 0)) * states,
         "lambda": bt.M * (16 * nspan + 12),
         "scores": bt.M * (8 * K + 8),
-        "occupancy": 24 * states + 8 * bt.M,
+        "occupancy": 16 * states + 4 * classes + 8 * bt.M,
     }
     if pruned:
         out["ctc_viterbi"] = DP_BYTES_PER_STATE * states

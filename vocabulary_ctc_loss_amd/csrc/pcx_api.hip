@@ -70,8 +70,9 @@ struct pcx_ctx {
   DevBuf meta, row_off, flags, dp_off, col2sel, U, tgt_rel, tgt_off;
   DevBuf part, lam, lamf, S, alpha, beta, utt_loss, utt_logp, utt_status;
   DevBuf Gam, g, dZ, dXacc, dwpart, dbpart, wt, eta, w32, b32, other, gu, ou;
+  DevBuf cmap, wg;  // selected-first column order of the recompute
   DevBuf arcmask, ubest, loss_full, logp_full, status_full;  // finite beam
-  DevBuf alpha_e, beta_e, utt_pm, utt_pe, pm_full, pe_full;   // scaled-value exponents
+  DevBuf utt_pm, utt_pe, pm_full, pe_full;   // scaled totals (mantissa, exponent)
   Meta* host_meta = nullptr;  // pinned
   // caller's allocator (both NULL: hipMalloc / hipFree)
   pcx_alloc_fn alloc = nullptr;
@@ -140,8 +141,9 @@ size_t total_bytes(const pcx_ctx* c) {
                           &c->beta, &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam,
                           &c->g, &c->dZ, &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta,
                           &c->w32, &c->b32, &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest,
-                          &c->loss_full, &c->logp_full, &c->status_full, &c->alpha_e,
-                          &c->beta_e, &c->utt_pm, &c->utt_pe, &c->pm_full, &c->pe_full};
+                          &c->loss_full, &c->logp_full, &c->status_full,
+                          &c->utt_pm, &c->utt_pe, &c->pm_full, &c->pe_full,
+                          &c->cmap, &c->wg};
   size_t t = 0;
   for (const DevBuf* b : bufs) t += b->cap;
   return t;
@@ -318,8 +320,8 @@ void pcx_destroy(pcx_ctx* c) {
                     &c->utt_loss, &c->utt_logp, &c->utt_status, &c->Gam, &c->g, &c->dZ,
                     &c->dXacc, &c->dwpart, &c->dbpart, &c->wt, &c->eta, &c->w32, &c->b32,
                     &c->other, &c->gu, &c->ou, &c->arcmask, &c->ubest, &c->loss_full,
-                    &c->logp_full, &c->status_full, &c->alpha_e, &c->beta_e, &c->utt_pm,
-                    &c->utt_pe, &c->pm_full, &c->pe_full};
+                    &c->logp_full, &c->status_full, &c->utt_pm, &c->utt_pe, &c->pm_full,
+                    &c->pe_full, &c->cmap, &c->wg};
   if (c->release) {
     // every call of the context is ordered before the last call's stream
     // tail: once that has finished, nothing of ours touches the workspace
@@ -430,10 +432,10 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
   ENSURE(lam, (size_t)M * sizeof(double));
   ENSURE(lamf, (size_t)M * sizeof(float));
   ENSURE(S, (size_t)K * M * sizeof(float));
+  // 8 bytes per lattice node each: FP64 max-plus scores (finite beam), then
+  // the sums as fp32 mantissa + int32 exponent
   ENSURE(alpha, (size_t)hm.dp_total * sizeof(double));
   ENSURE(beta, (size_t)hm.dp_total * sizeof(double));
-  ENSURE(alpha_e, (size_t)hm.dp_total * sizeof(int));
-  ENSURE(beta_e, (size_t)hm.dp_total * sizeof(int));
   ENSURE(utt_pm, (size_t)(N + 1) * sizeof(double));
   ENSURE(utt_pe, (size_t)(N + 1) * sizeof(int));
   ENSURE(utt_loss, (size_t)(N + 1) * sizeof(double));
@@ -486,8 +488,8 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
            launch_alpha_beta(st, (const float*)ctx->S.p, iM, N, hm.max_L,
                              (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                              (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
-                             (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p, nullptr,
-                             (double*)ctx->beta.p, nullptr, nullptr, nullptr, nullptr, nullptr,
+                             (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
+                             (double*)ctx->beta.p, nullptr, nullptr, nullptr, nullptr,
                              nullptr, 2, nullptr, (double*)ctx->ubest.p, 0));
     LAUNCH(K_BEAM_MASK,
            launch_beam_mask(st, (const float*)ctx->S.p, iM, N, hm.dp_total, hm.max_T, hm.max_L,
@@ -504,8 +506,8 @@ pcx_status pcx_forward(pcx_ctx* ctx, const void* X, const void* W, const void* b
                            (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                            (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
                            (const long long*)ctx->dp_off.p, (double*)ctx->alpha.p,
-                           (int*)ctx->alpha_e.p, (double*)ctx->beta.p, (int*)ctx->beta_e.p,
-                           (double*)ctx->utt_loss.p, (double*)ctx->utt_logp.p,
+                           (double*)ctx->beta.p, (double*)ctx->utt_loss.p,
+                           (double*)ctx->utt_logp.p,
                            (double*)ctx->utt_pm.p, (int*)ctx->utt_pe.p,
                            (int*)ctx->utt_status.p, pruned ? 1 : 0,
                            pruned ? (const uint8_t*)ctx->arcmask.p : nullptr, nullptr, 0));
@@ -552,8 +554,7 @@ static pcx_status run_occupancy(pcx_ctx* ctx, hipStream_t st) {
                                  (const int*)ctx->tgt_off.p, (const int*)ctx->tgt_rel.p,
                                  (const int*)ctx->utt_status.p, (const double*)ctx->utt_pm.p,
                                  (const int*)ctx->utt_pe.p, (const long long*)ctx->dp_off.p,
-                                 (const double*)ctx->alpha.p, (const int*)ctx->alpha_e.p,
-                                 (const double*)ctx->beta.p, (const int*)ctx->beta_e.p,
+                                 (const double*)ctx->alpha.p, (const double*)ctx->beta.p,
                                  (float*)ctx->Gam.p, (double*)ctx->g.p));
   return PCX_OK;
 }
@@ -673,6 +674,19 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (splitk < 1) splitk = 1;
   if (dW) ENSURE(dwpart, (size_t)splitk * C * D * sizeof(float));
 
+  // Where a chunk group can be expected to hold a tile's worth of selected
+  // classes or more (K close to V: small vocabularies), the recompute walks
+  // each group's columns unselected-first, so that the selected classes fill
+  // whole tiles whose product is skipped; its products then read the head
+  // rows they need gathered into wg.  (Not on the 256 x 256 bf16 core.)
+  const int Cg = CG < V ? CG : V;
+  const bool order = !big && (long long)ctx->K * Cg >= (long long)V * rec_tile_cols(cdt);
+  if (order) {
+    ENSURE(cmap, ((size_t)CG + 1) * sizeof(int));
+    ENSURE(wg, (size_t)CG * D * esz);
+  }
+  int* cmap = order ? (int*)ctx->cmap.p : nullptr;
+
   const int ngroups = (V + CG - 1) / CG;
   for (int gi = 0; gi < ngroups; ++gi) {
     const int c0 = gi * CG, c1 = (c0 + CG < V) ? c0 + CG : V, Cc = c1 - c0;
@@ -692,6 +706,9 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       sel += c0;
       w0 = 0;
     }
+    if (order)
+      LAUNCH(K_RECOMPUTE, launch_colperm(st, cdt, sel, w0, w0 + Cc, Wk, D, cmap, cmap + CG,
+                                         ctx->wg.p));
     for (int part = 0; part < G; ++part) {
       // frames [r0, r0 + Mp); S and Gamma keep their leading dimension M
       const int r0 = part * Mh;
@@ -703,7 +720,8 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
                               (const double*)ctx->g.p + r0, S + r0,
                               (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, CG,
                               (float*)ctx->dbpart.p, big, gu ? gu + r0 : nullptr,
-                              ou ? ou + r0 : nullptr, M));
+                              ou ? ou + r0 : nullptr, M, cmap, order ? ctx->wg.p : nullptr,
+                              order ? cmap + CG : nullptr));
       if (dX)
         LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, CG, Wk, Mp, D, w0, w0 + Cc,
                                dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
@@ -794,7 +812,7 @@ pcx_status pcx_get_discarded_mass(pcx_ctx* ctx, double* out, int64_t capacity) {
            launch_alpha_beta(st, (const float*)ctx->S.p, ctx->M, N, ctx->max_L,
                              (const int*)ctx->row_off.p, (const int*)ctx->tgt_off.p,
                              (const int*)ctx->tgt_rel.p, (const uint8_t*)ctx->flags.p,
-                             (const long long*)ctx->dp_off.p, nullptr, nullptr, nullptr, nullptr,
+                             (const long long*)ctx->dp_off.p, nullptr, nullptr,
                              (double*)ctx->loss_full.p, (double*)ctx->logp_full.p,
                              (double*)ctx->pm_full.p, (int*)ctx->pe_full.p,
                              (int*)ctx->status_full.p, 0, nullptr, nullptr, 1));

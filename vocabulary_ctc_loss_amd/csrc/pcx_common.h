@@ -177,7 +177,16 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart, int big,
                             const double* gu = nullptr, const float* ou = nullptr,
-                            long long ldS = 0);  // S / Gamma leading dimension (0: M)
+                            long long ldS = 0,  // S / Gamma leading dimension (0: M)
+                            const int* cmap = nullptr, const void* Wg = nullptr,
+                            const int* nu = nullptr);
+// Unselected-first column order of the chunk [c0, c1) into cmap[0 ..] and
+// *nu, and the head rows the recompute products read, gathered into Wg
+// (the recompute's cmap / Wg; not for the 256 x 256 bf16 core).
+hipError_t launch_colperm(hipStream_t st, int dtype, const int* col2sel, int c0, int c1,
+                          const void* W, int D, int* cmap, int* nu, void* Wg);
+// Columns of the recompute tile (of the cores that take a column order).
+int rec_tile_cols(int dtype);
 // wt: D x ldz scratch for the transposed weight chunk (bf16 only); with
 // stage_wt == 0 it already holds these columns (an earlier call staged them).
 // Rows of the recompute tile (one bias-gradient partial per row tile) and
@@ -214,8 +223,8 @@ hipError_t launch_widen(hipStream_t st, const void* src, float* dst, long long n
 // fwd_only: the forward recursion alone (am may then be NULL: losses only).
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
-                             const uint8_t* flags, const long long* dp_off, double* am, int* ae,
-                             double* bm, int* be, double* utt_loss, double* utt_logp,
+                             const uint8_t* flags, const long long* dp_off, double* am,
+                             double* bm, double* utt_loss, double* utt_logp,
                              double* utt_pm, int* utt_pe, int* utt_status, int mode,
                              const uint8_t* mask, double* best, int fwd_only);
 // Arc masks of a finite alignment beam from the max-plus scores.
@@ -228,8 +237,8 @@ hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss,
 hipError_t launch_occupancy(hipStream_t st, int M, int N, int max_T, int max_L,
                             const int* row_off, const int* tgt_off, const int* tgt_rel,
                             const int* utt_status, const double* utt_pm, const int* utt_pe,
-                            const long long* dp_off, const double* am, const int* ae,
-                            const double* bm, const int* be, float* Gam, double* g);
+                            const long long* dp_off, const double* am, const double* bm,
+                            float* Gam, double* g);
 // d_eta (device double) = grad * sum_m (g_m exp(S[0][m]) - Gamma[0][m]).
 hipError_t launch_blank_grad(hipStream_t st, const float* S, const float* Gam, const double* g,
                              int M, double grad, double* out);

@@ -140,40 +140,41 @@ __device__ __forceinline__ double sc_sum3(const Sc& a, const Sc& b, const Sc& c,
   return ldexp(a.m, a.e - emax) + ldexp(b.m, b.e - emax) + ldexp(c.m, c.e - emax);
 }
 
-// exp(S) of a log-probability S as m 2^n: Cody-Waite reduction S = n ln2 + r
-// (ln2 in a 32-bit head and a tail), |r| <= ln2 / 2, and e^r by its
-// degree-13 Taylor polynomial (truncation < 1e-17 relative), Estrin's
-// scheme.  S below -1e6 is taken as -1e6 (probability 2^-1.4e6, still a
-// scaled value); a NaN stays NaN.
+// exp(S) of an fp32 log-probability S as m 2^n, to fp32 precision (the
+// precision of S itself, an fp32 score): x = S log2(e) is formed as hi + lo
+// (hi the fp32 product, lo its rounding error by a fused multiply-add plus
+// S times the tail of log2(e)), n = rint(hi), and m = 2^((hi - n) + lo) by
+// the hardware exp2 (hi - n is exact and |(hi - n) + lo| <= 1/2 + 2^-20, so
+// m lies in [0.7, 1.42]); about 2^-22 relative error in all.  S below -1e6
+// is taken as -1e6 (probability 2^-1.4e6, still a scaled value); a NaN
+// stays NaN.
 __device__ __forceinline__ Sc sc_exp(float s) {
-  double x = (double)s;
-  x = x < -1e6 ? -1e6 : x;
-  const double n = rint(x * 0x1.71547652b82fep+0);
-  double r = fma(-n, 0x1.62e42ff000000p-1, x);
-  r = fma(-n, -0x1.718432a1b0e26p-35, r);
-  const double r2 = r * r, r4 = r2 * r2, r8 = r4 * r4;
-  const double p01 = r + 1.0;
-  const double p23 = fma(r, 0x1.5555555555555p-3, 0.5);
-  const double p45 = fma(r, 0x1.1111111111111p-7, 0x1.5555555555555p-5);
-  const double p67 = fma(r, 0x1.a01a01a01a01ap-13, 0x1.6c16c16c16c17p-10);
-  const double p89 = fma(r, 0x1.71de3a556c734p-19, 0x1.a01a01a01a01ap-16);
-  const double pab = fma(r, 0x1.ae64567f544e4p-26, 0x1.27e4fb7789f5cp-22);
-  const double pcd = fma(r, 0x1.6124613a86d09p-33, 0x1.1eed8eff8d898p-29);
-  const double q0 = fma(r2, p23, p01), q1 = fma(r2, p67, p45), q2 = fma(r2, pab, p89);
-  const double s0 = fma(r4, q1, q0), s1 = fma(r4, pcd, q2);
-  return {fma(r8, s1, s0), (int)n};
+  constexpr float L2E_HI = 0x1.715476p+0f;    // fp32 log2(e)
+  constexpr float L2E_LO = 0x1.4ae0c0p-26f;   // log2(e) - L2E_HI, rounded
+  const float x = s < -1e6f ? -1e6f : s;
+  const float hi = x * L2E_HI;
+  const float lo = fmaf(x, L2E_HI, -hi) + x * L2E_LO;
+  const float n = rintf(hi);
+  const float m = __builtin_amdgcn_exp2f((hi - n) + lo);
+  return {(double)m, (int)n};
 }
 
-// Buffers of the recursions.  Sum modes: am / ae the forward values
-// (emission of the node included), bm / be the backward values without the
-// node's emission, so that alpha * beta / P is the posterior of the node;
-// utt_pm / utt_pe the total P.  DP_MAX: am the best prefix scores vf, bm the
-// best suffix scores vb (log domain), best the best complete scores.
+// Stored form of a scaled value (the occupancy pass reads it): the mantissa
+// rounded to fp32 beside its exponent, one 8-byte word per lattice node.
+struct Sc32 {
+  float m;
+  int e;
+};
+
+// Buffers of the recursions, 8 bytes per lattice node.  Sum modes: am the
+// forward values (emission of the node included), bm the backward values
+// without the node's emission, both as Sc32, so that alpha * beta / P is the
+// posterior of the node; utt_pm / utt_pe the total P.  DP_MAX: am the best
+// prefix scores vf, bm the best suffix scores vb (FP64, log domain), best the
+// best complete scores.
 struct DpBufs {
   double* am;
-  int* ae;
   double* bm;
-  int* be;
   double* utt_loss;
   double* utt_logp;
   double* utt_pm;
@@ -475,8 +476,7 @@ __device__ __forceinline__ void alpha_sum(
   int* eb0 = reinterpret_cast<int*>(mb1 + cap);
   int* eb1 = eb0 + cap;
   const long long o0 = dp_off[n];
-  double* om = b.am != nullptr ? b.am + o0 : nullptr;
-  int* oe = b.am != nullptr ? b.ae + o0 : nullptr;
+  Sc32* om = b.am != nullptr ? reinterpret_cast<Sc32*>(b.am) + o0 : nullptr;
   const uint8_t* mk = PRUNED ? mask + o0 : nullptr;
   int sidx[SPT];
   long long ebase[SPT];
@@ -518,10 +518,7 @@ __device__ __forceinline__ void alpha_sum(
       }
       mb0[s] = a.m;
       eb0[s] = a.e;
-      if (om) {
-        om[s] = a.m;
-        oe[s] = a.e;
-      }
+      if (om) om[s] = Sc32{(float)a.m, a.e};
     }
   }
   lds_barrier();
@@ -564,10 +561,7 @@ __device__ __forceinline__ void alpha_sum(
           const Sc v = sc_make(sum * p.m, emax + p.e);
           cm[s] = v.m;
           ce[s] = v.e;
-          if (om) {
-            om[(long long)t * Sn + s] = v.m;
-            oe[(long long)t * Sn + s] = v.e;
-          }
+          if (om) om[(long long)t * Sn + s] = Sc32{(float)v.m, v.e};
         }
       }
       lds_barrier();
@@ -626,8 +620,7 @@ __device__ __forceinline__ void beta_sum(
   int* eb0 = reinterpret_cast<int*>(mb1 + cap);
   int* eb1 = eb0 + cap;
   const long long o0 = dp_off[n];
-  double* om = b.bm + o0;
-  int* oe = b.be + o0;
+  Sc32* om = reinterpret_cast<Sc32*>(b.bm) + o0;
   const uint8_t* mk = PRUNED ? mask + o0 : nullptr;
   int sidx[SPT];
   long long ebase[SPT];
@@ -670,8 +663,7 @@ __device__ __forceinline__ void beta_sum(
       const Sc u = fin ? sc_make(p.m, p.e) : Sc{0.0, ZERO_E};
       lm[s] = u.m;
       le[s] = u.e;
-      om[(long long)tl * Sn + s] = fin ? 0.5 : 0.0;
-      oe[(long long)tl * Sn + s] = fin ? 1 : ZERO_E;
+      om[(long long)tl * Sn + s] = fin ? Sc32{0.5f, 1} : Sc32{0.f, ZERO_E};
     }
   }
   lds_barrier();
@@ -714,9 +706,8 @@ __device__ __forceinline__ void beta_sum(
           cm[s] = v.m;
           ce[s] = v.e;
           // stored without the emission: the sum itself (not renormalised;
-          // at most 3 times a power of two)
-          om[(long long)t * Sn + s] = sum;
-          oe[(long long)t * Sn + s] = sum == 0.0 ? ZERO_E : emax;
+          // below 3 times a power of two)
+          om[(long long)t * Sn + s] = Sc32{(float)sum, sum == 0.0 ? ZERO_E : emax};
         }
       }
       lds_barrier();
@@ -863,9 +854,8 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
     int M, const int* __restrict__ row_off, const int* __restrict__ tgt_off,
     const int* __restrict__ tgt_rel, const int* __restrict__ utt_status,
     const double* __restrict__ utt_pm, const int* __restrict__ utt_pe,
-    const long long* __restrict__ dp_off, const double* __restrict__ am,
-    const int* __restrict__ ae, const double* __restrict__ bm, const int* __restrict__ be,
-    float* __restrict__ Gam, double* __restrict__ g, int Lcap) {
+    const long long* __restrict__ dp_off, const Sc32* __restrict__ am,
+    const Sc32* __restrict__ bm, float* __restrict__ Gam, double* __restrict__ g, int Lcap) {
   static_assert(OCC_THREADS % F == 0 && 64 % F == 0, "frames per round");
   extern __shared__ double sh[];
   constexpr int NW = OCC_THREADS / 64;
@@ -904,26 +894,37 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   lds_barrier();
   const double invP = 1.0 / utt_pm[n];
   const int Pe = utt_pe[n];
-  const double* Am = am + dp_off[n];
-  const int* Ae = ae + dp_off[n];
-  const double* Bm = bm + dp_off[n];
-  const int* Be = be + dp_off[n];
+  const Sc32* Ab = am + dp_off[n];
+  const Sc32* Bb = bm + dp_off[n];
   const int f = threadIdx.x % F;  // this thread's frame within a round
   for (int tb = t0; tb < t1; tb += F) {
     const int t = tb + f;
     const bool live = t < t1;
-    // q of (state, frame) pairs, state-major / frame-fastest
+    // q of (state, frame) pairs, state-major / frame-fastest; four states
+    // per thread at a time, their loads (of clamped, in-bounds nodes: a load
+    // under a per-lane condition is waited for on the spot) issued together
     double bl = 0.0, tot = 0.0;
-#pragma unroll 4
-    for (int s = threadIdx.x / F; s < Sn; s += OCC_THREADS / F) {
-      double q = 0.0;
-      if (live) {
-        const long long o = (long long)t * Sn + s;
-        q = ldexp(Am[o] * Bm[o] * invP, Ae[o] + Be[o] - Pe);
+    constexpr int SS = OCC_THREADS / F;  // state stride
+    const long long ro = (long long)(live ? t : t1 - 1) * Sn;
+    for (int s0 = threadIdx.x / F; s0 < Sn; s0 += 4 * SS) {
+      Sc32 a[4], bb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const long long o = ro + min(s0 + u * SS, Sn - 1);
+        a[u] = Ab[o];
+        bb[u] = Bb[o];
       }
-      s_q[s * F + f] = q;
-      tot += q;
-      if (!(s & 1)) bl += q;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u * SS;
+        if (s < Sn) {
+          const double q =
+              live ? ldexp((double)a[u].m * (double)bb[u].m * invP, a[u].e + bb[u].e - Pe) : 0.0;
+          s_q[s * F + f] = q;
+          tot += q;
+          if (!(s & 1)) bl += q;
+        }
+      }
     }
     // fixed-order sums per frame: a butterfly over the lanes of one frame
     // within each wavefront, then the wavefront sums in order
@@ -1031,8 +1032,8 @@ void dp_shape(int max_L, int& threads, int& spt) {
 
 hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int max_L,
                              const int* row_off, const int* tgt_off, const int* tgt_rel,
-                             const uint8_t* flags, const long long* dp_off, double* am, int* ae,
-                             double* bm, int* be, double* utt_loss, double* utt_logp,
+                             const uint8_t* flags, const long long* dp_off, double* am,
+                             double* bm, double* utt_loss, double* utt_logp,
                              double* utt_pm, int* utt_pe, int* utt_status, int mode,
                              const uint8_t* mask, double* best, int fwd_only) {
   if (N == 0) return hipSuccess;
@@ -1041,7 +1042,7 @@ hipError_t launch_alpha_beta(hipStream_t st, const float* S, int M, int N, int m
   // two frames of values: FP64 (and, for the sums, an int32 exponent each)
   const size_t shm = 2 * (size_t)spt * threads * (sizeof(double) + (mode == 2 ? 0 : sizeof(int)));
   const int grid = fwd_only ? N : 2 * N;
-  const DpBufs bufs{am, ae, bm, be, utt_loss, utt_logp, utt_pm, utt_pe, utt_status, best};
+  const DpBufs bufs{am, bm, utt_loss, utt_logp, utt_pm, utt_pe, utt_status, best};
 #define PCX_AB(SPT_, MODE_)                                                                  \
   k_alpha_beta<SPT_, MODE_><<<grid, threads, shm, st>>>(S, M, N, row_off, tgt_off, tgt_rel,  \
                                                         flags, dp_off, mask, bufs)
@@ -1084,8 +1085,8 @@ hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss, const 
 hipError_t launch_occupancy(hipStream_t st, int M, int N, int max_T, int max_L,
                             const int* row_off, const int* tgt_off, const int* tgt_rel,
                             const int* utt_status, const double* utt_pm, const int* utt_pe,
-                            const long long* dp_off, const double* am, const int* ae,
-                            const double* bm, const int* be, float* Gam, double* g) {
+                            const long long* dp_off, const double* am, const double* bm,
+                            float* Gam, double* g) {
   if (N == 0 || max_T <= 0) return hipSuccess;
   const int Lcap = max_L > 0 ? max_L : 1;
   // frames per round: the most whose q block leaves room for four
@@ -1099,7 +1100,9 @@ hipError_t launch_occupancy(hipStream_t st, int M, int N, int max_T, int max_L,
   dim3 grid(N, (max_T + OCC_FRAMES - 1) / OCC_FRAMES);
 #define PCX_OCC(FR)                                                                          \
   k_occupancy<FR><<<grid, OCC_THREADS, shm, st>>>(M, row_off, tgt_off, tgt_rel, utt_status,    \
-                                                  utt_pm, utt_pe, dp_off, am, ae, bm, be, Gam, g, \
+                                                  utt_pm, utt_pe, dp_off,                      \
+                                                  reinterpret_cast<const Sc32*>(am),           \
+                                                  reinterpret_cast<const Sc32*>(bm), Gam, g,   \
                                                   Lcap)
   switch (F) {
     case 8: PCX_OCC(8); break;

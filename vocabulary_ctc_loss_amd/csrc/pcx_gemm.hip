@@ -693,6 +693,9 @@ constexpr int SEL_DENSE = 8;
 // region beside the operand stages (the registers are taken by the
 // accumulators); with sixteen wavefronts (half the columns each) half of it.
 constexpr int SEL_PRE_BIG = 6;
+// Elements per thread whose loads the dense selected-class pass keeps in
+// flight together.
+constexpr int DENSE_ILP = 8;
 
 // Selected columns of one wavefront's tile block for the cooperative pass
 // (at most SEL_DENSE of them), in (fragment column, lane) order, with the S
@@ -757,7 +760,7 @@ __device__ __forceinline__ void sel_prefetch(SelPre<C>& p, const int* s_sel, int
 // fixed-order wave sum) goes to s_db_w[column].
 template <class C, typename T>
 __device__ __forceinline__ void sel_finish(const SelPre<C>& p, const double* s_g, int m0, int M,
-                                           int n0, int c0, double grad, T* __restrict__ dZ,
+                                           const int* s_col, double grad, T* __restrict__ dZ,
                                            int ldz, float* s_db_w) {
   const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / C::WGN;
 #pragma unroll
@@ -771,7 +774,7 @@ __device__ __forceinline__ void sel_finish(const SelPre<C>& p, const double* s_g
           // S <= 0 (a log-probability)
           const float dz =
               (float)(grad * (s_g[row] * exp_nonpos((double)p.s[k][t]) - (double)p.g[k][t]));
-          dZ[(long long)(m0 + row) * ldz + (n0 + p.col[k] - c0)] = Elem<T>::from_f32(dz);
+          dZ[(long long)(m0 + row) * ldz + s_col[p.col[k]]] = Elem<T>::from_f32(dz);
           sum += dz;
         }
       }
@@ -791,6 +794,13 @@ __device__ __forceinline__ void sel_finish(const SelPre<C>& p, const double* s_g
 // (g_m = sum_j gamma_j(m), zero on excluded rows).  The epilogue works on the
 // MFMA accumulators in place: dZ goes to the chunk block (row-major,
 // leading dimension ldz) and the tile's column sums to dbpart[mtile][col].
+//
+// cmap (optional): the tiles walk the chunk's columns in the order
+// cmap[0 .. c1 - c0) (the unselected classes first, see k_colperm; *nu of
+// them), so that the selected classes fill whole tiles, which need no
+// product and are left to k_dz_sel; the product of the other tiles reads
+// head rows from Wg, where row i holds the head row of column cmap[i].  Without cmap the tiles walk the columns in order and
+// read the head itself.
 template <class C>
 __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const typename C::type* __restrict__ X, const typename C::type* __restrict__ W,
@@ -799,7 +809,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     const double* __restrict__ g, const float* __restrict__ S, const float* __restrict__ Gam,
     double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
     int mtiles, int vec_ok, const double* __restrict__ gu, const float* __restrict__ lamu,
-    long long ldS) {
+    long long ldS, const int* __restrict__ cmap, const typename C::type* __restrict__ Wg,
+    const int* __restrict__ nu) {
   using T = typename C::type;
   constexpr int BM = C::BM, BN = C::BN;
   constexpr float LOG2E = 1.44269504088896340736f;
@@ -811,27 +822,47 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   __shared__ double s_g[BM];
   __shared__ float s_db[C::WGM][BN];
   __shared__ int s_list[BN], s_pos[BN], s_cnt[BN / 64];
+  __shared__ int s_col[BN];  // dZ column (within the chunk) of each tile column
   int mt, nt;
   grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
+  // in the unselected-first order the tiles of selected classes alone are
+  // k_dz_sel's
+  if (cmap != nullptr && n0 - c0 >= *nu) return;
+  // head rows of the product: the gathered rows (from row 0) or the head
+  const T* Bh = cmap != nullptr ? Wg : W;
+  const int nb0 = cmap != nullptr ? n0 - c0 : n0, nb1 = cmap != nullptr ? c1 - c0 : c1;
   // The product's first k stage is requested before the tile's row and
   // column data, so the two loads' latencies overlap.
   Prefetch<C, true, true> pf;
-  gemm_prefetch<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok);
-  // Row and column data of the tile.
+  gemm_prefetch<C, true, true>(pf, X, D, m0, M, Bh, D, nb0, nb1, 0, D, vec_ok, vec_ok);
+  // Row and column data of the tile.  The loads read clamped (in-bounds)
+  // places and frames unconditionally and the values past the tile's ends
+  // are masked afterwards, so that all of them are in flight together (a
+  // load under a per-lane condition is waited for on the spot).
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
-    s_sel[c] = v < c1 ? col2sel[v] : -1;
-    s_bias[c] = (bias != nullptr && v < c1) ? Elem<T>::to_f32(bias[v]) : 0.f;
+    const bool in = v < c1;
+    const int vc = in ? v : c1 - 1;
+    const int rv = cmap != nullptr ? cmap[vc - c0] : vc;
+    const int sl = col2sel[rv];
+    const float bv = bias != nullptr ? Elem<T>::to_f32(bias[rv]) : 0.f;
+    s_sel[c] = in ? sl : -1;
+    s_bias[c] = in ? bv : 0.f;
+    s_col[c] = rv - c0;
   }
   for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
     const int mm = m0 + rr;
-    const double gm = mm < M ? g[mm] : 0.0;
-    s_g[rr] = gm;
+    const bool in = mm < M;
+    const int mc = in ? mm : M - 1;
+    const double gv = g[mc];
+    const double guv = gu != nullptr ? gu[mc] : gv;
+    const float lv = lamu != nullptr ? lamu[mc] : lamf[mc];
+    s_g[rr] = in ? gv : 0.0;
     // unselected classes: dZ = rs * exp(z - shift); rs = grad g_m and shift =
     // lambda_m, or in the grouped form grad gu_m and the other column o_m
-    s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
-    s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
+    s_rs[rr] = in ? (float)(grad * guv) : 0.f;
+    s_lam2[rr] = in ? lv * LOG2E : 0.f;
   }
   lds_barrier();
   // A tile whose columns are all selected needs no recomputed logit (their
@@ -845,7 +876,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam, ldS);
   f32x16 acc[C::FM][C::FN];
   if (need_product) {
-    gemm_tile_run<C, true, true>(pf, X, D, m0, M, W, D, n0, c1, 0, D, vec_ok, vec_ok, acc,
+    gemm_tile_run<C, true, true>(pf, X, D, m0, M, Bh, D, nb0, nb1, 0, D, vec_ok, vec_ok, acc,
                                  smem);
   } else {
 #pragma unroll
@@ -861,13 +892,14 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   const bool dense = __syncthreads_or(pre.n > SEL_DENSE) != 0;
   // Unselected classes on the accumulators, four rows at a time; selected
   // classes (role 2) and columns past the chunk (role 3) are skipped here.
-  int csel[C::FN], crole[C::FN];
+  int csel[C::FN], crole[C::FN], ccol[C::FN];
   float cbv[C::FN], cs[C::FN];
 #pragma unroll
   for (int fj = 0; fj < C::FN; ++fj) {
     const int col = acc_col<C>(fj);
     csel[fj] = s_sel[col];
     cbv[fj] = s_bias[col];
+    ccol[fj] = s_col[col];
     crole[fj] = n0 + col < c1 ? (csel[fj] < 0 ? 0 : 2) : 3;
     cs[fj] = 0.f;
   }
@@ -889,7 +921,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
           const float dz = rs4[e] * __builtin_amdgcn_exp2f(
                                         fminf(fmaf(acc[fi][fj][4 * q + e] + cbv[fj], LOG2E, -l4[e]), 0.f));
           if (in && crole[fj] == 0) {
-            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
+            dZ[(long long)(m0 + row) * ldz + ccol[fj]] = Elem<T>::from_f32(dz);
             cs[fj] += dz;
           }
         }
@@ -930,15 +962,32 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     constexpr int CAP = C::STAGE_BYTES / (PADR * (int)sizeof(float));
     for (int k0 = 0; k0 < n_sel; k0 += CAP) {
       const int kn = min(CAP, n_sel - k0);
-      for (int idx = threadIdx.x; idx < kn * BM; idx += C::THREADS) {
-        const int kk = idx / BM, row = idx - kk * BM;
-        float dz = 0.f;
-        if (rows_full || m0 + row < M) {
-          const long long o = s_sel[s_list[k0 + kk]] * ldS + m0 + row;
-          // S <= 0 (a log-probability)
-          dz = (float)(grad * (s_g[row] * exp_nonpos((double)S[o]) - (double)Gam[o]));
+      const int total = kn * BM;
+      // DENSE_ILP elements per thread at a time: their S and Gamma loads (of
+      // clamped, in-bounds elements, masked afterwards) are all issued before
+      // the first is used
+      for (int base = threadIdx.x; base < total; base += DENSE_ILP * C::THREADS) {
+        float sv[DENSE_ILP], gv[DENSE_ILP];
+#pragma unroll
+        for (int u = 0; u < DENSE_ILP; ++u) {
+          const int idx = min(base + u * C::THREADS, total - 1);
+          const int kk = idx / BM, row = idx - kk * BM;
+          const long long o = (long long)s_sel[s_list[k0 + kk]] * ldS + min(m0 + row, M - 1);
+          sv[u] = S[o];
+          gv[u] = Gam[o];
         }
-        tmp[kk * PADR + row] = dz;
+#pragma unroll
+        for (int u = 0; u < DENSE_ILP; ++u) {
+          const int idx = base + u * C::THREADS;
+          if (idx < total) {
+            const int kk = idx / BM, row = idx - kk * BM;
+            // S <= 0 (a log-probability); rows past M give 0
+            tmp[kk * PADR + row] =
+                (rows_full || m0 + row < M)
+                    ? (float)(grad * (s_g[row] * exp_nonpos((double)sv[u]) - (double)gv[u]))
+                    : 0.f;
+          }
+        }
       }
       lds_barrier();
 #pragma unroll
@@ -952,7 +1001,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
             const int row = acc_row<C>(fi, r);
             if (rows_full || m0 + row < M) {
               const float dz = tmp[slot * PADR + row];
-              dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = Elem<T>::from_f32(dz);
+              dZ[(long long)(m0 + row) * ldz + ccol[fj]] = Elem<T>::from_f32(dz);
               cs[fj] += dz;
             }
           }
@@ -969,7 +1018,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   }
   // Few selected classes: each prefetched column of this wavefront by all 64
   // lanes (WM / 64 of the wavefront's rows each).
-  if (!dense) sel_finish<C, T>(pre, s_g, m0, M, n0, c0, grad, dZ, ldz, s_db[wm]);
+  if (!dense) sel_finish<C, T>(pre, s_g, m0, M, s_col, grad, dZ, ldz, s_db[wm]);
   lds_barrier();
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
@@ -977,7 +1026,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
       float t = s_db[0][c];
 #pragma unroll
       for (int q = 1; q < C::WGM; ++q) t += s_db[q][c];
-      dbpart[(long long)mt * ldz + (v - c0)] = t;
+      dbpart[(long long)mt * ldz + s_col[c]] = t;
     }
   }
 }
@@ -1991,34 +2040,207 @@ hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int
   return hipGetLastError();
 }
 
+// Logit gradient of the recompute tiles whose places are all selected
+// classes, in the unselected-first order (cmap, *nu): dZ = grad (g_m
+// exp(S[j][m]) - Gamma[j][m]) from S, Gamma and g alone, the formula of the
+// recompute's selected classes.  The tiles are the recompute's (BM frames x
+// BN places; the ones holding an unselected place return at once, the
+// recompute takes them), and each tile's column sums go to
+// dbpart[mtile][column], summed over its frames in order.  Per block of 64
+// places: each wavefront loads the class-major S and Gamma rows of 16 places
+// (unconditional loads of clamped frames, all issued before the first is
+// used), the values are transposed in LDS and written out as dZ rows.
+template <typename T, int BM, int BN>
+__global__ __launch_bounds__(256) void k_dz_sel(const int* __restrict__ col2sel, int c0, int c1,
+                                                const int* __restrict__ cmap,
+                                                const int* __restrict__ nu,
+                                                const double* __restrict__ g,
+                                                const float* __restrict__ S,
+                                                const float* __restrict__ Gam, long long ldS,
+                                                int M, double grad, T* __restrict__ dZ, int ldz,
+                                                float* __restrict__ dbpart, int mtiles) {
+  constexpr int CB = 64;       // places per block
+  constexpr int PW = CB / 4;   // places per wavefront
+  constexpr int RL = BM / 64;  // frames per lane
+  static_assert(BM % 64 == 0, "whole frames per lane");
+  __shared__ float s_dz[BM][CB + 1];
+  __shared__ double s_g[BM];
+  __shared__ int s_cls[CB], s_col[CB];
+  const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;
+  const int p0 = nt * BN;
+  if (p0 < *nu) return;
+  const int m0 = mt * BM;
+  const int np = min(BN, (c1 - c0) - p0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  for (int r = threadIdx.x; r < BM; r += 256) s_g[r] = m0 + r < M ? g[m0 + r] : 0.0;
+  for (int cb = 0; cb < np; cb += CB) {
+    const int nc = min(CB, np - cb);
+    if (threadIdx.x < CB) {
+      const bool in = (int)threadIdx.x < nc;
+      const int v = cmap[p0 + cb + (in ? (int)threadIdx.x : 0)];
+      const int cls = col2sel[v];
+      s_cls[threadIdx.x] = in ? cls : 0;
+      s_col[threadIdx.x] = v - c0;
+    }
+    __syncthreads();
+    float sv[PW][RL], gv[PW][RL];
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int c = w * PW + i;
+      const long long base = (long long)s_cls[c] * ldS;  // class 0 past nc
+#pragma unroll
+      for (int h = 0; h < RL; ++h) {
+        // clamped frames, loaded unconditionally (masked below)
+        const long long o = base + min(m0 + lane + 64 * h, M - 1);
+        sv[i][h] = S[o];
+        gv[i][h] = Gam[o];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < PW; ++i) {
+      const int c = w * PW + i;
+#pragma unroll
+      for (int h = 0; h < RL; ++h) {
+        const int r = lane + 64 * h;
+        // S <= 0 (a log-probability); rows past M give g = S = Gamma = 0
+        s_dz[r][c] = (c < nc && m0 + r < M)
+                         ? (float)(grad * (s_g[r] * exp_nonpos((double)sv[i][h]) - (double)gv[i][h]))
+                         : 0.f;
+      }
+    }
+    __syncthreads();
+    if (lane < nc)
+      for (int r = w; r < BM; r += 4)
+        if (m0 + r < M) dZ[(long long)(m0 + r) * ldz + s_col[lane]] = Elem<T>::from_f32(s_dz[r][lane]);
+    if ((int)threadIdx.x < nc) {
+      float t = 0.f;
+      for (int r = 0; r < BM; ++r) t += s_dz[r][threadIdx.x];
+      dbpart[(long long)mt * ldz + s_col[threadIdx.x]] = t;
+    }
+    __syncthreads();
+  }
+}
+
 template <typename T>
 hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void* b, int M, int D,
                        int c0, int c1, const int* col2sel, const float* lamf, const double* g,
                        const float* S, const float* Gam, double grad, void* dZ, int ldz,
-                       float* dbpart, const double* gu, const float* lamu, long long ldS) {
+                       float* dbpart, const double* gu, const float* lamu, long long ldS,
+                       const int* cmap, const void* Wg, const int* nu) {
   using C = typename Pick<T>::rec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
   if (grid == 0) return hipSuccess;
-  const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(W);
+  const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(cmap != nullptr ? Wg : W);
   k_recompute<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, c0, c1,
                                                col2sel, lamf, g, S, Gam, grad, (T*)dZ, ldz,
-                                               dbpart, mtiles, vec, gu, lamu, ldS);
+                                               dbpart, mtiles, vec, gu, lamu, ldS, cmap,
+                                               (const T*)Wg, nu);
+  if (cmap != nullptr)
+    k_dz_sel<T, C::BM, C::BN><<<grid, 256, 0, st>>>(col2sel, c0, c1, cmap, nu, g, S, Gam, ldS, M,
+                                                     grad, (T*)dZ, ldz, dbpart, mtiles);
   return hipGetLastError();
+}
+
+// Column order of the chunk [c0, c1) for the recompute: its unselected
+// columns (col2sel < 0) in ascending order, then its selected ones in
+// ascending order; cmap[i] is the column at place i and *nu the number of
+// unselected columns.  One work-group: a count pass, then a placement
+// pass over blocks of 1024 columns (wavefront ballots for the ranks).
+constexpr int PERM_THREADS = 1024;
+
+__global__ __launch_bounds__(PERM_THREADS) void k_colperm(const int* __restrict__ col2sel, int c0,
+                                                          int c1, int* __restrict__ cmap,
+                                                          int* __restrict__ nu) {
+  constexpr int NW = PERM_THREADS / 64;
+  __shared__ int s_w[NW];
+  __shared__ int s_total;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int cnt = 0;
+  for (int v = c0 + (int)threadIdx.x; v < c1; v += PERM_THREADS) cnt += col2sel[v] < 0;
+  for (int o = 32; o >= 1; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) s_w[w] = cnt;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int t = 0;
+    for (int q = 0; q < NW; ++q) t += s_w[q];
+    s_total = t;
+    *nu = t;
+  }
+  __syncthreads();
+  const int total_u = s_total;
+  int done_u = 0, done = 0;  // unselected / all columns of the blocks before
+  for (int b0 = c0; b0 < c1; b0 += PERM_THREADS) {
+    const int v = b0 + (int)threadIdx.x;
+    const bool in = v < c1;
+    const bool un = in && col2sel[v] < 0;
+    const unsigned long long bu = __ballot(un), bi = __ballot(in);
+    const unsigned long long below = (1ull << lane) - 1ull;
+    __syncthreads();  // s_w of the previous block has been read
+    if (lane == 0) s_w[w] = __popcll(bu);
+    __syncthreads();
+    int wu = 0, bu_all = 0;
+    for (int q = 0; q < NW; ++q) {
+      wu += q < w ? s_w[q] : 0;
+      bu_all += s_w[q];
+    }
+    const int ru = done_u + wu + __popcll(bu & below);         // rank among unselected
+    const int ri = done + w * 64 + __popcll(bi & below);       // rank among all
+    if (in) cmap[un ? ru : total_u + (ri - ru)] = v;
+    done_u += bu_all;
+    done += min(PERM_THREADS, c1 - b0);
+  }
+}
+
+// Wg[i][:] = W[cmap[i]][:] for the places i < round_up(*nu, tile)
+// (the rows any product tile reads; the remaining places are selected
+// columns of tiles without a product).  One work-group per place.
+template <typename T>
+__global__ __launch_bounds__(256) void k_gather_rows(const T* __restrict__ W, int D,
+                                                     const int* __restrict__ cmap,
+                                                     const int* __restrict__ nu, int tile,
+                                                     T* __restrict__ Wg) {
+  const int i = blockIdx.x;
+  const int lim = (*nu + tile - 1) / tile * tile;
+  if (i >= lim) return;
+  const T* src = W + (long long)cmap[i] * D;
+  T* dst = Wg + (long long)i * D;
+  for (int d = threadIdx.x; d < D; d += 256) dst[d] = src[d];
+}
+
+hipError_t launch_colperm(hipStream_t st, int dtype, const int* col2sel, int c0, int c1,
+                          const void* W, int D, int* cmap, int* nu, void* Wg) {
+  const int n = c1 - c0;
+  if (n <= 0) return hipSuccess;
+  k_colperm<<<1, PERM_THREADS, 0, st>>>(col2sel, c0, c1, cmap, nu);
+  if (dtype == 0)
+    k_gather_rows<float><<<n, 256, 0, st>>>((const float*)W, D, cmap, nu,
+                                            Pick<float>::rec::BN, (float*)Wg);
+  else
+    k_gather_rows<bf16_t><<<n, 256, 0, st>>>((const bf16_t*)W, D, cmap, nu,
+                                             Pick<bf16_t>::rec::BN, (bf16_t*)Wg);
+  return hipGetLastError();
+}
+
+int rec_tile_cols(int dtype) {
+  return dtype == 0 ? Pick<float>::rec::BN : Pick<bf16_t>::rec::BN;
 }
 
 hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W, const void* b,
                             int M, int D, int c0, int c1, const int* col2sel, const float* lamf,
                             const double* g, const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart, int big, const double* gu,
-                            const float* lamu, long long ldS) {
+                            const float* lamu, long long ldS, const int* cmap, const void* Wg,
+                            const int* nu) {
   if (ldS <= 0) ldS = M;
+  if ((cmap == nullptr) != (nu == nullptr)) return hipErrorInvalidValue;
   if (dtype == 0)
     return recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ, ldz,
-                              dbpart, gu, lamu, ldS);
+                              dbpart, gu, lamu, ldS, cmap, Wg, nu);
   if (!big)
     return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
-                               ldz, dbpart, gu, lamu, ldS);
+                               ldz, dbpart, gu, lamu, ldS, cmap, Wg, nu);
+  if (cmap != nullptr) return hipErrorInvalidValue;  // the 256 x 256 core walks columns in order
   using C = CfgBigRec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
