@@ -200,6 +200,22 @@ class Run:
                   stream=self.stream)
         c.backward(1.0, self.dX, self.dW, self.db, stream=self.stream)
 
+    def step_times(self, steps, warmup):
+        """Per-step times (ms) of `steps` steps after `warmup` untimed ones,
+        one event pair around each step, nothing else timed."""
+        import torch
+        for _ in range(warmup):
+            self.step()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        torch.cuda.synchronize()
+        for a, e in evs:
+            a.record(self.stream)
+            self.step()
+            e.record(self.stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(e) for a, e in evs]
+
     def measure(self, steps, warmup, beam=math.inf):
         """Warm-up, one untimed profiled step (per-family breakdown, dominant
         family), then `steps` timed steps with only the dominant family's
@@ -332,6 +348,14 @@ def main():
                                    if k in ("ctc_viterbi", "beam_mask", DP_KERNEL,
                                             "occupancy")},
                        "hbm_passes": rb["hbm_passes"]}
+        # the pages' timing protocol: 3 runs of 5 warm-up and 50 measured
+        # steps, the mean of the three run medians
+        head.ctx.set_beam(math.inf)
+        meds = [float(np.median(head.step_times(50, 5))) for _ in range(3)]
+        out["protocol_3x50"] = {"runs": 3, "warmup": 5, "measured": 50,
+                                "run_medians_ms": meds,
+                                "mean_of_medians_ms": float(np.mean(meds)),
+                                "frames_per_s": bt.M / (float(np.mean(meds)) / 1e3)}
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(bt, args.cpu_sample_utts)
     head.close()

@@ -848,6 +848,7 @@ __global__ __launch_bounds__(MASK_TS) void k_beam_mask(
 // frame-fastest: thread k always handles frame k mod F of a round, and a
 // class's Gamma stores for the F frames are contiguous.
 constexpr int OCC_THREADS = 256;
+constexpr int OCC_UNROLL = 8;  // states per thread whose loads are in flight together
 
 template <int F>
 __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
@@ -900,22 +901,23 @@ __global__ __launch_bounds__(OCC_THREADS) void k_occupancy(
   for (int tb = t0; tb < t1; tb += F) {
     const int t = tb + f;
     const bool live = t < t1;
-    // q of (state, frame) pairs, state-major / frame-fastest; four states
-    // per thread at a time, their loads (of clamped, in-bounds nodes: a load
-    // under a per-lane condition is waited for on the spot) issued together
+    // q of (state, frame) pairs, state-major / frame-fastest; OCC_UNROLL
+    // states per thread at a time, their loads (of clamped, in-bounds nodes:
+    // a load under a per-lane condition is waited for on the spot) issued
+    // together
     double bl = 0.0, tot = 0.0;
     constexpr int SS = OCC_THREADS / F;  // state stride
     const long long ro = (long long)(live ? t : t1 - 1) * Sn;
-    for (int s0 = threadIdx.x / F; s0 < Sn; s0 += 4 * SS) {
-      Sc32 a[4], bb[4];
+    for (int s0 = threadIdx.x / F; s0 < Sn; s0 += OCC_UNROLL * SS) {
+      Sc32 a[OCC_UNROLL], bb[OCC_UNROLL];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < OCC_UNROLL; ++u) {
         const long long o = ro + min(s0 + u * SS, Sn - 1);
         a[u] = Ab[o];
         bb[u] = Bb[o];
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < OCC_UNROLL; ++u) {
         const int s = s0 + u * SS;
         if (s < Sn) {
           const double q =

@@ -1484,12 +1484,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
     run_s[fj] = 0.0;
   }
   // the first tile's row data; later tiles' are loaded during the tile before
+  // (unconditional loads of a clamped id, masked afterwards: a load under a
+  // per-lane condition is waited for on the spot)
   int nsel = -2;
   float nbias = 0.f;
   if (threadIdx.x < C::BM) {
     const int v = c_begin + threadIdx.x;
-    nsel = v < c_end ? col2sel[v] : -2;  // -2: past the span
-    nbias = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+    const int vc = min(v, c_end - 1);
+    const int sl = col2sel[vc];
+    const float bv = bias != nullptr ? bf16_to_f32(bias[vc]) : 0.f;
+    nsel = v < c_end ? sl : -2;  // -2: past the span
+    nbias = v < c_end ? bv : 0.f;
   }
   BigPipe pipe;
   int par = 0;
@@ -1501,12 +1506,21 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
       s_bias[par][threadIdx.x] = nbias;
     }
     const BigNext next{v0 + C::BM < c_end, v0 + C::BM, c_end, f0, M};
+    // the next tile's row data is requested before this tile's product and
+    // used after it, so its latency hides behind the product
+    int psel = 0;
+    float pbias = 0.f;
+    const int vn = v0 + C::BM + (int)threadIdx.x;
+    if (next.valid && threadIdx.x < C::BM) {
+      const int vc = min(vn, c_end - 1);
+      psel = col2sel[vc];
+      pbias = bias != nullptr ? bf16_to_f32(bias[vc]) : 0.f;
+    }
     f32x16 acc[C::FM][C::FN];
     gemm_big<C>(W, D, v0, c_end, X, D, f0, M, D, acc, smem, pipe, next);
     if (next.valid && threadIdx.x < C::BM) {
-      const int v = v0 + C::BM + threadIdx.x;
-      nsel = v < c_end ? col2sel[v] : -2;
-      nbias = (bias != nullptr && v < c_end) ? bf16_to_f32(bias[v]) : 0.f;
+      nsel = vn < c_end ? psel : -2;
+      nbias = vn < c_end ? pbias : 0.f;
     }
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
@@ -1613,19 +1627,30 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   grouped_tile<4>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
   const int c_pad = c0 + ((c1 - c0 + 63) & ~63);
+  // Row and column data: unconditional loads of clamped (in-bounds) entries,
+  // masked afterwards, so that they are in flight together (a load under a
+  // per-lane condition is waited for on the spot).
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
-    s_sel[c] = v < c1 ? col2sel[v] : -1;
-    s_bias[c] = (bias != nullptr && v < c1) ? bf16_to_f32(bias[v]) : 0.f;
+    const bool in = v < c1;
+    const int vc = in ? v : c1 - 1;
+    const int sl = col2sel[vc];
+    const float bv = bias != nullptr ? bf16_to_f32(bias[vc]) : 0.f;
+    s_sel[c] = in ? sl : -1;
+    s_bias[c] = in ? bv : 0.f;
   }
   for (int rr = threadIdx.x; rr < BM; rr += C::THREADS) {
     const int mm = m0 + rr;
-    const double gm = mm < M ? g[mm] : 0.0;
-    s_g[rr] = gm;
+    const bool in = mm < M;
+    const int mc = in ? mm : M - 1;
+    const double gv = g[mc];
+    const double guv = gu != nullptr ? gu[mc] : gv;
+    const float lv = lamu != nullptr ? lamu[mc] : lamf[mc];
+    s_g[rr] = in ? gv : 0.0;
     // unselected classes: dZ = rs * exp(z - shift); rs = grad g_m and shift =
     // lambda_m, or in the grouped form grad gu_m and the other column o_m
-    s_rs[rr] = (float)(grad * (gu != nullptr ? (mm < M ? gu[mm] : 0.0) : gm));
-    s_lam2[rr] = mm < M ? (lamu != nullptr ? lamu[mm] : lamf[mm]) * LOG2E : 0.f;
+    s_rs[rr] = in ? (float)(grad * guv) : 0.f;
+    s_lam2[rr] = in ? lv * LOG2E : 0.f;
   }
   lds_barrier();
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
