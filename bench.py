@@ -53,10 +53,12 @@ KERNEL_SRC = {"fwd_gemm_lse": GEMM_SRC, "bwd_recompute_dz": GEMM_SRC, "dx_gemm":
 # Kernel families whose work is a slice of the head GEMMs: FLOPs per step.
 GEMM_KERNELS = ("fwd_gemm_lse", "bwd_recompute_dz", "dx_gemm", "dw_gemm")
 # The CTC recursions: per (frame, extended-label state) each writes its value
-# (alpha, beta: 2 x 8 B, an fp32 mantissa and an int32 exponent) and reads
-# one fp32 emission (2 x 4 B).
+# (alpha, beta: 2 x 8 B, an fp32 mantissa and an int32 exponent); per (frame,
+# distinct class of the utterance, blank included) each reads the fp32
+# emission once (2 x 4 B: the states of one class share it).
 DP_KERNEL = "ctc_alpha_beta"
-DP_BYTES_PER_STATE = 24
+DP_BYTES_PER_STATE = 16
+DP_BYTES_PER_CLASS = 8
 
 
 # Memory-bound passes beside the GEMMs, with their algorithmic bytes per step:
@@ -71,21 +73,22 @@ DP_BYTES_PER_STATE = 24
 #                   included), g written (8 B/frame);
 #   ctc_viterbi     as ctc_alpha_beta (best prefix / suffix scores);
 #   beam_mask       the two best-score tables read (16 B/state), the emission
-#                   (4 B/state), the arc mask written (1 B/state).
+#                   (4 B per frame and class), the arc mask written (1 B/state).
 def pass_bytes(bt, K, nspan, pruned=False):
     L = np.diff(bt.tgt_off).astype(np.int64)
     states = int(np.sum(bt.frame_counts.astype(np.int64) * (2 * L + 1)))
     classes = sum(int(t) * (len(np.unique(bt.tgt[bt.tgt_off[n]:bt.tgt_off[n + 1]])) + 1)
                   for n, t in enumerate(bt.frame_counts))
     out = {
-        DP_KERNEL: (DP_BYTES_PER_STATE + (2 if pruned else 0)) * states,
+        DP_KERNEL: (DP_BYTES_PER_STATE + (2 if pruned else 0)) * states
+                   + DP_BYTES_PER_CLASS * classes,
         "lambda": bt.M * (16 * nspan + 12),
         "scores": bt.M * (8 * K + 8),
         "occupancy": 16 * states + 4 * classes + 8 * bt.M,
     }
     if pruned:
-        out["ctc_viterbi"] = DP_BYTES_PER_STATE * states
-        out["beam_mask"] = 21 * states
+        out["ctc_viterbi"] = DP_BYTES_PER_STATE * states + DP_BYTES_PER_CLASS * classes
+        out["beam_mask"] = 17 * states + 4 * classes
     return out
 
 
