@@ -1054,14 +1054,26 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dx(
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
       const int col = n0 + acc_col<C>(fj);
+      float old[16];
+      if (!first) {
+        // the fragment's 16 accumulator values are loaded together (clamped,
+        // in-bounds addresses; a load under a per-lane condition is waited
+        // for on the spot), then updated
+        const int cc = min(col, D - 1);
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          const int row = min(m0 + acc_row<C>(fi, rr), M - 1);
+          old[rr] = dXacc[(long long)row * D + cc];
+        }
+      } else {
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) old[rr] = 0.f;
+      }
       if (col >= D) continue;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const int row = m0 + acc_row<C>(fi, rr);
-        if (row < M) {
-          float* p = dXacc + (long long)row * D + col;
-          *p = first ? acc[fi][fj][rr] : *p + acc[fi][fj][rr];
-        }
+        if (row < M) dXacc[(long long)row * D + col] = first ? acc[fi][fj][rr] : old[rr] + acc[fi][fj][rr];
       }
     }
 }
