@@ -17,8 +17,9 @@
 // from s-2 when s is a label different from the label two states back.  One
 // work-group owns one utterance; each thread owns up to SPT states and the
 // previous frame's values live in LDS (double-buffered, one barrier per
-// frame).  Emission scores for the next 8 frames are prefetched into
-// registers while the current 8 are processed.
+// frame).  Emission scores for the next 8 frames (4 with two states per
+// thread, 2 with four) are prefetched into registers while the current ones
+// are processed.
 #include <math.h>
 
 #include "pcx_common.h"
@@ -190,6 +191,40 @@ struct DpBufs {
 constexpr int ARC_IN_STAY = 1, ARC_IN_ADV = 2, ARC_IN_SKIP = 4;
 constexpr int ARC_OUT_STAY = 8, ARC_OUT_ADV = 16, ARC_OUT_SKIP = 32;
 
+// Emission (and arc-mask byte) of a state at frame t for the first block of
+// prefetch registers: a clamped, in-bounds frame and state are loaded
+// unconditionally and the value is masked afterwards (a load under a
+// per-lane condition is waited for on the spot, which had serialized these
+// loads).  States past Sn read class 0's row of S.
+template <bool MASK>
+__device__ __forceinline__ void dp_fetch(const float* __restrict__ S, long long ebase,
+                                         const uint8_t* __restrict__ mk, int t, int T, int s,
+                                         int Sn, float& e, int& m) {
+  const bool in = s < Sn && t >= 0 && t < T;
+  const int tc = min(max(t, 0), T - 1);
+  const float ev = S[ebase + tc];
+  e = in ? ev : 0.f;
+  if (MASK) {
+    const int mv = mk[(long long)tc * Sn + min(s, Sn - 1)];
+    m = in ? mv : 0;
+  } else {
+    m = 0;
+  }
+}
+
+// The same for the prefetch inside the frame loop, as conditional loads:
+// there they are issued a block of frames ahead and waited for only at the
+// block's end (with unconditional loads the compiler placed their waits
+// inside the frame steps, measured 15% slower).
+template <bool MASK>
+__device__ __forceinline__ void dp_fetch_next(const float* __restrict__ S, long long ebase,
+                                              const uint8_t* __restrict__ mk, int t, int T, int s,
+                                              int Sn, float& e, int& m) {
+  const bool in = s < Sn && t >= 0 && t < T;
+  e = in ? S[ebase + t] : 0.f;
+  m = (MASK && in) ? mk[(long long)t * Sn + s] : 0;
+}
+
 __device__ __forceinline__ double max3(double a, double b, double c) {
   return fmax(a, fmax(b, c));
 }
@@ -204,6 +239,9 @@ __device__ __forceinline__ void alpha_utt(
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     const uint8_t* __restrict__ mask, double* __restrict__ alpha, double* __restrict__ utt_loss,
     double* __restrict__ utt_logp, int* __restrict__ utt_status, double* __restrict__ best) {
+  // frames per prefetch block: fewer with more states per thread, so the
+  // prefetch registers fit beside the states'
+  constexpr int PFS = SPT >= 4 ? 2 : (SPT == 2 ? 4 : PF);
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   if (!flags[n]) {
@@ -239,15 +277,13 @@ __device__ __forceinline__ void alpha_utt(
     skip[j] = sk;
     ebase[j] = (long long)cls * M + row0;
   }
-  float ecur[SPT][PF], enxt[SPT][PF];
-  int mcur[SPT][PF], mnxt[SPT][PF];
+  float ecur[SPT][PFS], enxt[SPT][PFS];
+  int mcur[SPT][PFS], mnxt[SPT][PFS];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const bool in = sidx[j] < Sn && u < T;
-      ecur[j][u] = in ? S[ebase[j] + u] : 0.f;
-      mcur[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)u * Sn + sidx[j]] : 0;
+    for (int u = 0; u < PFS; ++u) {
+      dp_fetch<MODE == DP_PRUNED>(S, ebase[j], mk, u, T, sidx[j], Sn, ecur[j][u], mcur[j][u]);
     }
   // frame 0: only the first blank and the first label can start (pruned:
   // if their initial arcs are kept).
@@ -262,20 +298,18 @@ __device__ __forceinline__ void alpha_utt(
     }
   }
   lds_barrier();
-  for (int tb = 0; tb < T; tb += PF) {
-    if (tb + PF < T) {
+  for (int tb = 0; tb < T; tb += PFS) {
+    if (tb + PFS < T) {
 #pragma unroll
       for (int j = 0; j < SPT; ++j)
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          const int t = tb + PF + u;
-          const bool in = sidx[j] < Sn && t < T;
-          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
-          mnxt[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        for (int u = 0; u < PFS; ++u) {
+          const int t = tb + PFS + u;
+          dp_fetch_next<MODE == DP_PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, enxt[j][u], mnxt[j][u]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = tb + u;
       if (t >= T) break;
       if (t == 0) continue;
@@ -305,7 +339,7 @@ __device__ __forceinline__ void alpha_utt(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
+      for (int u = 0; u < PFS; ++u) {
         ecur[j][u] = enxt[j][u];
         mcur[j][u] = mnxt[j][u];
       }
@@ -345,6 +379,9 @@ __device__ __forceinline__ void beta_utt(
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     const uint8_t* __restrict__ mask, double* __restrict__ beta) {
+  // frames per prefetch block: fewer with more states per thread, so the
+  // prefetch registers fit beside the states'
+  constexpr int PFS = SPT >= 4 ? 2 : (SPT == 2 ? 4 : PF);
   if (!flags[n]) return;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
@@ -369,17 +406,15 @@ __device__ __forceinline__ void beta_utt(
     skip[j] = sk;
     ebase[j] = (long long)cls * M + row0;
   }
-  // Frames are visited downwards; block b covers frames T-1-b*PF-u, u < PF.
-  float ecur[SPT][PF], enxt[SPT][PF];
-  int mcur[SPT][PF], mnxt[SPT][PF];
+  // Frames are visited downwards; block b covers frames T-1-b*PFS-u, u < PFS.
+  float ecur[SPT][PFS], enxt[SPT][PFS];
+  int mcur[SPT][PFS], mnxt[SPT][PFS];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = T - 1 - u;
-      const bool in = sidx[j] < Sn && t >= 0;
-      ecur[j][u] = in ? S[ebase[j] + t] : 0.f;
-      mcur[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+      dp_fetch<MODE == DP_PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, ecur[j][u], mcur[j][u]);
     }
   const int tl = T - 1;
   double* lastbuf = (tl & 1) ? buf1 : buf0;
@@ -394,20 +429,18 @@ __device__ __forceinline__ void beta_utt(
     }
   }
   lds_barrier();
-  for (int tb = 0; tb < T; tb += PF) {
-    if (tb + PF < T) {
+  for (int tb = 0; tb < T; tb += PFS) {
+    if (tb + PFS < T) {
 #pragma unroll
       for (int j = 0; j < SPT; ++j)
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          const int t = T - 1 - (tb + PF + u);
-          const bool in = sidx[j] < Sn && t >= 0;
-          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
-          mnxt[j][u] = (MODE == DP_PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        for (int u = 0; u < PFS; ++u) {
+          const int t = T - 1 - (tb + PFS + u);
+          dp_fetch_next<MODE == DP_PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, enxt[j][u], mnxt[j][u]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = T - 1 - (tb + u);
       if (t < 0) break;
       if (t == T - 1) continue;
@@ -442,7 +475,7 @@ __device__ __forceinline__ void beta_utt(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
+      for (int u = 0; u < PFS; ++u) {
         ecur[j][u] = enxt[j][u];
         mcur[j][u] = mnxt[j][u];
       }
@@ -458,6 +491,9 @@ __device__ __forceinline__ void alpha_sum(
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     const uint8_t* __restrict__ mask, const DpBufs& b) {
+  // frames per prefetch block: fewer with more states per thread, so the
+  // prefetch registers fit beside the states'
+  constexpr int PFS = SPT >= 4 ? 2 : (SPT == 2 ? 4 : PF);
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
   if (!flags[n]) {
@@ -494,15 +530,13 @@ __device__ __forceinline__ void alpha_sum(
     skip[j] = sk;
     ebase[j] = (long long)cls * M + row0;
   }
-  float ecur[SPT][PF], enxt[SPT][PF];
-  int mcur[SPT][PF], mnxt[SPT][PF];
+  float ecur[SPT][PFS], enxt[SPT][PFS];
+  int mcur[SPT][PFS], mnxt[SPT][PFS];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const bool in = sidx[j] < Sn && u < T;
-      ecur[j][u] = in ? S[ebase[j] + u] : 0.f;
-      mcur[j][u] = (PRUNED && in) ? mk[(long long)u * Sn + sidx[j]] : 0;
+    for (int u = 0; u < PFS; ++u) {
+      dp_fetch<PRUNED>(S, ebase[j], mk, u, T, sidx[j], Sn, ecur[j][u], mcur[j][u]);
     }
   // frame 0: only the first blank and the first label can start (pruned:
   // if their initial arcs are kept).
@@ -522,20 +556,18 @@ __device__ __forceinline__ void alpha_sum(
     }
   }
   lds_barrier();
-  for (int tb = 0; tb < T; tb += PF) {
-    if (tb + PF < T) {
+  for (int tb = 0; tb < T; tb += PFS) {
+    if (tb + PFS < T) {
 #pragma unroll
       for (int j = 0; j < SPT; ++j)
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          const int t = tb + PF + u;
-          const bool in = sidx[j] < Sn && t < T;
-          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
-          mnxt[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        for (int u = 0; u < PFS; ++u) {
+          const int t = tb + PFS + u;
+          dp_fetch_next<PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, enxt[j][u], mnxt[j][u]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = tb + u;
       if (t >= T) break;
       if (t == 0) continue;
@@ -569,7 +601,7 @@ __device__ __forceinline__ void alpha_sum(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
+      for (int u = 0; u < PFS; ++u) {
         ecur[j][u] = enxt[j][u];
         mcur[j][u] = mnxt[j][u];
       }
@@ -611,6 +643,9 @@ __device__ __forceinline__ void beta_sum(
     const int* __restrict__ tgt_off, const int* __restrict__ tgt_rel,
     const uint8_t* __restrict__ flags, const long long* __restrict__ dp_off,
     const uint8_t* __restrict__ mask, const DpBufs& b) {
+  // frames per prefetch block: fewer with more states per thread, so the
+  // prefetch registers fit beside the states'
+  constexpr int PFS = SPT >= 4 ? 2 : (SPT == 2 ? 4 : PF);
   if (!flags[n]) return;
   const int row0 = row_off[n], T = row_off[n + 1] - row0;
   const int y0 = tgt_off[n], L = tgt_off[n + 1] - y0, Sn = 2 * L + 1;
@@ -638,17 +673,15 @@ __device__ __forceinline__ void beta_sum(
     skip[j] = sk;
     ebase[j] = (long long)cls * M + row0;
   }
-  // Frames are visited downwards; block b covers frames T-1-b*PF-u, u < PF.
-  float ecur[SPT][PF], enxt[SPT][PF];
-  int mcur[SPT][PF], mnxt[SPT][PF];
+  // Frames are visited downwards; block b covers frames T-1-b*PFS-u, u < PFS.
+  float ecur[SPT][PFS], enxt[SPT][PFS];
+  int mcur[SPT][PFS], mnxt[SPT][PFS];
 #pragma unroll
   for (int j = 0; j < SPT; ++j)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = T - 1 - u;
-      const bool in = sidx[j] < Sn && t >= 0;
-      ecur[j][u] = in ? S[ebase[j] + t] : 0.f;
-      mcur[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+      dp_fetch<PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, ecur[j][u], mcur[j][u]);
     }
   const int tl = T - 1;
   double* lm = (tl & 1) ? mb1 : mb0;
@@ -667,20 +700,18 @@ __device__ __forceinline__ void beta_sum(
     }
   }
   lds_barrier();
-  for (int tb = 0; tb < T; tb += PF) {
-    if (tb + PF < T) {
+  for (int tb = 0; tb < T; tb += PFS) {
+    if (tb + PFS < T) {
 #pragma unroll
       for (int j = 0; j < SPT; ++j)
 #pragma unroll
-        for (int u = 0; u < PF; ++u) {
-          const int t = T - 1 - (tb + PF + u);
-          const bool in = sidx[j] < Sn && t >= 0;
-          enxt[j][u] = in ? S[ebase[j] + t] : 0.f;
-          mnxt[j][u] = (PRUNED && in) ? mk[(long long)t * Sn + sidx[j]] : 0;
+        for (int u = 0; u < PFS; ++u) {
+          const int t = T - 1 - (tb + PFS + u);
+          dp_fetch_next<PRUNED>(S, ebase[j], mk, t, T, sidx[j], Sn, enxt[j][u], mnxt[j][u]);
         }
     }
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
+    for (int u = 0; u < PFS; ++u) {
       const int t = T - 1 - (tb + u);
       if (t < 0) break;
       if (t == T - 1) continue;
@@ -715,7 +746,7 @@ __device__ __forceinline__ void beta_sum(
 #pragma unroll
     for (int j = 0; j < SPT; ++j)
 #pragma unroll
-      for (int u = 0; u < PF; ++u) {
+      for (int u = 0; u < PFS; ++u) {
         ecur[j][u] = enxt[j][u];
         mcur[j][u] = mnxt[j][u];
       }
