@@ -1017,23 +1017,44 @@ __global__ __launch_bounds__(256) void k_blank_grad(const float* __restrict__ S,
   if (threadIdx.x == 0) *out = grad * part[0];
 }
 
-__global__ void k_loss_sum(int N, const double* __restrict__ utt_loss,
-                           const int* __restrict__ utt_status, Meta* __restrict__ meta) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+// Sum of the included utterances' losses and the counts of excluded ones.
+// One work-group: thread i takes utterances i, i + 256, ... in order (both
+// loads issued unconditionally), then a fixed-order tree over the threads,
+// so the result does not depend on timing.
+constexpr int LOSS_THREADS = 256;
+
+__global__ __launch_bounds__(LOSS_THREADS) void k_loss_sum(int N,
+                                                           const double* __restrict__ utt_loss,
+                                                           const int* __restrict__ utt_status,
+                                                           Meta* __restrict__ meta) {
+  __shared__ double s_tot[LOSS_THREADS];
+  __shared__ int s_nu[LOSS_THREADS], s_nf[LOSS_THREADS];
   double tot = 0.0;
   int nu = 0, nf = 0;
-  for (int n = 0; n < N; ++n) {
+  for (int n = threadIdx.x; n < N; n += LOSS_THREADS) {
     const int st = utt_status[n];
-    if (st == UTT_OK)
-      tot += utt_loss[n];
-    else if (st == UTT_UNALIGNABLE)
-      ++nu;
-    else
-      ++nf;
+    const double l = utt_loss[n];
+    tot += st == UTT_OK ? l : 0.0;
+    nu += st == UTT_UNALIGNABLE;
+    nf += st != UTT_OK && st != UTT_UNALIGNABLE;
   }
-  meta->loss = tot;
-  meta->n_unalignable = nu;
-  meta->n_nonfinite = nf;
+  s_tot[threadIdx.x] = tot;
+  s_nu[threadIdx.x] = nu;
+  s_nf[threadIdx.x] = nf;
+  __syncthreads();
+  for (int w = LOSS_THREADS / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      s_tot[threadIdx.x] += s_tot[threadIdx.x + w];
+      s_nu[threadIdx.x] += s_nu[threadIdx.x + w];
+      s_nf[threadIdx.x] += s_nf[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    meta->loss = s_tot[0];
+    meta->n_unalignable = s_nu[0];
+    meta->n_nonfinite = s_nf[0];
+  }
 }
 
 __global__ void k_fill_f32(float* __restrict__ p, long long n, float v) {
@@ -1111,7 +1132,7 @@ hipError_t launch_beam_mask(hipStream_t st, const float* S, int M, int N, long l
 
 hipError_t launch_loss_sum(hipStream_t st, int N, const double* utt_loss, const int* utt_status,
                            Meta* meta) {
-  k_loss_sum<<<1, 64, 0, st>>>(N, utt_loss, utt_status, meta);
+  k_loss_sum<<<1, LOSS_THREADS, 0, st>>>(N, utt_loss, utt_status, meta);
   return hipGetLastError();
 }
 

@@ -64,7 +64,20 @@ __global__ __launch_bounds__(1024) void k_prepare_utts(
     const bool ok = a >= 0 && e >= a && (long long)e <= L_tot;
     int r = 0;
     if (ok)
-      for (int i = a + lane; i + 1 < e; i += 64) r += (tgt[i] == tgt[i + 1]);
+      // four label pairs per lane at a time, loaded unconditionally from
+      // clamped positions (a load under a per-lane condition is waited for on
+      // the spot) and counted when in range
+      for (int i0 = a; i0 + 1 < e; i0 += 4 * 64) {
+        int x[4], y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int ic = min(i0 + lane + 64 * u, e - 2);
+          x[u] = tgt[ic];
+          y[u] = tgt[ic + 1];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) r += (i0 + lane + 64 * u + 1 < e) && x[u] == y[u];
+      }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) r += __shfl_xor(r, o, 64);
     if (lane == 0) {
@@ -140,33 +153,49 @@ __global__ __launch_bounds__(1024) void k_select(int V, int blank, int* __restri
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int per = ((V + nw - 1) / nw + 63) / 64 * 64;
   const int lo = min(V, wid * per), hi = min(V, lo + per);
+  // SEL_BATCH blocks of 64 ids at a time: their marks are loaded together
+  // (clamped ids, loaded unconditionally: a load under a per-lane condition is
+  // waited for on the spot), then counted or placed in id order.
+  constexpr int SEL_BATCH = 8;
   int cnt = 0;  // marked ids of this wavefront's range (wave-uniform)
-  for (int v0 = lo; v0 < hi; v0 += 64) {
-    const int v = v0 + lane;
-    cnt += __popcll(__ballot(v < hi && v != blank && col2sel[v] != 0));
+  for (int v0 = lo; v0 < hi; v0 += SEL_BATCH * 64) {
+    int mk[SEL_BATCH];
+#pragma unroll
+    for (int u = 0; u < SEL_BATCH; ++u) mk[u] = col2sel[min(v0 + 64 * u + lane, V - 1)];
+#pragma unroll
+    for (int u = 0; u < SEL_BATCH; ++u) {
+      const int v = v0 + 64 * u + lane;
+      cnt += __popcll(__ballot(v < hi && v != blank && mk[u] != 0));
+    }
   }
   long long tot;
   // lane 0 carries the wavefront's count: its exclusive prefix is the number
   // of marked ids in the ranges of the lower wavefronts
   const long long ex = block_exclusive_scan(lane == 0 ? cnt : 0, &tot, sm);
   int idx = 1 + (int)__shfl(ex, 0, 64);
-  for (int v0 = lo; v0 < hi; v0 += 64) {
-    const int v = v0 + lane;
-    const bool in = v < hi;
-    const bool sel = in && v != blank && col2sel[v] != 0;
-    const unsigned long long bal = __ballot(sel);
-    const int pos = idx + __popcll(bal & ((1ull << lane) - 1ull));
-    if (in) {
-      if (v == blank) {
-        col2sel[v] = 0;
-      } else if (sel) {
-        col2sel[v] = pos;
-        U[pos] = v;
-      } else {
-        col2sel[v] = -1;
+  for (int v0 = lo; v0 < hi; v0 += SEL_BATCH * 64) {
+    int mk[SEL_BATCH];
+#pragma unroll
+    for (int u = 0; u < SEL_BATCH; ++u) mk[u] = col2sel[min(v0 + 64 * u + lane, V - 1)];
+#pragma unroll
+    for (int u = 0; u < SEL_BATCH; ++u) {
+      const int v = v0 + 64 * u + lane;
+      const bool in = v < hi;
+      const bool sel = in && v != blank && mk[u] != 0;
+      const unsigned long long bal = __ballot(sel);
+      const int pos = idx + __popcll(bal & ((1ull << lane) - 1ull));
+      if (in) {
+        if (v == blank) {
+          col2sel[v] = 0;
+        } else if (sel) {
+          col2sel[v] = pos;
+          U[pos] = v;
+        } else {
+          col2sel[v] = -1;
+        }
       }
+      idx += __popcll(bal);
     }
-    idx += __popcll(bal);
   }
   if (threadIdx.x == 0) {
     U[0] = blank;
