@@ -1152,8 +1152,18 @@ __global__ __launch_bounds__(256) void k_grad_reduce(
     // same split order per element
     for (long long i = i0; i < n / 4; i += stride) {
       f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      for (int k = 0; k < splitk; ++k)
-        s += *reinterpret_cast<const f32x4*>(part + (long long)k * n + 4 * i);
+      // eight splits' loads in flight together (clamped split index, the
+      // extra ones not added), summed in split order
+      for (int k0 = 0; k0 < splitk; k0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = *reinterpret_cast<const f32x4*>(part + (long long)min(k0 + u, splitk - 1) * n +
+                                                 4 * i);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (k0 + u < splitk) s += v[u];
+      }
       T o[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
@@ -1167,7 +1177,14 @@ __global__ __launch_bounds__(256) void k_grad_reduce(
   }
   for (long long i = i0; i < n; i += stride) {
     float s = 0.f;
-    for (int k = 0; k < splitk; ++k) s += part[(long long)k * n + i];
+    for (int k0 = 0; k0 < splitk; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(long long)min(k0 + u, splitk - 1) * n + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < splitk) s += v[u];
+    }
     dW[row_base * D + i] = Elem<T>::from_f32(s);
   }
 }
