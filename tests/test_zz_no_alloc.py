@@ -111,6 +111,26 @@ def test_static_entry_matches_forward_backward_twice():
             assert rel_fro(got.double().cpu().numpy(), want.double().cpu().numpy()) <= 1e-12
 
 
+def test_static_entry_small_vocabulary_column_order():
+    """A small vocabulary with nearly every class selected, where the
+    recompute walks the chunk unselected-first (its column order and gathered
+    head rows also come from the static array): identical to the context
+    entry points."""
+    import torch
+    import oracle
+    bt = workloads.make_random(65, N=8, T_lo=250, T_hi=350, V=300, D=64, chunk=512, zipf_s=0.0)
+    U, _, _ = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
+    assert len(U) * min(bt.chunk, bt.V) >= bt.V * 128  # the column order runs
+    d = to_device(bt)
+    rloss, rinfo, rg = _reference(bt, d)
+    st, loss, info, g = _static(bt, d)
+    assert st == 0
+    assert loss == rloss and info.K == rinfo["K"]
+    for got, want in zip(g, rg):
+        if want is not None:
+            assert torch.equal(got, want)
+
+
 def test_static_entry_rejects_oversize():
     import torch
     from vocabulary_ctc_loss_amd import load
