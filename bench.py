@@ -377,6 +377,7 @@ def main():
                 "unit": "frames/s", "ms_per_step": e["ms_per_step"],
                 "ms_per_step_stats": e["ms_per_step_stats"],
                 "pct_mfma_peak": e["pct_mfma_peak"],
+                "workspace_GiB": e["info"]["workspace_bytes"] / 2**30,
                 "roofline": dict(kernel=e["dom"], **e["roof"]),
                 "kernels": e["kernels"], "hbm_passes": e["hbm_passes"],
             }

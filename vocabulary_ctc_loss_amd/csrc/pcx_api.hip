@@ -646,33 +646,41 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (dX && !dW && !db)
     while (G < DX_PARTS && nchunks >= 2 * G && M >= 2 * G * rtile) G *= 2;
   const int CG = G * C;  // columns per group
+  // Width (and leading dimension) of the group blocks: the group's columns,
+  // or the whole vocabulary rounded up to 64 when that is narrower (a small
+  // vocabulary in one wide chunk); the 256 x 256 core's zero padding of a
+  // group to a multiple of 64 columns still fits.
+  const int V64 = (V + 63) / 64 * 64;
+  const int LZ = CG < V64 ? CG : V64;
   // rows per part: whole row tiles, so that every part starts on a tile
   const int Mh = G == 1 ? M : ((M + G - 1) / G + rtile - 1) / rtile * rtile;
   const int mtiles = (Mh + rtile - 1) / rtile;  // row tiles of the largest part
-  ENSURE(dZ, (size_t)Mh * CG * esz);
-  ENSURE(dbpart, (size_t)mtiles * CG * sizeof(float));
+  ENSURE(dZ, (size_t)Mh * LZ * esz);
+  ENSURE(dbpart, (size_t)mtiles * LZ * sizeof(float));
   float* dxacc = nullptr;
   if (dX) {
     if (cdt == PCX_F32) {
       dxacc = (float*)dX;
     } else {
       ENSURE(dXacc, (size_t)M * D * sizeof(float));
-      ENSURE(wt, (size_t)D * CG * esz);
+      ENSURE(wt, (size_t)D * LZ * esz);
       dxacc = (float*)ctx->dXacc.p;
     }
   }
   if (widen) {
-    ENSURE(w32, (size_t)CG * D * sizeof(float));
-    if (ctx->b) ENSURE(b32, (size_t)CG * sizeof(float));
+    ENSURE(w32, (size_t)LZ * D * sizeof(float));
+    if (ctx->b) ENSURE(b32, (size_t)LZ * sizeof(float));
   }
   // Split of the frame reduction of dW: enough work-groups to fill the chip,
-  // at least 1024 frames per split; fixed for a given shape.
-  const int wtiles = dw_tiles(cdt, C, D);
+  // at least 1024 frames per split; fixed for a given shape.  (512 frames
+  // per split, 64 instead of 48 splits at V = 500, measured no faster.)
+  const int Cw = C < V ? C : V;  // widest chunk
+  const int wtiles = dw_tiles(cdt, Cw, D);
   int splitk = (1024 + wtiles - 1) / wtiles;
   const int maxsplit = (M + 1023) / 1024;
   if (splitk > maxsplit) splitk = maxsplit;
   if (splitk < 1) splitk = 1;
-  if (dW) ENSURE(dwpart, (size_t)splitk * C * D * sizeof(float));
+  if (dW) ENSURE(dwpart, (size_t)splitk * Cw * D * sizeof(float));
 
   // Where a chunk group can be expected to hold a tile's worth of selected
   // classes or more (K close to V: small vocabularies), the recompute walks
@@ -682,8 +690,8 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   const int Cg = CG < V ? CG : V;
   const bool order = !big && (long long)ctx->K * Cg >= (long long)V * rec_tile_cols(cdt);
   if (order) {
-    ENSURE(cmap, ((size_t)CG + 1) * sizeof(int));
-    ENSURE(wg, (size_t)CG * D * esz);
+    ENSURE(cmap, ((size_t)LZ + 1) * sizeof(int));
+    ENSURE(wg, (size_t)LZ * D * esz);
   }
   int* cmap = order ? (int*)ctx->cmap.p : nullptr;
 
@@ -707,7 +715,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       w0 = 0;
     }
     if (order)
-      LAUNCH(K_RECOMPUTE, launch_colperm(st, cdt, sel, w0, w0 + Cc, Wk, D, cmap, cmap + CG,
+      LAUNCH(K_RECOMPUTE, launch_colperm(st, cdt, sel, w0, w0 + Cc, Wk, D, cmap, cmap + LZ,
                                          ctx->wg.p));
     for (int part = 0; part < G; ++part) {
       // frames [r0, r0 + Mp); S and Gamma keep their leading dimension M
@@ -718,21 +726,21 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
              launch_recompute(st, cdt, (const char*)ctx->X + (size_t)r0 * D * esz, Wk, bk, Mp,
                               D, w0, w0 + Cc, sel, (const float*)ctx->lamf.p + r0,
                               (const double*)ctx->g.p + r0, S + r0,
-                              (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, CG,
+                              (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, LZ,
                               (float*)ctx->dbpart.p, big, gu ? gu + r0 : nullptr,
                               ou ? ou + r0 : nullptr, M, cmap, order ? ctx->wg.p : nullptr,
-                              order ? cmap + CG : nullptr));
+                              order ? cmap + LZ : nullptr));
       if (dX)
-        LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, CG, Wk, Mp, D, w0, w0 + Cc,
+        LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, LZ, Wk, Mp, D, w0, w0 + Cc,
                                dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
       // dW and db are only wanted with G == 1: this part is all M frames
       if (dW)
-        LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, CG, ctx->X, M, D, w0, w0 + Cc,
+        LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, LZ, ctx->X, M, D, w0, w0 + Cc,
                                (float*)ctx->dwpart.p, splitk));
       if (dW || db)
         LAUNCH(K_REDUCE, launch_grad_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc,
                                             D, dW, c0, (const float*)ctx->dbpart.p, mtiles, Cc,
-                                            CG, db, c0));
+                                            LZ, db, c0));
     }
   }
   if (dX && cdt != PCX_F32)
