@@ -125,8 +125,6 @@ enum : int { UTT_OK = 0, UTT_UNALIGNABLE = 1, UTT_NONFINITE = 2 };
 // Largest vocabulary span folded into one normalizer partial by the forward
 // kernel (one work-group walks one span of one frame tile).
 constexpr int LSE_SPAN_MAX = 2048;
-// Frames per work-group of the occupancy kernel.
-constexpr int OCC_FRAMES = 32;
 // Most parts the frames are split into for a backward that wants dX alone
 // (chunks are then taken in groups of as many).
 constexpr int DX_PARTS = 2;
