@@ -4,9 +4,9 @@
 the backward reuses S, so a selected class's logit gradient needs only S,
 the occupancy and g, never the recomputed logit.  When a chunk can be
 expected to hold a tile's worth of selected classes (K * min(C, V) >= V *
-tile width), the library walks the chunk's columns unselected-first: the
-selected classes then fill whole tiles, which skip the product and go to a
-pass of their own.  The same batch run with a narrow chunk (C = 64, below
+tile width) and at least a quarter of the classes are selected, the library
+walks the chunk's columns unselected-first: the selected classes then fill
+whole tiles, which skip the product and go to a pass of their own.  The same batch run with a narrow chunk (C = 64, below
 one tile width) takes the in-order recompute.  Both are held to the oracle's
 bar, to rounding-level agreement with each other, and the profiler's launch
 counts show which path ran.
@@ -60,7 +60,7 @@ def test_selected_first_order_matches_oracle_and_in_order(dtype, grouped):
     K = len(U)
     tile = 128 if dtype == "f32" else 256  # column tile of the recompute core
     print("dtype", dtype, "grouped", grouped, "K", K, "M", bt.M, flush=True)
-    assert K * min(bt.chunk, V) >= V * tile      # the ordered path
+    assert K * min(bt.chunk, V) >= V * tile and 4 * K >= V  # the ordered path
     narrow = dataclasses.replace(bt, chunk=64)
     assert K * 64 < V * tile                     # the in-order path
     # one chunk group: the order pass and the recompute; five groups in order

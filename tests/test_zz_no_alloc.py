@@ -120,7 +120,7 @@ def test_static_entry_small_vocabulary_column_order():
     import oracle
     bt = workloads.make_random(65, N=8, T_lo=250, T_hi=350, V=300, D=64, chunk=512, zipf_s=0.0)
     U, _, _ = oracle.select(bt.V, bt.blank, bt.frame_counts, bt.tgt_off, bt.tgt)
-    assert len(U) * min(bt.chunk, bt.V) >= bt.V * 128  # the column order runs
+    assert len(U) * min(bt.chunk, bt.V) >= bt.V * 128 and 4 * len(U) >= bt.V  # the order runs
     d = to_device(bt)
     rloss, rinfo, rg = _reference(bt, d)
     st, loss, info, g = _static(bt, d)

@@ -683,12 +683,15 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   if (dW) ENSURE(dwpart, (size_t)splitk * Cw * D * sizeof(float));
 
   // Where a chunk group can be expected to hold a tile's worth of selected
-  // classes or more (K close to V: small vocabularies), the recompute walks
-  // each group's columns unselected-first, so that the selected classes fill
-  // whole tiles whose product is skipped; its products then read the head
-  // rows they need gathered into wg.  (Not on the 256 x 256 bf16 core.)
+  // classes or more and at least a quarter of the classes are selected (K
+  // close to V: small vocabularies), the recompute walks each group's columns
+  // unselected-first, so that the selected classes fill whole tiles whose
+  // product is skipped; its products then read the head rows they need
+  // gathered into wg (which costs a copy of the unselected rows, hence the
+  // quarter).  (Not on the 256 x 256 bf16 core.)
   const int Cg = CG < V ? CG : V;
-  const bool order = !big && (long long)ctx->K * Cg >= (long long)V * rec_tile_cols(cdt);
+  const bool order = !big && (long long)ctx->K * Cg >= (long long)V * rec_tile_cols(cdt) &&
+                     4LL * ctx->K >= (long long)V;
   if (order) {
     ENSURE(cmap, ((size_t)LZ + 1) * sizeof(int));
     ENSURE(wg, (size_t)LZ * D * esz);
