@@ -25,6 +25,24 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   return static_cast<bf16_t>(u >> 16);
 }
 
+// exp(s) of an fp32 log-probability s as m 2^n, to fp32 precision (the
+// precision of s itself, an fp32 score): x = s log2(e) is formed as hi + lo
+// (hi the fp32 product, lo its rounding error by a fused multiply-add plus
+// s times the tail of log2(e)), n = rint(hi), and m = 2^((hi - n) + lo) by
+// the hardware exp2 (hi - n is exact and |(hi - n) + lo| <= 1/2 + 2^-20, so
+// m lies in [0.7, 1.42]); about 2^-22 relative error in all.  s below -1e6
+// is taken as -1e6; a NaN stays NaN.
+__device__ __forceinline__ float exp_split(float s, int& n) {
+  constexpr float L2E_HI = 0x1.715476p+0f;   // fp32 log2(e)
+  constexpr float L2E_LO = 0x1.4ae0c0p-26f;  // log2(e) - L2E_HI, rounded
+  const float x = s < -1e6f ? -1e6f : s;
+  const float hi = x * L2E_HI;
+  const float lo = fmaf(x, L2E_HI, -hi) + x * L2E_LO;
+  const float nf = rintf(hi);
+  n = (int)nf;
+  return __builtin_amdgcn_exp2f((hi - nf) + lo);
+}
+
 // exp(x) for x <= 0 in IEEE double (0 below the double range; branch-free).
 // Cody-Waite reduction x = n ln2 + r with ln2 split into a 32-bit head (so
 // n * head is exact) and a tail, |r| <= ln2 / 2, then the degree-13 Taylor

@@ -141,23 +141,12 @@ __device__ __forceinline__ double sc_sum3(const Sc& a, const Sc& b, const Sc& c,
   return ldexp(a.m, a.e - emax) + ldexp(b.m, b.e - emax) + ldexp(c.m, c.e - emax);
 }
 
-// exp(S) of an fp32 log-probability S as m 2^n, to fp32 precision (the
-// precision of S itself, an fp32 score): x = S log2(e) is formed as hi + lo
-// (hi the fp32 product, lo its rounding error by a fused multiply-add plus
-// S times the tail of log2(e)), n = rint(hi), and m = 2^((hi - n) + lo) by
-// the hardware exp2 (hi - n is exact and |(hi - n) + lo| <= 1/2 + 2^-20, so
-// m lies in [0.7, 1.42]); about 2^-22 relative error in all.  S below -1e6
-// is taken as -1e6 (probability 2^-1.4e6, still a scaled value); a NaN
-// stays NaN.
+// exp(S) of an fp32 log-probability S as a scaled value m 2^n, to fp32
+// precision (exp_split).
 __device__ __forceinline__ Sc sc_exp(float s) {
-  constexpr float L2E_HI = 0x1.715476p+0f;    // fp32 log2(e)
-  constexpr float L2E_LO = 0x1.4ae0c0p-26f;   // log2(e) - L2E_HI, rounded
-  const float x = s < -1e6f ? -1e6f : s;
-  const float hi = x * L2E_HI;
-  const float lo = fmaf(x, L2E_HI, -hi) + x * L2E_LO;
-  const float n = rintf(hi);
-  const float m = __builtin_amdgcn_exp2f((hi - n) + lo);
-  return {(double)m, (int)n};
+  int n;
+  const float m = exp_split(s, n);
+  return {(double)m, n};
 }
 
 // Stored form of a scaled value (the occupancy pass reads it): the mantissa

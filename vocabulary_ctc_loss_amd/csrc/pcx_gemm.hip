@@ -1620,6 +1620,17 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
 // addition the chunk block's columns between the chunk end and the next
 // multiple of 64 are written as zeros, because the dX product on the big
 // core reduces over whole 64-column steps.
+// dZ of a selected class on the bf16 core: grad (g p - Gamma) with p = exp(S)
+// to fp32 precision (exp_split; far below the bf16 rounding of the result and
+// the product's own error in S), combined in FP64 and rounded once.  The
+// NaN score of an excluded row (non-finite input; g and Gamma are 0 there)
+// is taken as -1e6, so its value is 0.
+__device__ __forceinline__ float sel_dz(double grad, double g, float s, float gam) {
+  int n;
+  const float m = exp_split(fmaxf(s, -1e6f), n);
+  return (float)(grad * fma(g, ldexp((double)m, n), -(double)gam));
+}
+
 template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     const bf16_t* __restrict__ X, const bf16_t* __restrict__ W, const bf16_t* __restrict__ bias,
@@ -1682,7 +1693,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     s_lam2[rr] = in ? lv * LOG2E : 0.f;
   }
   lds_barrier();
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wm = w / C::WGN;
+  // the wavefront index as a uniform (scalar) value
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = w / C::WGN;
   // Selected columns of this wavefront, in (fragment column, lane) order; with
   // at most SELP of them their S and Gamma values are loaded straight
   // into LDS now, behind the product (they do not depend on it).
@@ -1742,11 +1755,12 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
     cs[fj] = 0.f;
   }
   // Few selected classes (at most SELP in this wavefront): each
-  // column by all 64 lanes (one of the wavefront's rows each), in FP64 and
-  // rounded once, into LDS (one region per wavefront) with the column's sum
+  // column by all 64 lanes (one of the wavefront's rows each, sel_dz),
+  // into LDS (one region per wavefront) with the column's sum
   // over the wavefront's rows (a fixed-order wave sum) ...
   const bool dense = pn > SELP;
-  float* tmp = reinterpret_cast<float*>(smem) + w * (SELP * (C::WM + 1));
+  // this wavefront's share of the stage buffers (either pass below)
+  float* tmp = reinterpret_cast<float*>(smem) + w * (O_DB / C::WAVES / 4);
   if (!dense && pn > 0) {
     const int row = wm * C::WM + lane;
 #pragma unroll
@@ -1756,8 +1770,7 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
                                                          (w * SELP + k) * 512);
         float sum = 0.f, dz = 0.f;
         if (m0 + row < M) {
-          // S <= 0 (a log-probability)
-          dz = (float)(grad * (s_g[row] * exp_nonpos((double)pv[lane]) - (double)pv[64 + lane]));
+          dz = sel_dz(grad, s_g[row], pv[lane], pv[64 + lane]);
           sum = dz;
         }
         tmp[k * C::WM + lane] = dz;
@@ -1795,12 +1808,73 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
       }
     }
   }
-  if (!dense) {
+  // Many selected classes (more than SELP in this wavefront): in batches of
+  // up to SLOTS columns, each column by all 64 lanes (one row each) into an
+  // LDS slot, then each lane that owns a selected column of the batch takes
+  // its 32 rows from that column's slot into the accumulators, with their sum
+  // as its part of the column sum.  The wavefront's selected ids are listed
+  // in LDS (in the prefetch region, unused with this many) in (fragment
+  // column, lane) order.
+  if (dense) {
+    constexpr int SLOT = C::WM + 4;  // 16-byte aligned slots, 4 banks apart
+    constexpr int SLOTS = 8;  // (15 fit; 8 keeps the loads in registers)
+    static_assert(C::WAVES * SLOTS * SLOT * 4 <= O_DB && SELP * 128 >= C::WN, "dense pass LDS use");
+    float* buf = tmp;
+    int* list = reinterpret_cast<int*>(smem + O_PRE) + w * (SELP * 128);
+    const int h = lane >> 5;
+    int rank[C::FN], tot = 0;
+    bool mine[C::FN];
 #pragma unroll
     for (int fj = 0; fj < C::FN; ++fj) {
-      cs[fj] += __shfl_xor(cs[fj], 32, 64);
-      if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
+      const unsigned long long mk = __ballot(lane < 32 && csel[fj] >= 0);
+      const unsigned long long bit = 1ull << (lane & 31);
+      mine[fj] = (mk & bit) != 0ull;
+      rank[fj] = tot + __popcll(mk & (bit - 1ull));
+      tot += __popcll(mk);
+      if (lane < 32 && mine[fj]) list[rank[fj]] = csel[fj];
     }
+    const int trow = wm * C::WM + lane;
+    const int grow = min(m0 + trow, M - 1);
+    const bool rin = m0 + trow < M;
+    const double gr = s_g[trow];
+    for (int b0 = 0; b0 < tot; b0 += SLOTS) {
+      // every load of the batch in flight together (clamped to the last
+      // listed column past the end)
+      float sv[SLOTS], gv[SLOTS];
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k) {
+        const long long base = (long long)list[min(b0 + k, tot - 1)] * ldS + grow;
+        sv[k] = S[base];
+        gv[k] = Gam[base];
+      }
+#pragma unroll
+      for (int k = 0; k < SLOTS; ++k)
+        if (b0 + k < tot) buf[k * SLOT + lane] = rin ? sel_dz(grad, gr, sv[k], gv[k]) : 0.f;
+#pragma unroll
+      for (int fj = 0; fj < C::FN; ++fj) {
+        const int sl = rank[fj] - b0;
+        const bool own = mine[fj] && sl >= 0 && sl < SLOTS;
+        const float* src = buf + (own ? sl : 0) * SLOT + 4 * h;
+        float sum = 0.f;
+#pragma unroll
+        for (int fi = 0; fi < C::FM; ++fi)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x4 v4 = *reinterpret_cast<const f32x4*>(src + fi * 32 + 8 * q);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              acc[fi][fj][4 * q + e] = own ? v4[e] : acc[fi][fj][4 * q + e];
+              sum += v4[e];
+            }
+          }
+        if (own) cs[fj] = sum;
+      }
+    }
+  }
+#pragma unroll
+  for (int fj = 0; fj < C::FN; ++fj) {
+    cs[fj] += __shfl_xor(cs[fj], 32, 64);
+    if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
   }
   // ... and into the accumulators of the lanes that own the selected columns;
   // their column sums overwrite the ones just written (later writes of this
@@ -1833,9 +1907,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
   // Stores of four consecutive columns (8 bytes) per lane: a lane holds four
   // rows of one column, so lanes l, l ^ 1 and then l, l ^ 2 trade values until
   // lane l holds row (l & 3) of the group for columns (l & ~3) .. (l & ~3) + 3.
-  // With many selected classes (dense pass below) their columns are written
-  // here with the unselected formula and overwritten by that pass, from the
-  // same wavefront.
   {
     const int odd = lane & 1, b1 = (lane >> 1) & 1;
 #pragma unroll
@@ -1861,50 +1932,6 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_recompute_big(
         }
       }
       __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // Selected classes: dZ needs no recomputed logit, only S, Gamma and g.
-  // With few of them in this wavefront (the large-vocabulary case) each is
-  // done by all 64 lanes in the pass further down; with many, every lane
-  // does its own here.
-  // The dense pass's stores must land after this wavefront's packed stores
-  // to the same addresses: wait until those are acknowledged.
-  if (dense) {
-#pragma unroll
-    for (int fj = 0; fj < C::FN; ++fj)
-      if (crole[fj] == 2) cs[fj] = 0.f;
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
-    __builtin_amdgcn_sched_barrier(0);
-  }
-  if (dense) {
-#pragma unroll
-    for (int fj = 0; fj < C::FN; ++fj) {
-      if (crole[fj] != 2 || csel[fj] < 0) continue;
-      const float* Sp = S + csel[fj] * ldS + m0;
-      const float* Gp = Gam + csel[fj] * ldS + m0;
-#pragma unroll
-      for (int fi = 0; fi < C::FM; ++fi) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = acc_row<C>(fi, r);
-          if (rows_full || m0 + row < M) {
-            // S <= 0 (a log-probability)
-            const float dz =
-                (float)(grad * (s_g[row] * exp_nonpos((double)Sp[row]) - (double)Gp[row]));
-            dZ[(long long)(m0 + row) * ldz + (n0 + acc_col<C>(fj) - c0)] = f32_to_bf16(dz);
-            cs[fj] += dz;
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  if (dense) {
-#pragma unroll
-    for (int fj = 0; fj < C::FN; ++fj) {
-      cs[fj] += __shfl_xor(cs[fj], 32, 64);
-      if (lane < 32) s_db[wm][acc_col<C>(fj)] = cs[fj];
     }
   }
   lds_barrier();
