@@ -1564,15 +1564,25 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_fwd_lse_big(
           const int4 sel4 = *reinterpret_cast<const int4*>(&s_sel[par][r0]);
           const f32x4 b4 = *reinterpret_cast<const f32x4*>(&s_bias[par][r0]);
           const int sl[4] = {sel4.x, sel4.y, sel4.z, sel4.w};
+          float z[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float z = acc[fi][fj][4 * q + e] + b4[e];
-            chk = fmaf(z, 0.f, chk);
+            z[e] = acc[fi][fj][4 * q + e] + b4[e];
+            chk = fmaf(z[e], 0.f, chk);
+          }
+          // the gather, behind one test per group of four rows (selected
+          // rows are rare in a large vocabulary: most groups skip it whole)
+          if (max(max(sl[0], sl[1]), max(sl[2], sl[3])) >= 0 && frame < M) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (sl[e] >= 0) Zsel[(long long)sl[e] * M + frame] = z[e];
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
             // in the sum: every vocabulary row of the span, or (masked)
             // only the unselected ones
-            acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z : -INFINITY;
+            acc[fi][fj][4 * q + e] = (MASKED ? sl[e] == -1 : sl[e] >= -1) ? z[e] : -INFINITY;
             mx = fmaxf(mx, acc[fi][fj][4 * q + e]);
-            if (sl[e] >= 0 && frame < M) Zsel[(long long)sl[e] * M + frame] = z;
           }
           __builtin_amdgcn_sched_barrier(0);
         }
