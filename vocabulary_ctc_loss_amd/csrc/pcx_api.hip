@@ -655,8 +655,16 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   // rows per part: whole row tiles, so that every part starts on a tile
   const int Mh = G == 1 ? M : ((M + G - 1) / G + rtile - 1) / rtile * rtile;
   const int mtiles = (Mh + rtile - 1) / rtile;  // row tiles of the largest part
+  // The gradient reduction of a chunk runs inside the next chunk's recompute
+  // launch, as work-groups appended after its tiles (the launch's last,
+  // partial wave of tiles leaves CUs free for them); the last chunk's runs as
+  // a launch of its own.  The bias partials then alternate between two
+  // halves of dbpart, so that a recompute never writes the half its appended
+  // reduction reads.  (The 256 x 256 core keeps a launch per reduction.)
+  const bool fuse = !big && (dW || db) && G == 1;
+  const size_t dbhalf = (size_t)mtiles * LZ;
   ENSURE(dZ, (size_t)Mh * LZ * esz);
-  ENSURE(dbpart, (size_t)mtiles * LZ * sizeof(float));
+  ENSURE(dbpart, (fuse ? 2 : 1) * dbhalf * sizeof(float));
   float* dxacc = nullptr;
   if (dX) {
     if (cdt == PCX_F32) {
@@ -699,7 +707,9 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   int* cmap = order ? (int*)ctx->cmap.p : nullptr;
 
   const int ngroups = (V + CG - 1) / CG;
+  ReduceJob pend;  // a chunk's reduction still to run (nb == 0: none)
   for (int gi = 0; gi < ngroups; ++gi) {
+    float* dbp = (float*)ctx->dbpart.p + (fuse ? (size_t)(gi & 1) * dbhalf : 0);
     const int c0 = gi * CG, c1 = (c0 + CG < V) ? c0 + CG : V, Cc = c1 - c0;
     // The products see the group's head rows as rows [w0, w0 + Cc) of Wk
     // (the head itself, or its fp32 copy for a bf16-stored head).
@@ -729,10 +739,11 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
              launch_recompute(st, cdt, (const char*)ctx->X + (size_t)r0 * D * esz, Wk, bk, Mp,
                               D, w0, w0 + Cc, sel, (const float*)ctx->lamf.p + r0,
                               (const double*)ctx->g.p + r0, S + r0,
-                              (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, LZ,
-                              (float*)ctx->dbpart.p, big, gu ? gu + r0 : nullptr,
-                              ou ? ou + r0 : nullptr, M, cmap, order ? ctx->wg.p : nullptr,
-                              order ? cmap + LZ : nullptr));
+                              (const float*)ctx->Gam.p + r0, grad_loss, ctx->dZ.p, LZ, dbp,
+                              big, gu ? gu + r0 : nullptr, ou ? ou + r0 : nullptr, M, cmap,
+                              order ? ctx->wg.p : nullptr, order ? cmap + LZ : nullptr,
+                              fuse ? &pend : nullptr));
+      pend = ReduceJob{};
       if (dX)
         LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, LZ, Wk, Mp, D, w0, w0 + Cc,
                                dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
@@ -740,12 +751,18 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       if (dW)
         LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, LZ, ctx->X, M, D, w0, w0 + Cc,
                                (float*)ctx->dwpart.p, splitk));
-      if (dW || db)
-        LAUNCH(K_REDUCE, launch_grad_reduce(st, wdt, (const float*)ctx->dwpart.p, splitk, Cc,
-                                            D, dW, c0, (const float*)ctx->dbpart.p, mtiles, Cc,
-                                            LZ, db, c0));
+      if (dW || db) {
+        const ReduceJob rj = make_reduce_job(wdt, (const float*)ctx->dwpart.p, splitk, Cc, D, dW,
+                                             c0, dbp, mtiles, Cc, LZ, db, c0,
+                                             fuse ? 256 : 8192);
+        if (fuse)
+          pend = rj;
+        else
+          LAUNCH(K_REDUCE, launch_grad_reduce(st, rj));
+      }
     }
   }
+  if (pend.nb > 0) LAUNCH(K_REDUCE, launch_grad_reduce(st, pend));
   if (dX && cdt != PCX_F32)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;

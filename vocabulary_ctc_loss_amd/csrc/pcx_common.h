@@ -187,6 +187,29 @@ hipError_t launch_grouped_rowscale(hipStream_t st, const double* g, const double
 hipError_t launch_scores(hipStream_t st, float* S, const double* lam, int K, int M);
 
 // Backward head (pcx_gemm.hip).
+// The gradient reduction of one chunk: dW rows [row_base, row_base + rows)
+// from the splitk split partials and db columns [col_base, col_base + cols)
+// from the per-row-tile partials (leading dimension ld); either output may
+// be NULL.  nb work-groups of 256 threads do it (the first nb_db the db
+// columns); out_bf16: the outputs are bf16, else fp32.
+struct ReduceJob {
+  const float* part = nullptr;
+  int splitk = 0, rows = 0, D = 0;
+  void* dW = nullptr;
+  long long row_base = 0;
+  const float* dbpart = nullptr;
+  int mtiles = 0, cols = 0, ld = 0;
+  void* db = nullptr;
+  long long col_base = 0;
+  int nb_db = 0, nb = 0, vec4 = 0, out_bf16 = 0;
+};
+// max_wg: most work-groups for the dW part.
+ReduceJob make_reduce_job(int dtype, const float* part, int splitk, int rows, int D, void* dW,
+                          long long row_base, const float* dbpart, int mtiles, int cols, int ld,
+                          void* db, long long col_base, int max_wg = 8192);
+// rj (optional, fp32 and bf16 128-row cores only): a reduction appended to
+// the launch as rj->nb extra work-groups after the tiles.  It must not touch
+// what the recompute writes (the dZ block, dbpart).
 hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void* W,
                             const void* b, int M, int D, int c0, int c1,
                             const int* col2sel, const float* lamf, const double* g,
@@ -195,7 +218,7 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const double* gu = nullptr, const float* ou = nullptr,
                             long long ldS = 0,  // S / Gamma leading dimension (0: M)
                             const int* cmap = nullptr, const void* Wg = nullptr,
-                            const int* nu = nullptr);
+                            const int* nu = nullptr, const ReduceJob* rj = nullptr);
 // Unselected-first column order of the chunk [c0, c1) into cmap[0 ..] and
 // *nu, and the head rows the recompute products read, gathered into Wg
 // (the recompute's cmap / Wg; not for the 256 x 256 bf16 core).
@@ -214,13 +237,8 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
                      int stage_wt = 1);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
-// dW rows [row_base, row_base + rows) from the split partials and db
-// columns [col_base, col_base + cols) from the per-row-tile partials
-// (leading dimension ld), in one launch; either output may be NULL.
-hipError_t launch_grad_reduce(hipStream_t st, int dtype, const float* part, int splitk,
-                              int rows, int D, void* dW, long long row_base,
-                              const float* dbpart, int mtiles, int cols, int ld, void* db,
-                              long long col_base);
+// A gradient reduction as a launch of its own.
+hipError_t launch_grad_reduce(hipStream_t st, const ReduceJob& rj);
 hipError_t launch_cast_out(hipStream_t st, int dtype, const float* src, void* dst,
                            long long n);
 // dst[i] = fp32(src[i]) for n bf16 values.

@@ -697,6 +697,96 @@ constexpr int SEL_PRE_BIG = 6;
 // flight together.
 constexpr int DENSE_ILP = 8;
 
+// ------------------------------------------------------ gradient reduction
+// The two head-gradient reductions of one chunk, in work-groups of 256
+// threads: the first nb_db reduce the bias partials, 16 columns each
+// (db[col] = sum over row tiles of dbpart[tile][col]: sixteen fixed groups of
+// consecutive tiles, the group sums added in group order); the others reduce
+// the dW split partials (dW[row_base + r][d] = sum over k, in order, of
+// part[k][r][d]).  The db part is latency-bound and the dW part HBM-bound, so
+// they share a launch: their own, or the next chunk's recompute launch, whose
+// last partial wave of tiles leaves CUs free for them.
+constexpr int DB_GROUPS = 16;
+constexpr int DB_COLS = 256 / DB_GROUPS;
+
+// Work-group bid (0 .. rj.nb - 1) of the reduction; gs: DB_GROUPS x DB_COLS
+// floats of LDS.  Every thread of the work-group calls it.
+template <typename T>
+__device__ __forceinline__ void grad_reduce_wg(const ReduceJob& rj, int bid, float* gs) {
+  const float* __restrict__ part = rj.part;
+  const int splitk = rj.splitk, D = rj.D;
+  if (bid < rj.nb_db) {
+    const int lc = threadIdx.x % DB_COLS, q = threadIdx.x / DB_COLS;
+    const int c = bid * DB_COLS + lc;
+    const int per = (rj.mtiles + DB_GROUPS - 1) / DB_GROUPS;
+    const int k1 = min(rj.mtiles, (q + 1) * per);
+    float s = 0.f;
+    if (c < rj.cols) {
+#pragma unroll 8
+      for (int k = q * per; k < k1; ++k) s += rj.dbpart[(long long)k * rj.ld + c];
+    }
+    gs[q * DB_COLS + lc] = s;
+    lds_barrier();
+    if (q == 0 && c < rj.cols) {
+      float t = gs[lc];
+#pragma unroll
+      for (int g = 1; g < DB_GROUPS; ++g) t += gs[g * DB_COLS + lc];
+      static_cast<T*>(rj.db)[rj.col_base + c] = Elem<T>::from_f32(t);
+    }
+    return;
+  }
+  T* __restrict__ dW = static_cast<T*>(rj.dW);
+  const long long n = (long long)rj.rows * D;
+  const long long stride = (long long)(rj.nb - rj.nb_db) * 256;
+  const long long i0 = (long long)(bid - rj.nb_db) * 256 + threadIdx.x;
+  if (rj.vec4) {
+    // four consecutive elements per thread (16-byte partial loads); the
+    // same split order per element
+    for (long long i = i0; i < n / 4; i += stride) {
+      f32x4 s = {0.f, 0.f, 0.f, 0.f};
+      // eight splits' loads in flight together (clamped split index, the
+      // extra ones not added), summed in split order
+      for (int k0 = 0; k0 < splitk; k0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          v[u] = *reinterpret_cast<const f32x4*>(part + (long long)min(k0 + u, splitk - 1) * n +
+                                                 4 * i);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (k0 + u < splitk) s += v[u];
+      }
+      T o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
+      T* dst = dW + rj.row_base * D + 4 * i;
+      if (sizeof(T) == 4)
+        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(o);
+      else
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(o);
+    }
+    return;
+  }
+  for (long long i = i0; i < n; i += stride) {
+    float s = 0.f;
+    for (int k0 = 0; k0 < splitk; k0 += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(long long)min(k0 + u, splitk - 1) * n + i];
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (k0 + u < splitk) s += v[u];
+    }
+    dW[rj.row_base * D + i] = Elem<T>::from_f32(s);
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_grad_reduce(ReduceJob rj) {
+  __shared__ float gs[DB_GROUPS * DB_COLS];
+  grad_reduce_wg<T>(rj, blockIdx.x, gs);
+}
+
 // Selected columns of one wavefront's tile block for the cooperative pass
 // (at most SEL_DENSE of them), in (fragment column, lane) order, with the S
 // and Gamma values of the wavefront's rows (WM / 64 per lane).  They do not
@@ -810,9 +900,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     double grad, typename C::type* __restrict__ dZ, int ldz, float* __restrict__ dbpart,
     int mtiles, int vec_ok, const double* __restrict__ gu, const float* __restrict__ lamu,
     long long ldS, const int* __restrict__ cmap, const typename C::type* __restrict__ Wg,
-    const int* __restrict__ nu) {
+    const int* __restrict__ nu, ReduceJob rj, int ntile) {
   using T = typename C::type;
   constexpr int BM = C::BM, BN = C::BN;
+  static_assert(C::THREADS == 256, "the appended reduction takes 256-thread work-groups");
   constexpr float LOG2E = 1.44269504088896340736f;
   __shared__ __attribute__((aligned(16))) char smem[C::STAGE_BYTES];
   __shared__ int s_sel[BN];
@@ -823,8 +914,18 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   __shared__ float s_db[C::WGM][BN];
   __shared__ int s_list[BN], s_pos[BN], s_cnt[BN / 64];
   __shared__ int s_col[BN];  // dZ column (within the chunk) of each tile column
+  if ((int)blockIdx.x >= ntile) {
+    // a work-group of the appended reduction (another chunk's gradients;
+    // nothing this launch's tiles read or write)
+    float* gs = reinterpret_cast<float*>(smem);
+    if (rj.out_bf16)
+      grad_reduce_wg<bf16_t>(rj, (int)blockIdx.x - ntile, gs);
+    else
+      grad_reduce_wg<float>(rj, (int)blockIdx.x - ntile, gs);
+    return;
+  }
   int mt, nt;
-  grouped_tile<8>(xcd_tile(blockIdx.x, gridDim.x), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
+  grouped_tile<8>(xcd_tile(blockIdx.x, ntile), mtiles, (c1 - c0 + BN - 1) / BN, mt, nt);
   const int m0 = mt * BM, n0 = c0 + nt * BN;
   // in the unselected-first order the tiles of selected classes alone are
   // k_dz_sel's
@@ -1108,87 +1209,6 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_dw(
       }
     }
 }
-
-// The two head-gradient reductions of one chunk in one launch of 256-thread
-// blocks: the first nb_db blocks reduce the bias partials, 16 columns each
-// (db[col] = sum over row tiles of dbpart[tile][col]: sixteen fixed groups of
-// consecutive tiles, the group sums added in group order); the other blocks
-// reduce the dW split partials (dW[row_base + r][d] = sum over k, in order,
-// of part[k][r][d]).  The db part is latency-bound and the dW part
-// HBM-bound, so they share the launch.
-constexpr int DB_GROUPS = 16;
-constexpr int DB_COLS = 256 / DB_GROUPS;
-template <typename T>
-__global__ __launch_bounds__(256) void k_grad_reduce(
-    const float* __restrict__ part, int splitk, int rows, int D, T* __restrict__ dW,
-    long long row_base, const float* __restrict__ dbpart, int mtiles, int cols, int ld,
-    T* __restrict__ db, long long col_base, int nb_db, int vec4) {
-  if ((int)blockIdx.x < nb_db) {
-    __shared__ float gs[DB_GROUPS][DB_COLS];
-    const int lc = threadIdx.x % DB_COLS, q = threadIdx.x / DB_COLS;
-    const int c = blockIdx.x * DB_COLS + lc;
-    const int per = (mtiles + DB_GROUPS - 1) / DB_GROUPS;
-    const int k1 = min(mtiles, (q + 1) * per);
-    float s = 0.f;
-    if (c < cols) {
-#pragma unroll 8
-      for (int k = q * per; k < k1; ++k) s += dbpart[(long long)k * ld + c];
-    }
-    gs[q][lc] = s;
-    lds_barrier();
-    if (q == 0 && c < cols) {
-      float t = gs[0][lc];
-#pragma unroll
-      for (int g = 1; g < DB_GROUPS; ++g) t += gs[g][lc];
-      db[col_base + c] = Elem<T>::from_f32(t);
-    }
-    return;
-  }
-  const long long n = (long long)rows * D;
-  const long long stride = (long long)(gridDim.x - nb_db) * blockDim.x;
-  const long long i0 = (blockIdx.x - nb_db) * (long long)blockDim.x + threadIdx.x;
-  if (vec4) {
-    // four consecutive elements per thread (16-byte partial loads); the
-    // same split order per element
-    for (long long i = i0; i < n / 4; i += stride) {
-      f32x4 s = {0.f, 0.f, 0.f, 0.f};
-      // eight splits' loads in flight together (clamped split index, the
-      // extra ones not added), summed in split order
-      for (int k0 = 0; k0 < splitk; k0 += 8) {
-        f32x4 v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          v[u] = *reinterpret_cast<const f32x4*>(part + (long long)min(k0 + u, splitk - 1) * n +
-                                                 4 * i);
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (k0 + u < splitk) s += v[u];
-      }
-      T o[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) o[e] = Elem<T>::from_f32(s[e]);
-      T* dst = dW + row_base * D + 4 * i;
-      if (sizeof(T) == 4)
-        *reinterpret_cast<f32x4*>(dst) = *reinterpret_cast<const f32x4*>(o);
-      else
-        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(o);
-    }
-    return;
-  }
-  for (long long i = i0; i < n; i += stride) {
-    float s = 0.f;
-    for (int k0 = 0; k0 < splitk; k0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(long long)min(k0 + u, splitk - 1) * n + i];
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (k0 + u < splitk) s += v[u];
-    }
-    dW[row_base * D + i] = Elem<T>::from_f32(s);
-  }
-}
-
 // dst[d][c] = src[c][d] for a rows x D block (64 x 64 tiles through LDS);
 // columns c in [rows, rows_pad) of dst are written as zeros.
 template <typename T>
@@ -2217,17 +2237,17 @@ hipError_t recompute_t(hipStream_t st, const void* X, const void* W, const void*
                        int c0, int c1, const int* col2sel, const float* lamf, const double* g,
                        const float* S, const float* Gam, double grad, void* dZ, int ldz,
                        float* dbpart, const double* gu, const float* lamu, long long ldS,
-                       const int* cmap, const void* Wg, const int* nu) {
+                       const int* cmap, const void* Wg, const int* nu, const ReduceJob* rj) {
   using C = typename Pick<T>::rec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
-  if (grid == 0) return hipSuccess;
+  const ReduceJob job = rj != nullptr ? *rj : ReduceJob{};
+  if (grid + job.nb == 0) return hipSuccess;
   const int vec = (D % C::VEC == 0) && aligned16(X) && aligned16(cmap != nullptr ? Wg : W);
-  k_recompute<C><<<grid, C::THREADS, 0, st>>>((const T*)X, (const T*)W, (const T*)b, M, D, c0, c1,
-                                               col2sel, lamf, g, S, Gam, grad, (T*)dZ, ldz,
-                                               dbpart, mtiles, vec, gu, lamu, ldS, cmap,
-                                               (const T*)Wg, nu);
-  if (cmap != nullptr)
+  k_recompute<C><<<grid + job.nb, C::THREADS, 0, st>>>(
+      (const T*)X, (const T*)W, (const T*)b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad,
+      (T*)dZ, ldz, dbpart, mtiles, vec, gu, lamu, ldS, cmap, (const T*)Wg, nu, job, grid);
+  if (cmap != nullptr && grid > 0)
     k_dz_sel<T, C::BM, C::BN><<<grid, 256, 0, st>>>(col2sel, c0, c1, cmap, nu, g, S, Gam, ldS, M,
                                                      grad, (T*)dZ, ldz, dbpart, mtiles);
   return hipGetLastError();
@@ -2322,16 +2342,17 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
                             const double* g, const float* S, const float* Gam, double grad,
                             void* dZ, int ldz, float* dbpart, int big, const double* gu,
                             const float* lamu, long long ldS, const int* cmap, const void* Wg,
-                            const int* nu) {
+                            const int* nu, const ReduceJob* rj) {
   if (ldS <= 0) ldS = M;
   if ((cmap == nullptr) != (nu == nullptr)) return hipErrorInvalidValue;
   if (dtype == 0)
     return recompute_t<float>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ, ldz,
-                              dbpart, gu, lamu, ldS, cmap, Wg, nu);
+                              dbpart, gu, lamu, ldS, cmap, Wg, nu, rj);
   if (!big)
     return recompute_t<bf16_t>(st, X, W, b, M, D, c0, c1, col2sel, lamf, g, S, Gam, grad, dZ,
-                               ldz, dbpart, gu, lamu, ldS, cmap, Wg, nu);
+                               ldz, dbpart, gu, lamu, ldS, cmap, Wg, nu, rj);
   if (cmap != nullptr) return hipErrorInvalidValue;  // the 256 x 256 core walks columns in order
+  if (rj != nullptr && rj->nb > 0) return hipErrorInvalidValue;  // no appended reduction here
   using C = CfgBigRec;
   const int mtiles = ceil_div(M, C::BM);
   const int grid = mtiles * ceil_div(c1 - c0, C::BN);
@@ -2432,30 +2453,41 @@ int dw_tiles(int dtype, int C, int D) {
   return ceil_div(C, Pick<bf16_t>::dw::BM) * ceil_div(D, Pick<bf16_t>::dw::BN);
 }
 
-hipError_t launch_grad_reduce(hipStream_t st, int dtype, const float* part, int splitk,
-                              int rows, int D, void* dW, long long row_base,
-                              const float* dbpart, int mtiles, int cols, int ld, void* db,
-                              long long col_base) {
-  const long long n = dW ? (long long)rows * D : 0;
+ReduceJob make_reduce_job(int dtype, const float* part, int splitk, int rows, int D, void* dW,
+                          long long row_base, const float* dbpart, int mtiles, int cols, int ld,
+                          void* db, long long col_base, int max_wg) {
+  ReduceJob j;
+  j.part = part;
+  j.splitk = splitk;
+  j.rows = dW ? rows : 0;
+  j.D = D;
+  j.dW = dW;
+  j.row_base = row_base;
+  j.dbpart = dbpart;
+  j.mtiles = mtiles;
+  j.cols = cols;
+  j.ld = ld;
+  j.db = db;
+  j.col_base = col_base;
+  j.out_bf16 = dtype != 0;
+  const long long n = (long long)j.rows * D;
   // 16-byte partial loads when the rows' output starts on a four-element
   // boundary (the partials themselves are 16-byte aligned when n is a
   // multiple of four)
   const size_t esz = dtype == 0 ? 4 : 2;
-  const int vec4 = n % 4 == 0 &&
-                   ((uintptr_t)dW + (uintptr_t)(row_base * D) * esz) % (4 * esz) == 0;
-  const int nb_dw = n ? grid_cap(vec4 ? n / 4 : n, 256) : 0;
-  const int nb_db = (db && cols > 0) ? ceil_div(cols, DB_COLS) : 0;
-  if (nb_dw + nb_db == 0) return hipSuccess;
-  if (dtype == 0)
-    k_grad_reduce<float><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
-                                                       (float*)dW, row_base, dbpart, mtiles,
-                                                       cols, ld, (float*)db, col_base, nb_db,
-                                                       vec4);
+  j.vec4 = n % 4 == 0 && ((uintptr_t)dW + (uintptr_t)(row_base * D) * esz) % (4 * esz) == 0;
+  const int nb_dw = n ? grid_cap(j.vec4 ? n / 4 : n, 256, max_wg) : 0;
+  j.nb_db = (db && cols > 0) ? ceil_div(cols, DB_COLS) : 0;
+  j.nb = nb_dw + j.nb_db;
+  return j;
+}
+
+hipError_t launch_grad_reduce(hipStream_t st, const ReduceJob& rj) {
+  if (rj.nb == 0) return hipSuccess;
+  if (rj.out_bf16)
+    k_grad_reduce<bf16_t><<<rj.nb, 256, 0, st>>>(rj);
   else
-    k_grad_reduce<bf16_t><<<nb_dw + nb_db, 256, 0, st>>>(part, splitk, dW ? rows : 0, D,
-                                                        (bf16_t*)dW, row_base, dbpart, mtiles,
-                                                        cols, ld, (bf16_t*)db, col_base, nb_db,
-                                                        vec4);
+    k_grad_reduce<float><<<rj.nb, 256, 0, st>>>(rj);
   return hipGetLastError();
 }
 
