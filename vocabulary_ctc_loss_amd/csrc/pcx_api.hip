@@ -707,6 +707,9 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
   int* cmap = order ? (int*)ctx->cmap.p : nullptr;
 
   const int ngroups = (V + CG - 1) / CG;
+  // bf16 dX on the 256 x 256 core: the last product into each row's
+  // accumulator writes the bf16 result itself (no separate cast pass)
+  const bool cast_in_dx = dX && cdt != PCX_F32 && big && ((uintptr_t)dX & 7u) == 0;
   ReduceJob pend;  // a chunk's reduction still to run (nb == 0: none)
   for (int gi = 0; gi < ngroups; ++gi) {
     float* dbp = (float*)ctx->dbpart.p + (fuse ? (size_t)(gi & 1) * dbhalf : 0);
@@ -746,7 +749,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
       pend = ReduceJob{};
       if (dX)
         LAUNCH(K_DX, launch_dx(st, cdt, ctx->dZ.p, LZ, Wk, Mp, D, w0, w0 + Cc,
-                               dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0));
+                               dxacc + (size_t)r0 * D, gi == 0, ctx->wt.p, big, part == 0,
+                               cast_in_dx && gi == ngroups - 1
+                                   ? (void*)((char*)dX + (size_t)r0 * D * esz)
+                                   : nullptr));
       // dW and db are only wanted with G == 1: this part is all M frames
       if (dW)
         LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, LZ, ctx->X, M, D, w0, w0 + Cc,
@@ -763,7 +769,7 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
     }
   }
   if (pend.nb > 0) LAUNCH(K_REDUCE, launch_grad_reduce(st, pend));
-  if (dX && cdt != PCX_F32)
+  if (dX && cdt != PCX_F32 && !cast_in_dx)
     LAUNCH(K_CAST, launch_cast_out(st, cdt, dxacc, dX, (long long)M * D));
   ctx->bwd_done = true;
   return PCX_OK;

@@ -232,9 +232,11 @@ int rec_tile_cols(int dtype);
 // the number of output tiles of one dW product.
 int rec_tile_rows(int dtype, int big);
 int dw_tiles(int dtype, int C, int D);
+// out_bf16 (256 x 256 core only, 8-byte aligned): the last product into
+// these rows of the accumulator writes the bf16 result there instead.
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W,
                      int M, int D, int c0, int c1, float* dXacc, int first, void* wt, int big,
-                     int stage_wt = 1);
+                     int stage_wt = 1, void* out_bf16 = nullptr);
 hipError_t launch_dw(hipStream_t st, int dtype, const void* dZ, int ldz, const void* X,
                      int M, int D, int c0, int c1, float* part, int splitk);
 // A gradient reduction as a launch of its own.

@@ -1984,7 +1984,8 @@ template <class C>
 __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restrict__ dZ,
                                                           const bf16_t* __restrict__ Wt, int ldz,
                                                           int M, int D, int Kp,
-                                                          float* __restrict__ dXacc, int first) {
+                                                          float* __restrict__ dXacc, int first,
+                                                          bf16_t* __restrict__ out) {
   __shared__ __attribute__((aligned(16))) char smem[C::LDS_BYTES];
   const int ntiles = (D + C::BN - 1) / C::BN;
   // tiles in groups of 4 row tiles: the 32 work-groups an XCD runs at once
@@ -2000,7 +2001,9 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
   // values until lane l holds row (l & 3) of each four-row group for the
   // columns (l & ~3) .. (l & ~3) + 3; eight lanes then cover 128 contiguous
   // bytes of a row.  One 32 x 32 fragment at a time, its loads issued before
-  // its stores.
+  // its stores.  With `out` (the last product into this accumulator) the sums
+  // go to out as bf16 (round to nearest even, as the separate cast would)
+  // instead of back to the accumulator.
   const int lane = threadIdx.x & 63, odd = lane & 1, b1 = (lane >> 1) & 1;
 #pragma unroll
   for (int fi = 0; fi < C::FM; ++fi) {
@@ -2031,8 +2034,16 @@ __global__ __launch_bounds__(C::THREADS, 1) void k_dx_big(const bf16_t* __restri
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int row = m0 + acc_row<C>(fi, 4 * q) + (lane & 3);
-        if (row < M && col < D)
-          *reinterpret_cast<f32x4*>(dXacc + (long long)row * D + col) = old[q] + val[q];
+        if (row < M && col < D) {
+          const f32x4 sum = old[q] + val[q];
+          if (out != nullptr) {
+            const uint2 h = {(uint32_t)f32_to_bf16(sum[0]) | ((uint32_t)f32_to_bf16(sum[1]) << 16),
+                             (uint32_t)f32_to_bf16(sum[2]) | ((uint32_t)f32_to_bf16(sum[3]) << 16)};
+            *reinterpret_cast<uint2*>(out + (long long)row * D + col) = h;
+          } else {
+            *reinterpret_cast<f32x4*>(dXacc + (long long)row * D + col) = sum;
+          }
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -2053,6 +2064,7 @@ int grid_cap(long long n, int threads, int cap = 8192) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -2366,7 +2378,9 @@ hipError_t launch_recompute(hipStream_t st, int dtype, const void* X, const void
 
 hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const void* W, int M,
                      int D, int c0, int c1, float* dXacc, int first, void* wt, int big,
-                     int stage_wt) {
+                     int stage_wt, void* out_bf16) {
+  if (out_bf16 != nullptr && !(dtype != 0 && big && aligned8(out_bf16)))
+    return hipErrorInvalidValue;  // only the 256 x 256 core writes bf16 itself
   const int Cc = c1 - c0;
   if (dtype == 0) {
     using C = Pick<float>::dx;
@@ -2397,7 +2411,7 @@ hipError_t launch_dx(hipStream_t st, int dtype, const void* dZ, int ldz, const v
       const int grid = ceil_div(M, C::BM) * ceil_div(D, C::BN);
       if (grid == 0) return hipSuccess;
       k_dx_big<C><<<grid, C::THREADS, 0, st>>>((const bf16_t*)dZ, (const bf16_t*)wt, ldz, M, D,
-                                                Kp, dXacc, first);
+                                                Kp, dXacc, first, (bf16_t*)out_bf16);
       return hipGetLastError();
     }
     using C = Pick<bf16_t>::dx;
