@@ -930,6 +930,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   // in the unselected-first order the tiles of selected classes alone are
   // k_dz_sel's
   if (cmap != nullptr && n0 - c0 >= *nu) return;
+  // End of the places this tile forms: in the unselected-first order only the
+  // unselected ones (the selected places of a tile that also holds unselected
+  // ones are k_dz_sel's too, so this tile's epilogue has no selected class).
+  const int c1e = cmap != nullptr ? c0 + *nu : c1;
   // head rows of the product: the gathered rows (from row 0) or the head
   const T* Bh = cmap != nullptr ? Wg : W;
   const int nb0 = cmap != nullptr ? n0 - c0 : n0, nb1 = cmap != nullptr ? c1 - c0 : c1;
@@ -943,8 +947,8 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   // load under a per-lane condition is waited for on the spot).
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
-    const bool in = v < c1;
-    const int vc = in ? v : c1 - 1;
+    const bool in = v < c1e;
+    const int vc = in ? v : c1e - 1;
     const int rv = cmap != nullptr ? cmap[vc - c0] : vc;
     const int sl = col2sel[rv];
     const float bv = bias != nullptr ? Elem<T>::to_f32(bias[rv]) : 0.f;
@@ -971,10 +975,10 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   // is skipped.  (Small vocabularies, where K is close to V, and the densely
   // selected low ids of Zipf-distributed labels.)
   bool any_unsel = false;
-  for (int c = threadIdx.x; c < BN; c += C::THREADS) any_unsel |= n0 + c < c1 && s_sel[c] < 0;
+  for (int c = threadIdx.x; c < BN; c += C::THREADS) any_unsel |= n0 + c < c1e && s_sel[c] < 0;
   const bool need_product = __syncthreads_or(any_unsel) != 0;
   SelPre<C> pre;
-  sel_prefetch<C>(pre, s_sel, n0, c1, m0, M, S, Gam, ldS);
+  sel_prefetch<C>(pre, s_sel, n0, c1e, m0, M, S, Gam, ldS);
   f32x16 acc[C::FM][C::FN];
   if (need_product) {
     gemm_tile_run<C, true, true>(pf, X, D, m0, M, Bh, D, nb0, nb1, 0, D, vec_ok, vec_ok, acc,
@@ -1001,7 +1005,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
     csel[fj] = s_sel[col];
     cbv[fj] = s_bias[col];
     ccol[fj] = s_col[col];
-    crole[fj] = n0 + col < c1 ? (csel[fj] < 0 ? 0 : 2) : 3;
+    crole[fj] = n0 + col < c1e ? (csel[fj] < 0 ? 0 : 2) : 3;
     cs[fj] = 0.f;
   }
 #pragma unroll
@@ -1123,7 +1127,7 @@ __global__ __launch_bounds__(C::THREADS, C::MINWG) void k_recompute(
   lds_barrier();
   for (int c = threadIdx.x; c < BN; c += C::THREADS) {
     const int v = n0 + c;
-    if (v < c1) {
+    if (v < c1e) {
       float t = s_db[0][c];
 #pragma unroll
       for (int q = 1; q < C::WGM; ++q) t += s_db[q][c];
@@ -2191,12 +2195,15 @@ __global__ __launch_bounds__(256) void k_dz_sel(const int* __restrict__ col2sel,
   __shared__ int s_cls[CB], s_col[CB];
   const int mt = blockIdx.x % mtiles, nt = blockIdx.x / mtiles;
   const int p0 = nt * BN;
-  if (p0 < *nu) return;
   const int m0 = mt * BM;
   const int np = min(BN, (c1 - c0) - p0);
+  // the tile's selected places: all of them, or those past the unselected
+  // ones in the tile that holds both (k_recompute forms the rest)
+  const int pb = max(0, *nu - p0);
+  if (pb >= np) return;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   for (int r = threadIdx.x; r < BM; r += 256) s_g[r] = m0 + r < M ? g[m0 + r] : 0.0;
-  for (int cb = 0; cb < np; cb += CB) {
+  for (int cb = pb; cb < np; cb += CB) {
     const int nc = min(CB, np - cb);
     if (threadIdx.x < CB) {
       const bool in = (int)threadIdx.x < nc;
