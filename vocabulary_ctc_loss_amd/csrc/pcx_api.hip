@@ -758,6 +758,10 @@ pcx_status pcx_backward(pcx_ctx* ctx, double grad_loss, void* dX, void* dW, void
         LAUNCH(K_DW, launch_dw(st, cdt, ctx->dZ.p, LZ, ctx->X, M, D, w0, w0 + Cc,
                                (float*)ctx->dwpart.p, splitk));
       if (dW || db) {
+        // Appended to a recompute launch, its work-groups reserve the
+        // recompute's LDS and registers (three per CU), so the dW part takes
+        // 256 of them, each thread summing several elements (measured against
+        // 128, 512 and 2304: 128 and 256 best).
         const ReduceJob rj = make_reduce_job(wdt, (const float*)ctx->dwpart.p, splitk, Cc, D, dW,
                                              c0, dbp, mtiles, Cc, LZ, db, c0,
                                              fuse ? 256 : 8192);
